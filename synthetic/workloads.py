@@ -1,0 +1,244 @@
+"""Workload shapes and seeded generators for the routed MXFP4 MoE layer.
+
+Shapes follow the DeepSeek-V4.1-Flash layer described on the three pages
+(384 routed experts with 6 active plus 1 shared: ai.rs article, table in
+"What V4.1 Flash is, in bytes"; experts of 3 x 5120 x 2304 FP4 weights:
+FreeToken issue #444, "Architecture delta vs deepseek_v4"; packed E2M1 codes
+with one E8M0 scale per 32 weights: same issue, janit's comment, section 2).
+
+Every array is produced from its own keyed PCG64 stream, so any one expert,
+token or router matrix can be regenerated alone (the oracle checks single
+experts of a 6.7 GiB bank without generating the rest):
+
+    [seed, cfg_id, 0, copy, e, m]  expert e (e == E is the shared expert),
+                                   matrix m: 0 gate, 1 up, 2 down.
+                                   Codes first (uniform bytes), then scales.
+    [seed, cfg_id, 1]              router weight, N(0, router_std)
+    [seed, cfg_id, 2, i]           token i, N(0, 1)
+    [seed, cfg_id, 2, b, 0]        correlated blocks: base vector of block b
+    [seed, cfg_id, 2, b, j + 1]    correlated blocks: noise of token j
+    [seed, cfg_id, 3]              popularity ranks for the Zipf logit offset
+
+Floating-point samples are drawn in fp64, rounded to fp32 (round to nearest
+even) and then to bf16 (round to nearest even on the fp32 bit pattern). The
+result is handed out as uint16 bit patterns; both sides decode the same bits.
+"""
+
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic layer call: T tokens through an E-expert top-k layer."""
+
+    name: str
+    cfg_id: int
+    T: int          # tokens per call
+    H: int          # hidden size (K of gate/up, N of down)
+    E: int          # routed experts
+    k: int          # experts chosen per token
+    I: int          # expert intermediate size
+    exp_lo: int     # E8M0 exponent range (inclusive), scale byte = 127 + exp
+    exp_hi: int
+    router_std: float = 0.02
+    zipf_s: float | None = None     # per-expert popularity offset on logits
+    block: int = 0                  # >0: tokens drawn in correlated blocks
+    noise: float = 0.5              # correlated blocks: x = base + noise * n
+    shared: int = 1                 # shared experts (always weight 1)
+    desc: str = field(default="", compare=False)
+
+    @property
+    def R(self) -> int:
+        return self.T * self.k
+
+
+WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny", 0, T=8, H=256, E=16, k=2, I=128, exp_lo=-6, exp_hi=-2,
+                 desc="8 tokens, hidden 256, 16 experts top-2 + 1 shared, I=128"),
+        Workload("decode", 1, T=1, H=5120, E=384, k=6, I=2304, exp_lo=-8, exp_hi=-4,
+                 desc="1 token at the real layer shape, 384 experts top-6 + 1 shared"),
+        Workload("spec5", 2, T=5, H=5120, E=384, k=6, I=2304, exp_lo=-8, exp_hi=-4,
+                 block=5,
+                 desc="5-token verification block, correlated tokens"),
+        Workload("prefill2k_zipf", 3, T=2048, H=5120, E=384, k=6, I=2304,
+                 exp_lo=-8, exp_hi=-4, zipf_s=1.1,
+                 desc="2048-token prefill, Zipf(1.1) expert popularity offset"),
+        Workload("prefill16k", 4, T=16384, H=5120, E=384, k=6, I=2304,
+                 exp_lo=-8, exp_hi=-4,
+                 desc="16384-token prefill, uniform router"),
+    ]
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# ---------------------------------------------------------------------------
+# bf16 bit patterns
+# ---------------------------------------------------------------------------
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """fp64 -> fp32 (RNE) -> bf16 (RNE on the fp32 bits); returns uint16.
+
+    Only finite inputs are expected (normal samples)."""
+    f = np.ascontiguousarray(np.asarray(v, dtype=np.float64).astype(np.float32))
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def _normal_bf16(key, n: int, std: float = 1.0) -> np.ndarray:
+    rng = np.random.default_rng(key)
+    return f64_to_bf16_bits(rng.normal(0.0, std, n))
+
+
+# ---------------------------------------------------------------------------
+# experts
+# ---------------------------------------------------------------------------
+
+def _matrix(key, n_rows: int, k_cols: int, exp_lo: int, exp_hi: int):
+    """Codes [n_rows][k_cols/2] and scales [n_rows][k_cols/32] of one matrix."""
+    if k_cols % 32:
+        raise ValueError("K must be a multiple of 32")
+    rng = np.random.default_rng(key)
+    codes = rng.integers(0, 256, n_rows * (k_cols // 2), dtype=np.uint8)
+    scales = (127 + rng.integers(exp_lo, exp_hi + 1, n_rows * (k_cols // 32))).astype(np.uint8)
+    return codes.reshape(n_rows, k_cols // 2), scales.reshape(n_rows, k_cols // 32)
+
+
+def gen_expert(w: Workload, seed: int, e: int, copy: int = 0) -> dict:
+    """The six arrays of expert e (e == w.E is the shared expert).
+
+    gate/up: [I][H/2] codes, [I][H/32] scales; down: [H][I/2], [H][I/32].
+    Row-major along the reduction dimension K; byte b of a row holds
+    elements 2b (low nibble) and 2b+1 (high nibble)."""
+    base = [seed, w.cfg_id, 0, copy, e]
+    gc, gs = _matrix(base + [0], w.I, w.H, w.exp_lo, w.exp_hi)
+    uc, us = _matrix(base + [1], w.I, w.H, w.exp_lo, w.exp_hi)
+    dc, ds = _matrix(base + [2], w.H, w.I, w.exp_lo, w.exp_hi)
+    return dict(gate_codes=gc, gate_scales=gs, up_codes=uc, up_scales=us,
+                down_codes=dc, down_scales=ds)
+
+
+def bank_shapes(E: int, H: int, I: int) -> dict:
+    return dict(
+        gate_up_codes=(E, 2, I, H // 2),
+        gate_up_scales=(E, 2, I, H // 32),
+        down_codes=(E, H, I // 2),
+        down_scales=(E, H, I // 32),
+    )
+
+
+def gen_bank(w: Workload, seed: int, copy: int = 0, shared: bool = False,
+             experts=None, threads: int | None = None) -> dict:
+    """Bank arrays in the library's layout.
+
+    gate_up_codes  [E][2][I][H/2]   (matrix 0 = gate, 1 = up)
+    gate_up_scales [E][2][I][H/32]
+    down_codes     [E][H][I/2]
+    down_scales    [E][H][I/32]
+
+    shared=True gives the one-expert bank of the shared expert. `experts`
+    restricts generation to a subset (other slots stay zero)."""
+    E = 1 if shared else w.E
+    arrs = {k: np.zeros(s, dtype=np.uint8) for k, s in bank_shapes(E, w.H, w.I).items()}
+    ids = [0] if shared else (range(w.E) if experts is None else experts)
+
+    def fill(slot: int) -> None:
+        x = gen_expert(w, seed, w.E if shared else slot, copy)
+        arrs["gate_up_codes"][slot, 0] = x["gate_codes"]
+        arrs["gate_up_codes"][slot, 1] = x["up_codes"]
+        arrs["gate_up_scales"][slot, 0] = x["gate_scales"]
+        arrs["gate_up_scales"][slot, 1] = x["up_scales"]
+        arrs["down_codes"][slot] = x["down_codes"]
+        arrs["down_scales"][slot] = x["down_scales"]
+
+    n = threads or _threads()
+    if n > 1 and len(ids) > 1:
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(fill, ids))
+    else:
+        for s in ids:
+            fill(s)
+    arrs.update(E=E, H=w.H, I=w.I)
+    return arrs
+
+
+# ---------------------------------------------------------------------------
+# router, tokens, bias
+# ---------------------------------------------------------------------------
+
+def gen_router(w: Workload, seed: int) -> np.ndarray:
+    """Router weight [E][H] as bf16 bits, N(0, router_std)."""
+    return _normal_bf16([seed, w.cfg_id, 1], w.E * w.H, w.router_std).reshape(w.E, w.H)
+
+
+def gen_tokens(w: Workload, seed: int, call: int = 0, T: int | None = None) -> np.ndarray:
+    """Activations [T][H] as bf16 bits for call number `call` of a pool.
+
+    Independent tokens use stream index call*T + t. Correlated blocks use
+    block index `call`: x_j = base + noise * n_j, sampled in fp64, then
+    rounded once to bf16."""
+    T = w.T if T is None else T
+    if w.block:
+        base = np.random.default_rng([seed, w.cfg_id, 2, call, 0]).normal(0.0, 1.0, w.H)
+        rows = []
+        for j in range(T):
+            n = np.random.default_rng([seed, w.cfg_id, 2, call, j + 1]).normal(0.0, 1.0, w.H)
+            rows.append(f64_to_bf16_bits(base + w.noise * n))
+        return np.stack(rows)
+    out = np.empty((T, w.H), dtype=np.uint16)
+
+    def fill(t: int) -> None:
+        out[t] = _normal_bf16([seed, w.cfg_id, 2, call * T + t], w.H)
+
+    if T > 256:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(T)))
+    else:
+        for t in range(T):
+            fill(t)
+    return out
+
+
+def gen_zipf_bias(w: Workload, seed: int) -> np.ndarray | None:
+    """Per-expert logit offset -s*ln(rank) with a seeded rank permutation.
+
+    Adding ln of a Zipf(s) popularity to a logit multiplies that expert's
+    softmax numerator by rank^-s. Returned as fp32 (both sides consume these
+    exact fp32 values), or None when the workload has no offset."""
+    if w.zipf_s is None:
+        return None
+    rank = np.random.default_rng([seed, w.cfg_id, 3]).permutation(w.E) + 1
+    return (-w.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
+
+
+def gen_inputs(w: Workload, seed: int = 0, call: int = 0, copy: int = 0,
+               with_bank: bool = True) -> dict:
+    """Everything one layer call consumes."""
+    d = dict(workload=w, seed=seed,
+             x=gen_tokens(w, seed, call),
+             w_router=gen_router(w, seed),
+             bias=gen_zipf_bias(w, seed))
+    if with_bank:
+        d["routed"] = gen_bank(w, seed, copy)
+        d["shared"] = gen_bank(w, seed, copy, shared=True)
+    return d
+
