@@ -1,0 +1,192 @@
+/*
+ * moe_mxfp4.h -- C ABI of the routed MXFP4 mixture-of-experts layer on
+ * MI355X (gfx950).
+ *
+ * The layer (DeepSeek-V4.1-Flash's MoE block as the pages describe it):
+ *   384 routed experts with 6 chosen per token plus 1 shared expert
+ *     (ai.rs article on DeepSeek-V4.1-Flash, table in "What V4.1 Flash is,
+ *     in bytes"; FreeToken issue #444, "Architecture delta vs deepseek_v4");
+ *   each expert three 5120 x 2304 FP4 matrices (FreeToken issue #444,
+ *     "Architecture delta vs deepseek_v4") stored as packed E2M1 codes with
+ *     one E8M0 scale per 32 weights (same issue, janit's comment, section 2);
+ *   the shared expert gets the same input and arithmetic as the routed ones
+ *     (ai.rs article, "What remains is the reference rounding itself");
+ *   the gate is a discrete top-k choice whose accumulation order must be
+ *     fixed for runs to be reproducible (same section).
+ * Softmax scoring, renormalised top-k weights and the SwiGLU expert form are
+ * the readings taken where the pages are silent.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All array pointers are DEVICE pointers (HIP), except `bank` structs,
+ *    which live in host memory and hold device pointers.
+ *  - The caller owns every buffer. The library allocates nothing, frees
+ *    nothing and keeps no pointer after a call returns; scratch memory comes
+ *    only from the caller's workspace `ws` (`ws_bytes` long, 16-byte aligned).
+ *    moe_workspace_bytes(T, H, I, E, k) bytes suffice for every call below.
+ *  - Work is enqueued on `stream` and the call returns without waiting; the
+ *    host never synchronises. Results are valid after the stream reaches
+ *    them. Calls on distinct streams with distinct buffers may overlap.
+ *  - bf16 arrays are passed as `const void*` holding bf16 bit patterns.
+ *  - Arguments are validated before anything is enqueued: on a negative
+ *    return nothing was launched. A device fault surfaces at the caller's
+ *    next stream synchronisation. No C++ exception crosses this boundary.
+ *  - T == 0 is valid and does nothing.
+ *  - Results are bitwise reproducible: no floating-point atomics, and every
+ *    sum is taken in a fixed order.
+ *
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), H and I multiples of 32,
+ * 32 <= H <= 8192, 32 <= I <= 4096, T*k < 2^31. Violations return
+ * MOE_ERR_INVALID_ARG (malformed) or MOE_ERR_UNSUPPORTED (outside limits).
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null required pointer, misalignment, bad size */
+  MOE_ERR_UNSUPPORTED = -2, /* well-formed but outside the compiled limits  */
+  MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than the call needs          */
+  MOE_ERR_HIP = -4          /* a kernel launch failed                        */
+};
+
+/*
+ * An MXFP4 expert bank (FreeToken issue #444, janit's comment, section 2:
+ * packed E2M1 codes plus one E8M0 scale per 32 weights, not transposed).
+ *
+ *   gate_up_codes  [E][2][I][H/2]   matrix 0 = gate, 1 = up; K = H
+ *   gate_up_scales [E][2][I][H/32]
+ *   down_codes     [E][H][I/2]      K = I
+ *   down_scales    [E][H][I/32]
+ *
+ * Rows run along the reduction dimension K. Byte b of a row holds element
+ * 2b in its low nibble and 2b+1 in its high nibble. E2M1 codes 0..7 are
+ * +{0, 0.5, 1, 1.5, 2, 3, 4, 6} and 8..15 their negatives; scale byte s
+ * multiplies its 32 elements by 2^(s-127), and s == 255 is NaN (OCP MX).
+ * Code arrays must be 16-byte aligned. The shared expert is a bank with E=1.
+ */
+typedef struct moe_mxfp4_bank {
+  const uint8_t* gate_up_codes;
+  const uint8_t* gate_up_scales;
+  const uint8_t* down_codes;
+  const uint8_t* down_scales;
+  int32_t E, H, I;
+} moe_mxfp4_bank;
+
+/* Workspace bytes that suffice for any call below at these sizes. */
+size_t moe_workspace_bytes(int T, int H, int I, int E, int k);
+
+/* Human-readable name of a return code (static string). */
+const char* moe_status_str(int status);
+
+/*
+ * Router: logits, softmax, top-k with renormalised weights.
+ * The gate picks k experts per token (ai.rs article, "How 502 GB runs on a
+ * 32 GB card": 6 of 384 per layer) and is a discrete switch (same article,
+ * "What remains is the reference rounding itself").
+ *
+ *   x_bf16        [T][H] bf16, 16-byte aligned
+ *   w_router_bf16 [E][H] bf16, 16-byte aligned
+ *   logit_bias    [E] fp32 added to every token's logits, or NULL
+ *   topk_ids      [T][k] int32 out: chosen experts by descending logit;
+ *                 exact ties go to the lower expert id
+ *   topk_w        [T][k] fp32 out: exp(l_j - l_1) / sum_j' exp(l_j' - l_1),
+ *                 i.e. the softmax over all E renormalised over the chosen k
+ *   logits_out    [T][E] fp32 out (x W_r^T + bias, fp32 accumulation), or
+ *                 NULL to keep them in the workspace
+ * Logits accumulate bf16 products exactly in fp32.
+ */
+int moe_router_topk(const void* x_bf16, const void* w_router_bf16,
+                    const float* logit_bias, int T, int H, int E, int k,
+                    int32_t* topk_ids, float* topk_w, float* logits_out,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Bucketing: a stable counting sort of the T*k (token, slot) pairs by
+ * expert id, computed with prefix sums and no atomics. Pairs are taken in
+ * (token, slot) order, so each expert's rows list its tokens ascending. The
+ * pages trace run-to-run differences to slot assignment that depends on
+ * timing (ai.rs article, "What remains is the reference rounding itself");
+ * this order is a pure function of topk_ids.
+ *
+ *   topk_ids       [T][k] int32 in
+ *   expert_offsets [E+1] int32 out: rows of expert e are
+ *                  [expert_offsets[e], expert_offsets[e+1])
+ *   row_token      [T*k] int32 out: token of each row
+ *   inv_row        [T][k] int32 out: row of pair (t, j)
+ * Ids outside [0, E) are dropped: their inv_row entry is -1, they own no
+ * row, and expert_offsets[E] counts only valid pairs.
+ */
+int moe_permute(const int32_t* topk_ids, int T, int k, int E,
+                int32_t* expert_offsets, int32_t* row_token, int32_t* inv_row,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Expert FFN over bucketed rows with MXFP4 weights (FreeToken issue #444,
+ * "Architecture delta vs deepseek_v4" for the 3 x 5120 x 2304 shape; the
+ * SwiGLU form is the reading taken where the pages are silent):
+ *   y_rows[r] = W_down[e] (silu(W_gate[e] x_t) * (W_up[e] x_t)),
+ *   e = the bucket holding r, t = row_token[r], silu(z) = z / (1 + e^-z).
+ * Weights are dequantised exactly; products accumulate in fp32.
+ *
+ *   x_bf16         [T][H] bf16 activations
+ *   bank           routed bank (E experts) or a one-expert bank
+ *   expert_offsets [E+1] int32 from moe_permute; NULL only when bank->E == 1,
+ *                  meaning rows [0, R)
+ *   row_token      [R] int32 in [0, T); NULL means row r reads token r (R <= T).
+ *                  Out-of-range entries and offsets are clamped, never read
+ *                  or written out of bounds (the affected rows are garbage)
+ *   R              number of rows (== expert_offsets[E])
+ *   y_rows         [R][H] fp32 out
+ */
+int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
+                         const int32_t* expert_offsets, const int32_t* row_token,
+                         int T, int R, float* y_rows,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Weighted combine in a fixed order (the pages tie irreproducible outputs to
+ * a varying accumulation order: ai.rs article, "What remains is the
+ * reference rounding itself"):
+ *   out[t] = y_shared[t] + sum_{j = 0..k-1} topk_w[t][j] * y_rows[inv_row[t][j]]
+ * summed in fp32 in the order shown. Pairs with inv_row == -1 add nothing.
+ *
+ *   y_rows [R][H] fp32; inv_row [T][k]; topk_w [T][k];
+ *   y_shared [T][H] fp32 or NULL; out [T][H] fp32 (may not alias inputs).
+ *   R is needed to bounds-check inv_row (entries >= R are an error the
+ *   kernel turns into a NaN row rather than an out-of-bounds read).
+ */
+int moe_combine(const float* y_rows, const int32_t* inv_row, const float* topk_w,
+                const float* y_shared, int T, int k, int H, int R, float* out,
+                hipStream_t stream);
+
+/*
+ * The whole layer: router -> top-k -> bucketing -> routed experts and the
+ * shared expert -> combine, all enqueued on `stream` with no host sync.
+ *
+ *   routed         bank of E routed experts (E, H, I taken from it)
+ *   shared         one-expert bank added with weight 1, or NULL
+ *   out            [T][H] fp32
+ *   topk_ids_out   [T][k] int32 or NULL; topk_w_out [T][k] fp32 or NULL
+ */
+int moe_layer_forward(const void* x_bf16, const void* w_router_bf16,
+                      const float* logit_bias, const moe_mxfp4_bank* routed,
+                      const moe_mxfp4_bank* shared, int T, int k, float* out,
+                      int32_t* topk_ids_out, float* topk_w_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,27 @@
+"""Routed MXFP4 mixture-of-experts layer on MI355X (gfx950).
+
+The layer runs in hand-written HIP kernels behind the C ABI of
+include/moe_mxfp4.h; this package holds those sources (csrc/), their build
+script (build.py) and a ctypes binding (_lib.py) with the same call names.
+"""
+
+from ._lib import (  # noqa: F401
+    Bank,
+    BankTensors,
+    MoeError,
+    MOE_ERR_HIP,
+    MOE_ERR_INVALID_ARG,
+    MOE_ERR_UNSUPPORTED,
+    MOE_ERR_WORKSPACE,
+    MOE_OK,
+    header_functions,
+    lib,
+    moe_combine,
+    moe_expert_ffn_mxfp4,
+    moe_layer_forward,
+    moe_permute,
+    moe_router_topk,
+    moe_workspace_bytes,
+    status_str,
+    workspace,
+)

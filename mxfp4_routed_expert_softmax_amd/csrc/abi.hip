@@ -1,0 +1,258 @@
+// extern "C" entry points: argument validation, workspace layout and launch
+// order. Everything is validated before the first launch, so an error
+// return means nothing was enqueued. The host never synchronises.
+#include "moe_mxfp4.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr int kMaxH = 8192;
+constexpr int kMaxI = 4096;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by the calls. INVALID_ARG for malformed values,
+// UNSUPPORTED for well-formed values outside the compiled limits.
+int check_dims(int T, int H, int E, int k, int I) {
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 32 || I % 32 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || k > kMaxK || H > kMaxH || I > kMaxI) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k >= (1ll << 31) || (long long)T * H >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_bank(const moe_mxfp4_bank* b) {
+  if (!b || !b->gate_up_codes || !b->gate_up_scales || !b->down_codes || !b->down_scales)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(b->gate_up_codes) || !aligned16(b->down_codes)) return MOE_ERR_INVALID_ARG;
+  if (b->E <= 0 || b->H <= 0 || b->I <= 0 || b->H % 32 || b->I % 32) return MOE_ERR_INVALID_ARG;
+  if (b->E > kMaxE || b->H > kMaxH || b->I > kMaxI) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+BankView view(const moe_mxfp4_bank* b) {
+  return BankView{b->gate_up_codes, b->gate_up_scales, b->down_codes, b->down_scales, b->E};
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+// Workspace of moe_layer_forward; the other calls need a subset of it.
+struct LayerWs {
+  float* logits;
+  int32_t* ids;
+  float* w;
+  int32_t* offsets;
+  int32_t* active;
+  int32_t* row_token;
+  int32_t* inv_row;
+  void* perm;
+  float* h;
+  float* h_sh;
+  float* y;
+  float* y_sh;
+  size_t bytes;
+};
+
+LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
+  const size_t R = (size_t)T * k;
+  Carve c(ws);
+  LayerWs L;
+  L.logits = c.take<float>((size_t)T * E);
+  L.ids = c.take<int32_t>(R);
+  L.w = c.take<float>(R);
+  L.offsets = c.take<int32_t>((size_t)E + 1);
+  L.active = c.take<int32_t>((size_t)E);
+  L.row_token = c.take<int32_t>(R);
+  L.inv_row = c.take<int32_t>(R);
+  L.perm = c.take<char>(permute_ws_bytes(T, k, E));
+  L.h = c.take<float>(R * I);
+  L.h_sh = c.take<float>((size_t)T * I);
+  L.y = c.take<float>(R * H);
+  L.y_sh = c.take<float>((size_t)T * H);
+  L.bytes = c.off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(int T, int H, int I, int E, int k) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
+  return layer_ws(nullptr, T, H, I, E, k).bytes;
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int moe_router_topk(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
+                    int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
+                    float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(T, H, E, k, 32);
+  if (st != MOE_OK) return st;
+  if (!x_bf16 || !w_router_bf16 || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_router_bf16)) return MOE_ERR_INVALID_ARG;
+  float* logits = logits_out;
+  if (!logits) {
+    if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < (size_t)T * E * sizeof(float)) return MOE_ERR_WORKSPACE;
+    logits = static_cast<float*>(ws);
+  }
+  if (T == 0) return MOE_OK;
+  launch_router_logits(static_cast<const uint16_t*>(x_bf16),
+                       static_cast<const uint16_t*>(w_router_bf16), logit_bias, T, H, E, logits,
+                       stream);
+  launch_topk(logits, T, E, k, topk_ids, topk_w, stream);
+  return launch_status();
+}
+
+int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                int32_t* row_token, int32_t* inv_row, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  int st = check_dims(T, 32, E, k, 32);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !expert_offsets || !row_token || !inv_row) return MOE_ERR_INVALID_ARG;
+  const size_t need = align_up((size_t)E * sizeof(int32_t)) + permute_ws_bytes(T, k, E);
+  if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  Carve c(ws);
+  int32_t* active = c.take<int32_t>(E);
+  void* perm = c.take<char>(permute_ws_bytes(T, k, E));
+  launch_permute(topk_ids, T, k, E, expert_offsets, row_token, inv_row, active, perm, stream);
+  return launch_status();
+}
+
+int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
+                         const int32_t* expert_offsets, const int32_t* row_token, int T, int R,
+                         float* y_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_bank(bank);
+  if (st != MOE_OK) return st;
+  st = check_dims(T, bank->H, bank->E, 1, bank->I);
+  if (st != MOE_OK) return st;
+  if (R < 0 || !x_bf16 || !y_rows || !aligned16(x_bf16) || !aligned16(y_rows))
+    return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets && bank->E != 1) return MOE_ERR_INVALID_ARG;
+  if (!row_token && R > T) return MOE_ERR_INVALID_ARG;
+  const size_t need = ffn_ws_bytes(T, bank->H, bank->I, R, false);
+  if (need && (!ws || !aligned16(ws))) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (T == 0 || R == 0) return MOE_OK;
+  FfnProblem p{};
+  p.x = static_cast<const uint16_t*>(x_bf16);
+  p.T = T;
+  p.H = bank->H;
+  p.I = bank->I;
+  p.routed = view(bank);
+  p.offsets = expert_offsets;
+  p.active = nullptr;
+  p.row_token = row_token;
+  p.R = R;
+  p.routed_slots = expert_offsets ? (bank->E < R ? bank->E : R) : 1;
+  p.h = static_cast<float*>(ws);
+  p.y = y_rows;
+  p.has_shared = false;
+  launch_expert_ffn(p, stream);
+  return launch_status();
+}
+
+int moe_combine(const float* y_rows, const int32_t* inv_row, const float* topk_w,
+                const float* y_shared, int T, int k, int H, int R, float* out,
+                hipStream_t stream) {
+  int st = check_dims(T, H, k, k, 32);
+  if (st != MOE_OK) return st;
+  if (R < 0 || !inv_row || !topk_w || !out || (R > 0 && !y_rows)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(out) || (y_rows && !aligned16(y_rows)) || (y_shared && !aligned16(y_shared)))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  launch_combine(y_rows, inv_row, topk_w, y_shared, T, k, H, R, out, stream);
+  return launch_status();
+}
+
+int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
+                      const moe_mxfp4_bank* routed, const moe_mxfp4_bank* shared, int T, int k,
+                      float* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  int st = check_bank(routed);
+  if (st != MOE_OK) return st;
+  const int E = routed->E, H = routed->H, I = routed->I;
+  st = check_dims(T, H, E, k, I);
+  if (st != MOE_OK) return st;
+  if (shared) {
+    st = check_bank(shared);
+    if (st != MOE_OK) return st;
+    if (shared->E != 1 || shared->H != H || shared->I != I) return MOE_ERR_INVALID_ARG;
+  }
+  if (!x_bf16 || !w_router_bf16 || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
+    return MOE_ERR_INVALID_ARG;
+  const LayerWs need = layer_ws(nullptr, T, H, I, E, k);
+  if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < need.bytes) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+
+  const LayerWs L = layer_ws(ws, T, H, I, E, k);
+  int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
+  float* w = topk_w_out ? topk_w_out : L.w;
+  const int R = T * k;
+
+  launch_router_logits(static_cast<const uint16_t*>(x_bf16),
+                       static_cast<const uint16_t*>(w_router_bf16), logit_bias, T, H, E, L.logits,
+                       stream);
+  launch_topk(L.logits, T, E, k, ids, w, stream);
+  launch_permute(ids, T, k, E, L.offsets, L.row_token, L.inv_row, L.active, L.perm, stream);
+
+  FfnProblem p{};
+  p.x = static_cast<const uint16_t*>(x_bf16);
+  p.T = T;
+  p.H = H;
+  p.I = I;
+  p.routed = view(routed);
+  p.offsets = L.offsets;
+  p.active = L.active;
+  p.row_token = L.row_token;
+  p.R = R;
+  p.routed_slots = E < R ? E : R;
+  p.h = L.h;
+  p.y = L.y;
+  p.has_shared = shared != nullptr;
+  if (shared) {
+    p.shared = view(shared);
+    p.h_sh = L.h_sh;
+    p.y_sh = L.y_sh;
+  }
+  launch_expert_ffn(p, stream);
+  launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
+  return launch_status();
+}
+
+}  // extern "C"

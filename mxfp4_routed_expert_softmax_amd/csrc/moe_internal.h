@@ -1,0 +1,62 @@
+// Internal launchers behind the C ABI. Arguments are already validated by
+// the entry points; each launcher only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Token counts up to this use the GEMV router; above it the MFMA GEMM.
+constexpr int kRouterGemvMaxT = 16;
+// Pair counts up to this are bucketed by one workgroup.
+constexpr int kPermuteChunk = 2048;
+
+void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
+                          int T, int H, int E, float* logits, hipStream_t s);
+void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                 hipStream_t s);
+
+size_t permute_ws_bytes(int T, int k, int E);
+// `active` [E] receives the ids of experts with rows, ascending, then -1s.
+void launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                    int32_t* row_token, int32_t* inv_row, int32_t* active,
+                    void* ws, hipStream_t s);
+
+// One MXFP4 bank as the kernels see it.
+struct BankView {
+  const uint8_t* gu_codes;
+  const uint8_t* gu_scales;
+  const uint8_t* d_codes;
+  const uint8_t* d_scales;
+  int E;
+};
+
+// Expert FFN over bucketed rows: routed bank rows (offsets/active/row_token)
+// plus, optionally, the shared expert over all T tokens.
+struct FfnProblem {
+  const uint16_t* x;   // [T][H] bf16
+  int T, H, I;
+  BankView routed;
+  const int32_t* offsets;    // [E+1] or null (single expert, rows [0, R))
+  const int32_t* active;     // [E] active expert list or null (derive from offsets)
+  const int32_t* row_token;  // [R] or null (row r is token r)
+  int R;                     // routed rows
+  int routed_slots;          // upper bound of experts with rows
+  float* h;                  // [R][I] fp32 scratch
+  float* y;                  // [R][H] fp32 out
+  bool has_shared;
+  BankView shared;
+  float* h_sh;               // [T][I]
+  float* y_sh;               // [T][H]
+};
+
+size_t ffn_ws_bytes(int T, int H, int I, int R, bool shared);
+void launch_expert_ffn(const FfnProblem& p, hipStream_t s);
+
+void launch_combine(const float* y_rows, const int32_t* inv_row, const float* w,
+                    const float* y_shared, int T, int k, int H, int R, float* out,
+                    hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,195 @@
+// Router: logits = x W_r^T (+ bias) and the softmax top-k selection.
+//
+// The gate chooses k of E experts per token (ai.rs article on
+// DeepSeek-V4.1-Flash, "How 502 GB runs on a 32 GB card") and acts as a
+// switch whose choice amplifies rounding (same article, "What remains is the
+// reference rounding itself"), so the selection here is exact on the fp32
+// logits with a fixed tie rule: larger logit first, equal logits -> lower id.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Small T: one wave per expert row, 16-byte loads of W_r, fp32 dot products.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
+  const int lane = lane_id();
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int nv = H >> 3;  // 16-byte vectors per row
+  const uint4* wrow = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
+  const float b = bias ? bias[e] : 0.0f;
+  for (int t0 = 0; t0 < T; t0 += 4) {
+    const int nt = min(4, T - t0);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 5
+    for (int c = lane; c < nv; c += kWave) {
+      const uint4 w = wrow[c];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < nt) {
+          const uint4 xv = reinterpret_cast<const uint4*>(x + (size_t)(t0 + t) * H)[c];
+          acc[t] = dot8_bf16(w, xv, acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0 && t < nt) logits[(size_t)(t0 + t) * E + e] = s + b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large T: bf16 MFMA GEMM, C[T][E] = X[T][H] W[E][H]^T. A workgroup of four
+// waves owns a 128 x 128 tile; each wave a 64 x 64 sub-tile made of 4 x 4
+// v_mfma_f32_16x16x32_bf16 blocks. Both operands are K-contiguous, so every
+// lane loads 8 consecutive bf16 (16 bytes) of one row per operand and K step.
+// A and B use the same (lane group -> K offset) assignment, which is all a
+// dot product needs; the output layout is lane l, element v ->
+// (row 4*(l/16) + v, column l%16) of each 16 x 16 block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * 128 + (wave >> 1) * 64;
+  const int n0 = blockIdx.y * 128 + (wave & 1) * 64;
+  const int r16 = lane & 15, kg = (lane >> 4) * 8;
+
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = min(m0 + 16 * i + r16, T - 1);
+    const int n = min(n0 + 16 * i + r16, E - 1);
+    arow[i] = x + (size_t)m * H + kg;
+    brow[i] = wr + (size_t)n * H + kg;
+  }
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    bf16x8_t a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *reinterpret_cast<const bf16x8_t*>(arow[i] + k0);
+      b[i] = *reinterpret_cast<const bf16x8_t*>(brow[i] + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 16 * j + r16;
+    if (n >= E) continue;
+    const float bn = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 16 * i + 4 * (lane >> 4) + v;
+        if (m < T) logits[(size_t)m * E + n] = acc[i][j][v] + bn;
+      }
+  }
+}
+
+void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
+                          int T, int H, int E, float* logits, hipStream_t s) {
+  if (T <= kRouterGemvMaxT) {
+    hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4), dim3(256), 0, s,
+                       x, wr, bias, T, H, E, logits);
+  } else {
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 127) / 128, (E + 127) / 128),
+                       dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k: one wave per token. Lane l holds logits l, l+64, ... (E <= 1024, so
+// at most 16 per lane). Each of the k rounds takes the lane-local best
+// untaken entry, then a butterfly argmax across the wave under the order
+// (larger value, then lower id); the winner's owner marks it taken. Weights
+// are exp(l_j - l_1) normalised over the chosen k (the full-softmax
+// normaliser cancels). NaN logits rank as -inf.
+// ---------------------------------------------------------------------------
+constexpr int kTopkMaxPerLane = 16;
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T,
+                                                   int E, int k, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* L = logits + (size_t)t * E;
+  float v[kTopkMaxPerLane];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    const int e = lane + kWave * i;
+    float val = -INFINITY;
+    if (e < E) {
+      val = L[e];
+      val = (val != val) ? -INFINITY : val;
+    } else {
+      taken |= 1u << i;
+    }
+    v[i] = val;
+  }
+  float my_val = 0.0f, top = 0.0f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+      const int e = lane + kWave * i;
+      if (!((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+    if (lane == j) {
+      my_val = bv;
+      my_id = bi;
+    }
+    if (j == 0) top = bv;
+  }
+  const float z = (lane < k) ? expf(my_val - top) : 0.0f;
+  const float sum = wave_sum(z);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my_id;
+    w[(size_t)t * k + lane] = z / sum;
+  }
+}
+
+void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                 hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+}
+
+}  // namespace moe

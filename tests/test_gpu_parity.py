@@ -1,0 +1,367 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every test runs the library on cuda:0 and compares with oracle values
+computed on the CPU from the same seeded bits. Sub-steps are compared one by
+one (logits, ids, weights, bucketing, per-row expert outputs, the combined
+output), not just the final tensor.
+"""
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import moe as O
+from tests import _helpers as HP
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+M = pytest.importorskip("mxfp4_routed_expert_softmax_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    M.lib()  # fails loudly when the library is not built
+    yield
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------
+
+def run_router(w, x_bits, wr_bits, bias, k=None):
+    k = w.k if k is None else k
+    T = x_bits.shape[0]
+    x, wr = HP.to_dev(x_bits), HP.to_dev(wr_bits)
+    b = None if bias is None else HP.to_dev(bias)
+    ids = torch.empty((T, k), dtype=torch.int32, device=HP.dev())
+    wt = torch.empty((T, k), dtype=torch.float32, device=HP.dev())
+    lg = torch.empty((T, w.E), dtype=torch.float32, device=HP.dev())
+    M.moe_router_topk(x, wr, b, k, ids, wt, lg, None)
+    return _np(lg), _np(ids), _np(wt)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "spec5", "prefill2k_zipf", "prefill16k"])
+def test_router_topk_matches_oracle(name):
+    w = S.get(name)
+    x = S.gen_tokens(w, 0)
+    wr = S.gen_router(w, 0)
+    bias = S.gen_zipf_bias(w, 0)
+    ref = O.route(x, wr, bias, w.k)
+    lg, ids, wt = run_router(w, x, wr, bias)
+    L = ref["logits"]
+    err = np.abs(lg - L).max() / np.abs(L).max()
+    assert err < 1e-5, err
+    HP.check_routing(ref, ids, wt, w.k)
+
+
+def test_router_zero_weights_tie_to_lowest_ids():
+    w = S.get("tiny")
+    x = S.gen_tokens(w, 0)
+    wr = np.zeros((w.E, w.H), np.uint16)
+    for k in (1, 2, w.E):
+        _, ids, wt = run_router(w, x, wr, None, k)
+        assert np.all(ids == np.arange(k)[None, :])
+        assert np.allclose(wt, 1.0 / k, rtol=1e-6)
+
+
+def test_router_bias_only_and_k_equals_e():
+    w = S.get("tiny")
+    x = np.zeros((3, w.H), np.uint16)
+    bias = np.random.default_rng(2).normal(size=w.E).astype(np.float32)
+    ref = O.route(x, S.gen_router(w, 0), bias, w.E)
+    _, ids, wt = run_router(w, x, S.gen_router(w, 0), bias, w.E)
+    assert np.array_equal(ids, ref["ids"])
+    assert np.allclose(wt, ref["w"], atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Bucketing
+# ---------------------------------------------------------------------------
+
+def run_permute(ids_np, E):
+    T, k = ids_np.shape
+    ids = HP.to_dev(ids_np.astype(np.int32))
+    off = torch.empty(E + 1, dtype=torch.int32, device=HP.dev())
+    rt = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device=HP.dev())
+    inv = torch.empty((T, k), dtype=torch.int32, device=HP.dev())
+    ws = M.workspace(T, 32, 32, E, k, HP.dev())
+    M.moe_permute(ids, E, off, rt, inv, ws)
+    return _np(off), _np(rt)[: T * k], _np(inv)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 384, 6), (5, 384, 6), (8, 16, 2), (341, 384, 6),
+                                   (342, 384, 6), (2048, 384, 6), (16384, 384, 6),
+                                   (1000, 1024, 8), (37, 1, 1)])
+def test_permute_bit_exact(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    off, rt, inv = run_permute(ids, E)
+    roff, rrt, rinv = O.permute(ids, E)
+    assert np.array_equal(off, roff)
+    assert np.array_equal(rt, rrt)
+    assert np.array_equal(inv, rinv)
+
+
+def test_permute_skewed_and_invalid_ids():
+    rng = np.random.default_rng(11)
+    T, E, k = 3000, 384, 6
+    ids = np.stack([np.sort(rng.choice(20, size=k, replace=False))[::-1] for _ in range(T)])
+    ids[5, 2] = -1
+    ids[2999, 0] = E + 3
+    off, rt, inv = run_permute(ids, E)
+    valid = (ids >= 0) & (ids < E)
+    clean = np.where(valid, ids, 0)
+    roff, _, _ = O.permute(clean, E)
+    assert off[E] == valid.sum()
+    assert inv[5, 2] == -1 and inv[2999, 0] == -1
+    # the valid pairs are bucketed exactly as the oracle buckets them alone
+    for e in range(E):
+        toks = rt[off[e]:off[e + 1]]
+        ref_t = [t for t in range(T) if e in ids[t]]
+        assert toks.tolist() == ref_t
+    for t in range(T):
+        for j in range(k):
+            if valid[t, j]:
+                assert rt[inv[t, j]] == t and off[ids[t, j]] <= inv[t, j] < off[ids[t, j] + 1]
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN
+# ---------------------------------------------------------------------------
+
+def run_ffn(x_bits, bank_np, offsets, row_token, R):
+    x = HP.to_dev(x_bits)
+    bank = HP.bank_to_dev(bank_np)
+    off = None if offsets is None else HP.to_dev(np.asarray(offsets, np.int32))
+    rt = None if row_token is None else HP.to_dev(np.asarray(row_token, np.int32))
+    y = torch.full((max(R, 1), bank.H), float("nan"), dtype=torch.float32, device=HP.dev())
+    ws = torch.empty(R * bank.I * 4 + 256, dtype=torch.uint8, device=HP.dev())
+    M.moe_expert_ffn_mxfp4(x, bank, off, rt, R, y, ws)
+    return _np(y)[:R]
+
+
+def test_ffn_tiny_rows_match_oracle():
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    r = O.route(d["x"], d["w_router"], None, w.k)
+    y = run_ffn(d["x"], d["routed"], r["offsets"], r["row_token"], w.R)
+    ref = O.expert_rows(r["x"], d["routed"], r["offsets"], r["row_token"])
+    for row in range(w.R):
+        assert HP.rel_l2(y[row], ref[row]) < 1e-5, row
+    ysh = run_ffn(d["x"], d["shared"], None, None, w.T)
+    assert HP.rel_l2(ysh, O.shared_out(r["x"], d["shared"])) < 1e-5
+
+
+def _identity_bank(n, up_codes=None, up_scales=None):
+    codes = np.zeros((n, n // 2), np.uint8)
+    for i in range(n):
+        codes[i, i // 2] = 0x02 if i % 2 == 0 else 0x20
+    one = np.full((n, n // 32), 127, np.uint8)
+    uc = codes if up_codes is None else up_codes
+    us = one if up_scales is None else up_scales
+    return dict(gate_up_codes=np.stack([codes, uc])[None].copy(),
+                gate_up_scales=np.stack([one, us])[None].copy(),
+                down_codes=codes[None].copy(), down_scales=one[None].copy())
+
+
+def test_ffn_identity_probe_gives_silu_x_times_x():
+    n = 64
+    x_bits = S.f64_to_bf16_bits(np.random.default_rng(9).normal(0, 2, (6, n)))
+    y = run_ffn(x_bits, _identity_bank(n), None, None, 6)
+    x = O.bf16_to_f64(x_bits)
+    ref = x * x / (1 + np.exp(-x))
+    assert np.allclose(y, ref, rtol=2e-6, atol=1e-30)
+
+
+def test_ffn_decodes_every_code_and_scale_exactly():
+    # gate rows are 1.0 at column k0 and x is one-hot at k0, so g = 1 and
+    # h[n] = silu(1) * W_up[n][k0]; down is the identity, so y[n] = h[n].
+    n = 256
+    rng = np.random.default_rng(3)
+    for k0 in (0, 1, 77, 255):
+        gate = np.zeros((n, n // 2), np.uint8)
+        gate[:, k0 // 2] = 0x02 if k0 % 2 == 0 else 0x20
+        up = np.zeros((n, n // 2), np.uint8)
+        codes = np.arange(n) % 16
+        nib = codes if k0 % 2 == 0 else codes << 4
+        up[:, k0 // 2] = nib.astype(np.uint8)
+        up_sc = np.full((n, n // 32), 127, np.uint8)
+        up_sc[:, k0 // 32] = rng.choice([100, 119, 123, 124, 127, 128, 131, 150], size=n)
+        bank = _identity_bank(n, up, up_sc)
+        bank["gate_up_codes"][0, 0] = gate
+        x = np.zeros((1, n), np.uint16)
+        x[0, k0] = 0x3F80  # 1.0
+        y = run_ffn(x, bank, None, None, 1)[0]
+        ref = O.expert_ffn(O.bf16_to_f64(x), *O.expert_weights(bank, 0))[0]
+        vals = O.E2M1_TABLE[codes] * np.ldexp(1.0, up_sc[:, k0 // 32].astype(int) - 127)
+        assert np.allclose(ref, vals / (1 + np.exp(-1.0)), rtol=1e-15)
+        assert np.allclose(y, ref, rtol=1e-6, atol=0), k0
+        assert np.array_equal(np.signbit(y), np.signbit(ref))
+
+
+def test_ffn_nan_scale_propagates():
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    sh = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d["shared"].items()}
+    sh["down_scales"][0, 5, 1] = 255
+    y = run_ffn(d["x"], sh, None, None, w.T)
+    assert np.all(np.isnan(y[:, 5])) and np.all(np.isfinite(np.delete(y, 5, axis=1)))
+
+
+# ---------------------------------------------------------------------------
+# Combine
+# ---------------------------------------------------------------------------
+
+def test_combine_fixed_order_matches_oracle():
+    rng = np.random.default_rng(4)
+    T, k, H = 37, 6, 5120
+    R = T * k
+    y = rng.normal(size=(R, H)).astype(np.float32)
+    inv = rng.permutation(R).reshape(T, k).astype(np.int32)
+    wts = rng.random((T, k)).astype(np.float32)
+    ysh = rng.normal(size=(T, H)).astype(np.float32)
+    out = torch.empty((T, H), dtype=torch.float32, device=HP.dev())
+    M.moe_combine(HP.to_dev(y), HP.to_dev(inv), HP.to_dev(wts), HP.to_dev(ysh), out)
+    ref = O.combine(y.astype(np.float64), inv, wts.astype(np.float64), ysh.astype(np.float64))
+    assert HP.rel_l2(_np(out), ref) < 1e-6
+    M.moe_combine(HP.to_dev(y), HP.to_dev(inv), HP.to_dev(wts), None, out)
+    assert HP.rel_l2(_np(out), O.combine(y.astype(np.float64), inv, wts.astype(np.float64))) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+
+def run_layer(x_bits, wr_bits, bias, routed_dev, shared_dev, k):
+    T = x_bits.shape[0]
+    x, wr = HP.to_dev(x_bits), HP.to_dev(wr_bits)
+    b = None if bias is None else HP.to_dev(bias)
+    out = torch.empty((T, routed_dev.H), dtype=torch.float32, device=HP.dev())
+    ids = torch.empty((T, k), dtype=torch.int32, device=HP.dev())
+    wt = torch.empty((T, k), dtype=torch.float32, device=HP.dev())
+    ws = M.workspace(T, routed_dev.H, routed_dev.I, routed_dev.E, k, HP.dev())
+    M.moe_layer_forward(x, wr, b, routed_dev, shared_dev, k, out, ids, wt, ws)
+    return _np(out), _np(ids), _np(wt)
+
+
+def _layer_parity(w, x_bits, wr, bias, routed, shared, tokens=None):
+    ref = O.layer(x_bits, wr, bias, routed, shared, w.k, tokens=tokens)
+    out, ids, wt = run_layer(x_bits, wr, bias, HP.bank_to_dev(routed),
+                             None if shared is None else HP.bank_to_dev(shared), w.k)
+    tok = ref["tokens"]
+    alt = HP.check_routing(ref, ids, wt, w.k)
+    ref_out = HP.reference_rows(ref, routed, shared, tok, alt)
+    err = HP.rel_l2(out[tok], ref_out)
+    print(f"{w.name}: rel-L2 {err:.3e} over {len(tok)} tokens; near-tie swaps {len(alt)}")
+    assert err <= HP.OUT_TOL
+    return err
+
+
+def test_layer_tiny():
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    err = _layer_parity(w, d["x"], d["w_router"], None, d["routed"], d["shared"])
+    assert err < 1e-5          # fp32 accumulation of exact products
+
+
+def test_layer_tiny_without_shared_and_with_bias():
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    bias = np.linspace(-1, 1, w.E).astype(np.float32)
+    _layer_parity(w, d["x"], d["w_router"], bias, d["routed"], None)
+
+
+def _selected_ids(w, x, wr, bias):
+    """Experts the oracle selects, plus every near-tie alternative."""
+    r = O.route(x, wr, bias, w.k)
+    sel = set(r["ids"].reshape(-1).tolist())
+    for t in range(x.shape[0]):
+        if r["margin"][t] <= HP.MARGIN:
+            for c in O.near_tie_candidates(r["logits"][t], w.k):
+                sel |= set(c)
+    return sorted(sel)
+
+
+def _selected_bank(w, x, wr, bias):
+    """Bank with only the selected experts generated (others stay zero): the
+    layer must read nothing else."""
+    sel = _selected_ids(w, x, wr, bias)
+    return S.gen_bank(w, 0, experts=sel), sel
+
+
+@pytest.mark.parametrize("name", ["decode", "spec5"])
+def test_layer_small_batch_real_shape(name):
+    w = S.get(name)
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    routed, sel = _selected_bank(w, x, wr, None)
+    shared = S.gen_bank(w, 0, shared=True)
+    if name == "spec5":
+        print(f"spec5 union of routed experts: {len(sel)} of {w.T * w.k}")
+    _layer_parity(w, x, wr, None, routed, shared)
+
+
+def test_layer_decode_token_pool_real_shape():
+    # several decode tokens of the benchmark's pool, as independent calls
+    w = S.get("decode")
+    wr = S.gen_router(w, 0)
+    xs = [S.gen_tokens(w, 0, call=c) for c in (1, 2, 3)]
+    sel = sorted(set().union(*[_selected_ids(w, x, wr, None) for x in xs]))
+    routed = S.gen_bank(w, 0, experts=sel)
+    shared = S.gen_bank(w, 0, shared=True)
+    for x in xs:
+        _layer_parity(w, x, wr, None, routed, shared)
+
+
+def test_layer_is_bitwise_deterministic():
+    w = S.get("spec5")
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    routed, _ = _selected_bank(w, x, wr, None)
+    rd, sd = HP.bank_to_dev(routed), HP.bank_to_dev(S.gen_bank(w, 0, shared=True))
+    a = run_layer(x, wr, None, rd, sd, w.k)
+    b = run_layer(x, wr, None, rd, sd, w.k)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+@pytest.mark.parametrize("name,tokens", [
+    ("prefill2k_zipf", [0, 1, 2, 511, 1024, 1500, 2046, 2047]),
+    ("prefill16k", [0, 1, 4097, 8191, 12000, 16383]),
+])
+def test_layer_prefill_sampled_tokens(name, tokens):
+    w = S.get(name)
+    x, wr, bias = S.gen_tokens(w, 0), S.gen_router(w, 0), S.gen_zipf_bias(w, 0)
+    routed = S.gen_bank(w, 0)
+    shared = S.gen_bank(w, 0, shared=True)
+    _layer_parity(w, x, wr, bias, routed, shared, tokens=tokens)
+
+
+# ---------------------------------------------------------------------------
+# ABI behaviour on the device
+# ---------------------------------------------------------------------------
+
+def test_abi_zero_tokens_is_a_noop_and_small_workspace_is_rejected():
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    rd, sd = HP.bank_to_dev(d["routed"]), HP.bank_to_dev(d["shared"])
+    x = HP.to_dev(d["x"])
+    wr = HP.to_dev(d["w_router"])
+    out = torch.full((w.T, w.H), 3.0, dtype=torch.float32, device=HP.dev())
+    ws = M.workspace(w.T, w.H, w.I, w.E, w.k, HP.dev())
+    M.moe_layer_forward(x[:0], wr, None, rd, sd, w.k, out[:0], ws=ws)
+    assert torch.all(out == 3.0)
+    small = ws[: M.moe_workspace_bytes(w.T, w.H, w.I, w.E, w.k) - 256]
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_layer_forward(x, wr, None, rd, sd, w.k, out, ws=small)
+    assert ei.value.status == M.MOE_ERR_WORKSPACE
+    assert torch.all(out == 3.0)
