@@ -23,7 +23,8 @@
  *  - The caller owns every buffer. The library allocates nothing, frees
  *    nothing and keeps no pointer after a call returns; scratch memory comes
  *    only from the caller's workspace `ws` (`ws_bytes` long, 16-byte aligned).
- *    moe_workspace_bytes(T, H, I, E, k) bytes suffice for every call below.
+ *    moe_workspace_bytes(T, H, I, E, k) bytes suffice for every call below
+ *    (for moe_expert_ffn_mxfp4 with R rows, take k = ceil(R / T)).
  *  - Work is enqueued on `stream` and the call returns without waiting; the
  *    host never synchronises. Results are valid after the stream reaches
  *    them. Calls on distinct streams with distinct buffers may overlap.
@@ -31,7 +32,8 @@
  *  - Arguments are validated before anything is enqueued: on a negative
  *    return nothing was launched. A device fault surfaces at the caller's
  *    next stream synchronisation. No C++ exception crosses this boundary.
- *  - T == 0 is valid and does nothing.
+ *  - T == 0 is valid and does nothing (data pointers may then be NULL; the
+ *    sizes and banks are still validated).
  *  - Results are bitwise reproducible: no floating-point atomics, and every
  *    sum is taken in a fixed order.
  *

@@ -13,7 +13,8 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_mxfp4.so")
+# MOE_MXFP4_LIB points the binding at another build of the same library
+LIB_PATH = os.environ.get("MOE_MXFP4_LIB") or os.path.join(PKG, "libmoe_mxfp4.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe_mxfp4.h")
 
 MOE_OK = 0

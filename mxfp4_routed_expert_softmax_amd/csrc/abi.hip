@@ -100,7 +100,12 @@ extern "C" {
 
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
-  return layer_ws(nullptr, T, H, I, E, k).bytes;
+  const int R = T * k;
+  size_t b = layer_ws(nullptr, T, H, I, E, k).bytes;
+  const size_t d = decode_ws_bytes(T, H, I, E, k, R, false, true);
+  const size_t f = decode_ws_bytes(T, H, I, E, k, R, true, false);
+  b = b > d ? b : d;
+  return b > f ? b : f;
 }
 
 const char* moe_status_str(int status) {
@@ -119,6 +124,7 @@ int moe_router_topk(const void* x_bf16, const void* w_router_bf16, const float* 
                     float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(T, H, E, k, 32);
   if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
   if (!x_bf16 || !w_router_bf16 || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16)) return MOE_ERR_INVALID_ARG;
   float* logits = logits_out;
@@ -127,7 +133,6 @@ int moe_router_topk(const void* x_bf16, const void* w_router_bf16, const float* 
     if (ws_bytes < (size_t)T * E * sizeof(float)) return MOE_ERR_WORKSPACE;
     logits = static_cast<float*>(ws);
   }
-  if (T == 0) return MOE_OK;
   launch_router_logits(static_cast<const uint16_t*>(x_bf16),
                        static_cast<const uint16_t*>(w_router_bf16), logit_bias, T, H, E, logits,
                        stream);
@@ -140,11 +145,11 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_of
                 hipStream_t stream) {
   int st = check_dims(T, 32, E, k, 32);
   if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
   if (!topk_ids || !expert_offsets || !row_token || !inv_row) return MOE_ERR_INVALID_ARG;
   const size_t need = align_up((size_t)E * sizeof(int32_t)) + permute_ws_bytes(T, k, E);
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-  if (T == 0) return MOE_OK;
   Carve c(ws);
   int32_t* active = c.take<int32_t>(E);
   void* perm = c.take<char>(permute_ws_bytes(T, k, E));
@@ -159,14 +164,34 @@ int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
   if (st != MOE_OK) return st;
   st = check_dims(T, bank->H, bank->E, 1, bank->I);
   if (st != MOE_OK) return st;
-  if (R < 0 || !x_bf16 || !y_rows || !aligned16(x_bf16) || !aligned16(y_rows))
+  if (R < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0 || R == 0) return MOE_OK;
+  if (!x_bf16 || !y_rows || !aligned16(x_bf16) || !aligned16(y_rows))
     return MOE_ERR_INVALID_ARG;
   if (!expert_offsets && bank->E != 1) return MOE_ERR_INVALID_ARG;
   if (!row_token && R > T) return MOE_ERR_INVALID_ARG;
-  const size_t need = ffn_ws_bytes(T, bank->H, bank->I, R, false);
+  const bool few = R <= kDecodeFfnMaxR;
+  const size_t need = few ? decode_ws_bytes(T, bank->H, bank->I, bank->E, 1, R, true, false)
+                          : ffn_ws_bytes(T, bank->H, bank->I, R, false);
   if (need && (!ws || !aligned16(ws))) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-  if (T == 0 || R == 0) return MOE_OK;
+  if (few) {
+    DecodeLaunch d{};
+    d.ffn_mode = 1;
+    d.x = static_cast<const uint16_t*>(x_bf16);
+    d.routed = view(bank);
+    d.T = T;
+    d.H = bank->H;
+    d.I = bank->I;
+    d.E = bank->E;
+    d.k = 1;
+    d.R = R;
+    d.offsets = expert_offsets;
+    d.row_token = row_token;
+    d.y_rows = y_rows;
+    launch_decode(d, ws, stream);
+    return launch_status();
+  }
   FfnProblem p{};
   p.x = static_cast<const uint16_t*>(x_bf16);
   p.T = T;
@@ -190,10 +215,11 @@ int moe_combine(const float* y_rows, const int32_t* inv_row, const float* topk_w
                 hipStream_t stream) {
   int st = check_dims(T, H, k, k, 32);
   if (st != MOE_OK) return st;
-  if (R < 0 || !inv_row || !topk_w || !out || (R > 0 && !y_rows)) return MOE_ERR_INVALID_ARG;
+  if (R < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!inv_row || !topk_w || !out || (R > 0 && !y_rows)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(out) || (y_rows && !aligned16(y_rows)) || (y_shared && !aligned16(y_shared)))
     return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
   launch_combine(y_rows, inv_row, topk_w, y_shared, T, k, H, R, out, stream);
   return launch_status();
 }
@@ -212,13 +238,36 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float
     if (st != MOE_OK) return st;
     if (shared->E != 1 || shared->H != H || shared->I != I) return MOE_ERR_INVALID_ARG;
   }
+  if (T == 0) return MOE_OK;
   if (!x_bf16 || !w_router_bf16 || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
-  const LayerWs need = layer_ws(nullptr, T, H, I, E, k);
+  const bool few = T <= kDecodeMaxT;
+  const size_t need = few ? decode_ws_bytes(T, H, I, E, k, T * k, false, shared != nullptr)
+                          : layer_ws(nullptr, T, H, I, E, k).bytes;
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < need.bytes) return MOE_ERR_WORKSPACE;
-  if (T == 0) return MOE_OK;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (few) {
+    DecodeLaunch d{};
+    d.ffn_mode = 0;
+    d.x = static_cast<const uint16_t*>(x_bf16);
+    d.wr = static_cast<const uint16_t*>(w_router_bf16);
+    d.bias = logit_bias;
+    d.routed = view(routed);
+    d.has_shared = shared != nullptr;
+    if (shared) d.shared = view(shared);
+    d.T = T;
+    d.H = H;
+    d.I = I;
+    d.E = E;
+    d.k = k;
+    d.R = T * k;
+    d.out = out;
+    d.ids_out = topk_ids_out;
+    d.w_out = topk_w_out;
+    launch_decode(d, ws, stream);
+    return launch_status();
+  }
 
   const LayerWs L = layer_ws(ws, T, H, I, E, k);
   int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;

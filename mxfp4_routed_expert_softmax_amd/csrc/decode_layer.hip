@@ -1,0 +1,978 @@
+// The layer for a few tokens (decode, verification blocks) in three launches.
+//
+// Decode moves ~132 MB of expert weights per token, about 17 us of HBM time
+// at 8 TB/s; the pages' own decode model is bandwidth over routed expert
+// bytes per token (FreeToken issue #444, janit's comment, section 1), and a
+// verification block pays for the union of its tokens' experts (ai.rs
+// article on DeepSeek-V4.1-Flash, "The draft head that works and does not
+// pay"). Every launch boundary costs a few microseconds, and inside a launch
+// what costs is any chain of dependent round trips a workgroup waits
+// through. So:
+//
+//   route   [router rows][routing][shared expert gate/up]
+//   gate/up [routed gate/up items][shared expert down]
+//   down    [routed down items; the last one per column also combines]
+//
+// The shared expert needs no routing, so its gate/up streams while the
+// router and the top-k run, and its down streams with the routed gate/up.
+// Within `route`, the routing workgroup waits for the router workgroups'
+// flags; those have lower indices, and the dispatcher starts workgroups in
+// index order, so they have started and finish: no deadlock whatever the
+// occupancy. A flag holds a 64-bit epoch unique to the launch, so the
+// workspace needs no initialisation; the wait is bounded (on timeout it
+// records the failure in a status word and goes on with whatever logits it
+// has, which cannot make an access go out of bounds). Data crossing
+// workgroups inside a launch (logits, y rows for the combine) moves through
+// agent-scope relaxed atomics, which are performed at the device coherence
+// point, and a producer drains its stores (s_waitcnt) before it raises a
+// flag or bumps a counter, so no cache-wide fence is needed. Data crossing a
+// launch boundary uses plain loads and stores.
+//
+// Gate/up and down items are one-shot workgroups: weight loads first (one
+// batch covers a whole row), then the activations, then the math; nothing
+// waits for another workgroup. The down workgroup that finishes a column of
+// 32 outputs last (a per-column counter, zeroed by `route`) sums that
+// column's shared row and its k routed rows in the fixed order
+// y_shared + w_0 y_0 + ... + w_{k-1} y_{k-1}.
+//
+// moe_expert_ffn_mxfp4 with few rows reuses the gate/up and down kernels
+// behind a one-workgroup kernel that turns caller offsets into the slot
+// table.
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMT = 4;          // token rows staged per pass
+constexpr int kGuLanes = 32;    // gate/up: 32 lanes per row, 2 rows per wave
+constexpr int kGuRows = 8;      // gate/up rows per item
+constexpr int kGuU = 5;         // gate/up chunks per lane per batch (K = 5120 in one)
+constexpr int kDnRows = 32;     // down: 8 lanes per row, 8 rows per wave
+constexpr int kDnU = 9;         // down chunks per lane per batch (K = 2304 in one)
+constexpr int kRouterV = 16;    // router: 16-byte vectors per lane (H <= 8192)
+constexpr long kSpinLimit = 1L << 20;  // polls (with s_sleep) before giving up
+
+constexpr int kLdsGu = kMT * kGuLanes * kGuU * 64;  // bf16 x chunks
+constexpr int kLdsDn = kMT * 8 * kDnU * 128;        // fp32 h chunks
+constexpr int kLdsBytes = kLdsGu > kLdsDn ? kLdsGu : kLdsDn;
+
+// Buffer loads through a resource that spans one weight matrix: 32-bit
+// offsets with immediate strides, and offsets past the end return zero (so
+// the tail of the last row needs no clamp or branch).
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t matrix_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// Coherent accessors for data handed between workgroups of one launch.
+template <class V>
+__device__ __forceinline__ V cld(const V* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class V>
+__device__ __forceinline__ void cst(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copies `total` 16-byte elements into LDS in rounds of kStageB per thread:
+// each round issues all its loads before any store (clamped indices repeat
+// the last element, so there is no branch to sink the loads into).
+constexpr int kStageB = 3;
+template <class V, class Src, class Dst>
+__device__ __forceinline__ void stage_rows(int total, Src src, Dst dst) {
+  for (int base = 0; base < total; base += kStageB * kThreads) {
+    V v[kStageB];
+#pragma unroll
+    for (int i = 0; i < kStageB; ++i) v[i] = src(min(base + (int)threadIdx.x + i * kThreads, total - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kStageB; ++i) dst(min(base + (int)threadIdx.x + i * kThreads, total - 1), v[i]);
+  }
+}
+
+struct Slot {
+  int e;      // expert slot in its bank
+  int row0;   // first row of h / y
+  int m;      // rows
+  bool shared;
+};
+
+}  // namespace
+
+struct DecodeArgs {
+  const uint16_t* x;
+  const uint16_t* wr;
+  const float* bias;
+  BankView routed, shared;
+  int has_shared;
+  int T, H, I, E, k, R;
+  const int32_t* offsets_in;    // FFN mode: caller's bucket offsets
+  const int32_t* row_token_in;  // FFN mode (null = identity)
+  float* out;
+  int32_t* ids_out;
+  float* w_out;
+  float* logits;       // [T][E]
+  float* route_w;      // [T][k]
+  int32_t* tab;        // [1 + 3 * max_slots]: n_slots, expert[], row0[], m[]
+  int32_t* row_token;  // [rows]
+  int32_t* inv_row;    // [T][k]
+  float* h;            // [rows][I]
+  float* y;            // [rows][H]
+  uint64_t* flags;     // [nb_router] router flags
+  int32_t* cnt_dn;     // [dn_items] routed down items finished per column
+  uint64_t epoch;
+  int32_t* status;
+  int max_slots;       // routed slots
+  int rows;            // rows of h and y (routed rows, then T shared rows)
+  int nb_router, gu_items, dn_items;
+};
+
+namespace {
+
+__device__ __forceinline__ int load_nslots(const DecodeArgs& a) {
+  return min(max(a.tab[0], 0), a.max_slots);
+}
+
+// Slot s of the table, every field clamped so that it addresses only the
+// bank and the h / y rows that exist, whatever the table holds.
+__device__ __forceinline__ Slot load_slot(const DecodeArgs& a, int s) {
+  const int32_t* t = a.tab + 1;
+  const int e = min(max(t[s], 0), a.routed.E - 1);
+  const int row0 = min(max(t[a.max_slots + s], 0), a.rows);
+  const int m = min(max(t[2 * a.max_slots + s], 0), a.rows - row0);
+  return Slot{e, row0, m, false};
+}
+
+__device__ __forceinline__ Slot shared_slot(const DecodeArgs& a) {
+  return Slot{0, a.R, a.T, true};
+}
+
+// ---------------------------------------------------------------------------
+// Router rows: one wave per expert row, all row loads in flight at once.
+// ---------------------------------------------------------------------------
+__device__ void router_rows(const DecodeArgs& a, int b) {
+  const int lane = lane_id();
+  const int e = b * 4 + (threadIdx.x >> 6);
+  if (e < a.E) {
+    const int nv = a.H >> 3;
+    const uint4* wrow = reinterpret_cast<const uint4*>(a.wr + (size_t)e * a.H);
+    uint4 wv[kRouterV];
+#pragma unroll
+    for (int i = 0; i < kRouterV; ++i) wv[i] = wrow[min(lane + kWave * i, nv - 1)];
+    const float bb = a.bias ? a.bias[e] : 0.0f;
+    for (int t = 0; t < a.T; ++t) {
+      const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H);
+      uint4 xv[kRouterV];
+#pragma unroll
+      for (int i = 0; i < kRouterV; ++i) xv[i] = xr[min(lane + kWave * i, nv - 1)];
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kRouterV; ++i)
+        if (lane + kWave * i < nv) acc = dot8_bf16(wv[i], xv[i], acc);
+      acc = wave_sum(acc);
+      if (lane == 0) cst(a.logits + (size_t)t * a.E + e, acc + bb);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) cst(a.flags + b, a.epoch);
+}
+
+// ---------------------------------------------------------------------------
+// Routing: top-k per token (one wave per token) and atomic-free bucketing.
+// ---------------------------------------------------------------------------
+
+// Order-preserving key of (logit, expert): a larger key is a larger logit,
+// and among equal logits the lower expert id. NaN ranks as -inf.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  v = (v != v) ? -INFINITY : v;
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xf, 0xf, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xf, 0xf, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Wave-wide maximum of a 64-bit key, returned to every lane: DPP exchanges
+// within each row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror),
+// then the four row maxima through readlane.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  v = dpp_max_step<0x140>(v);  // row_mirror
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    m = x > m ? x : m;
+  }
+  return m;
+}
+
+// Wave-wide top-k of one logit row; lanes < k write ids / weights. Lane l
+// holds experts l, l+64, ... (E <= 1024); each round takes the best untaken
+// key of every lane and the wave maximum of those.
+__device__ void topk_row(const float* L, int E, int k, int* ids, float* w) {
+  const int lane = lane_id();
+  uint64_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = e < E ? topk_key(cld(L + e), e) : 0;  // 0 is below every real key
+  }
+  float my_val = 0.0f, top = 0.0f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
+    const uint64_t win = wave_max_key(best);
+    const int id = (int)(0xffffffffu - (uint32_t)win);
+    uint32_t b = (uint32_t)(win >> 32);
+    b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
+    const float val = __uint_as_float(b);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key[i] == win) key[i] = 0;
+    if (lane == j) {
+      my_val = val;
+      my_id = id;
+    }
+    if (j == 0) top = val;
+  }
+  const float z = (lane < k) ? expf(my_val - top) : 0.0f;
+  const float sum = wave_sum(z);
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = z / sum;
+  }
+}
+
+__device__ void routing(const DecodeArgs& a, char* lds) {
+  // router flags, polled in parallel by this one workgroup
+  for (long it = 0;; ++it) {
+    bool ok = true;
+    for (int i = threadIdx.x; i < a.nb_router; i += kThreads) ok &= cld(a.flags + i) == a.epoch;
+    if (__syncthreads_and(ok)) break;
+    if (it > kSpinLimit) {
+      if (threadIdx.x == 0) cst(a.status, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  const int R = a.R;
+  int* s_ids = reinterpret_cast<int*>(lds);
+  float* s_w = reinterpret_cast<float*>(s_ids + R);
+  int* s_first = reinterpret_cast<int*>(s_w + R);
+  int* s_tmp = s_first + R;
+  for (int t = threadIdx.x >> 6; t < a.T; t += kThreads / kWave)
+    topk_row(a.logits + (size_t)t * a.E, a.E, a.k, s_ids + t * a.k, s_w + t * a.k);
+  __syncthreads();
+  // Stable counting sort by ranks, no atomics: pair p (token p / k) of
+  // expert e goes to row (#pairs with a smaller expert) + (#earlier pairs
+  // with the same expert). The first pair of each expert owns its slot.
+  int n_first = 0;
+  for (int p = threadIdx.x; p < R; p += kThreads) {
+    const int e = s_ids[p];
+    int less = 0, before = 0, same = 0;
+    for (int q = 0; q < R; ++q) {
+      const int f = s_ids[q];
+      less += f < e;
+      same += f == e;
+      before += (f == e) & (q < p);
+    }
+    const int row = less + before;
+    a.row_token[row] = p / a.k;
+    a.inv_row[p] = row;
+    a.route_w[p] = s_w[p];
+    if (a.ids_out) a.ids_out[p] = e;
+    if (a.w_out) a.w_out[p] = s_w[p];
+    s_first[p] = before == 0 ? (less << 11 | same) : -1;  // row0, count (R <= 1024)
+    n_first += before == 0;
+  }
+  int n_act = 0;
+  block_exclusive_scan(n_first, s_tmp, &n_act);
+  int32_t* tex = a.tab + 1;
+  for (int p = threadIdx.x; p < R; p += kThreads) {
+    const int fp = s_first[p];
+    if (fp < 0) continue;
+    const int e = s_ids[p];
+    int slot = 0;
+    for (int q = 0; q < R; ++q) slot += (s_first[q] >= 0) & (s_ids[q] < e);
+    tex[slot] = e;
+    tex[a.max_slots + slot] = fp >> 11;
+    tex[2 * a.max_slots + slot] = fp & 2047;
+  }
+  if (threadIdx.x == 0) a.tab[0] = n_act;
+  for (int i = threadIdx.x; i < a.dn_items; i += kThreads) a.cnt_dn[i] = 0;
+}
+
+// Slot table from caller offsets (FFN mode). Thread i owns experts 4i..4i+3,
+// so a block scan of per-thread counts gives slots in ascending expert order.
+// Buckets are clamped to [0, R]; at most max_slots slots are written.
+__global__ __launch_bounds__(kThreads) void ffn_table_kernel(DecodeArgs a) {
+  __shared__ int s_tmp[32];
+  int cnt[4], lo[4], act = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x * 4 + q;
+    int l = 0, h = 0;
+    if (e < a.E) {
+      if (a.offsets_in) {
+        l = min(max(a.offsets_in[e], 0), a.R);
+        h = min(max(a.offsets_in[e + 1], l), a.R);
+      } else if (e == 0) {
+        h = a.R;
+      }
+    }
+    cnt[q] = h - l;
+    lo[q] = l;
+    act += h > l;
+  }
+  int n_act = 0;
+  int s = block_exclusive_scan(act, s_tmp, &n_act);
+  int32_t* tex = a.tab + 1;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (cnt[q] > 0 && s < a.max_slots) {
+      tex[s] = threadIdx.x * 4 + q;
+      tex[a.max_slots + s] = lo[q];
+      tex[2 * a.max_slots + s] = cnt[q];
+      ++s;
+    }
+  }
+  if (threadIdx.x == 0) a.tab[0] = min(n_act, a.max_slots);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU item: 8 rows. 32 lanes per row (each wave-wide 16-byte
+// load covers 2 rows x 512 contiguous bytes), so a K = 5120 row pair is one
+// batch of 5 chunks per lane; weight loads are issued before the
+// activations are staged. h is written with plain stores (read by a later
+// launch).
+// ---------------------------------------------------------------------------
+template <int MT>
+__device__ void gateup_item(const DecodeArgs& a, const Slot& sd, int rb, uint4* s_x,
+                            const int32_t* rtok) {
+  const BankView bk = sd.shared ? a.shared : a.routed;
+  const int H = a.H, I = a.I;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int n = rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes;
+  const bool row_ok = n < I;
+  const int nr = row_ok ? n : I - 1;
+  const int kc = H >> 5;
+  const uint32_t crow = (uint32_t)H >> 1, srow = (uint32_t)H >> 5;
+  const uint8_t* gbase = bk.gu_codes + (size_t)sd.e * 2 * I * crow;
+  const uint8_t* sbase = bk.gu_scales + (size_t)sd.e * 2 * I * srow;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, I * crow);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)I * crow, I * crow);
+  const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, I * srow);
+  const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)I * srow, I * srow);
+  constexpr int kStride = kGuLanes * kGuU * 4;  // uint4 per staged token row
+
+  for (int t0 = 0; t0 < sd.m; t0 += MT) {
+    const int nt = min(MT, sd.m - t0);
+    float ag[MT], au[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ag[t] = au[t] = 0.0f;
+    for (int c0 = 0; c0 < kc; c0 += kGuLanes * kGuU) {
+      const int cn = min(kc - c0, kGuLanes * kGuU);
+      uint4 wg[kGuU], wu[kGuU];
+      uint32_t sg[kGuU], su[kGuU];
+      // every lane loads (chunks past the row end are unused), so the loads
+      // form one straight-line batch
+      const int co = nr * crow + (c0 + j) * 16, so = nr * srow + c0 + j;
+#pragma unroll
+      for (int u = 0; u < kGuU; ++u) {
+        wg[u] = bload16(rg, co + u * kGuLanes * 16);
+        wu[u] = bload16(ru, co + u * kGuLanes * 16);
+        sg[u] = bload8(rgs, so + u * kGuLanes);
+        su[u] = bload8(rus, so + u * kGuLanes);
+      }
+      __syncthreads();
+      stage_rows<uint4>(
+          nt * cn * 4,
+          [&](int idx) {
+            const int t = idx / (cn * 4), q = idx - t * cn * 4;
+            const int r = sd.row0 + t0 + t;
+            int tok = sd.shared ? r - a.R : (rtok ? rtok[r] : r);
+            tok = min(max(tok, 0), a.T - 1);
+            return reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + c0 * 32)[q];
+          },
+          [&](int idx, uint4 v) {
+            // piece p of chunk c goes to p * K + c: lanes reading consecutive
+            // chunks then read consecutive 16-byte words (no bank conflicts)
+            const int t = idx / (cn * 4), q = idx - t * cn * 4;
+            s_x[t * kStride + (q & 3) * (kGuLanes * kGuU) + (q >> 2)] = v;
+          });
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kGuU; ++u) {
+        const int c = kGuLanes * u + j;
+        if (c < cn) {
+          const float fg = e8m0_to_f32(sg[u]), fu = e8m0_to_f32(su[u]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            if (t < nt) {
+              const uint4* xv = s_x + t * kStride + c;
+              constexpr int P = kGuLanes * kGuU;
+              const uint4 x0 = xv[0], x1 = xv[P], x2 = xv[2 * P], x3 = xv[3 * P];
+              float pg = dot8_fp4_bf16(wg[u].x, x0, 0.0f);
+              pg = dot8_fp4_bf16(wg[u].y, x1, pg);
+              pg = dot8_fp4_bf16(wg[u].z, x2, pg);
+              pg = dot8_fp4_bf16(wg[u].w, x3, pg);
+              float pu = dot8_fp4_bf16(wu[u].x, x0, 0.0f);
+              pu = dot8_fp4_bf16(wu[u].y, x1, pu);
+              pu = dot8_fp4_bf16(wu[u].z, x2, pu);
+              pu = dot8_fp4_bf16(wu[u].w, x3, pu);
+              ag[t] = fmaf(pg, fg, ag[t]);
+              au[t] = fmaf(pu, fu, au[t]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float g = group_sum<kGuLanes>(ag[t]);
+      const float u = group_sum<kGuLanes>(au[t]);
+      if (row_ok && j == 0 && t < nt) a.h[(size_t)(sd.row0 + t0 + t) * I + n] = silu_mul(g, u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down item: 32 output rows, 8 lanes per row (each wave-wide load covers 8
+// whole 128-byte lines), K = 2304 in one batch of 9 chunks per lane; weight
+// loads before the h rows are staged. `coherent` stores y for a consumer in
+// the same launch.
+// ---------------------------------------------------------------------------
+template <int MT>
+__device__ void down_item(const DecodeArgs& a, const Slot& sd, int rb, f32x4_t* s_h, float* y,
+                          bool coherent) {
+  const BankView bk = sd.shared ? a.shared : a.routed;
+  const int H = a.H, I = a.I;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int n = rb * kDnRows + wave * 8 + (lane >> 3);
+  const bool row_ok = n < H;
+  const int nr = row_ok ? n : H - 1;
+  const int kc = I >> 5;
+  const uint32_t crow = (uint32_t)I >> 1, srow = (uint32_t)I >> 5;
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(bk.d_codes + (size_t)sd.e * H * crow, H * crow);
+  const __amdgpu_buffer_rsrc_t rds = matrix_rsrc(bk.d_scales + (size_t)sd.e * H * srow, H * srow);
+  constexpr int kStride = 8 * kDnU * 8;  // f32x4_t per staged row
+
+  for (int t0 = 0; t0 < sd.m; t0 += MT) {
+    const int nt = min(MT, sd.m - t0);
+    float acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
+    for (int c0 = 0; c0 < kc; c0 += 8 * kDnU) {
+      const int cn = min(kc - c0, 8 * kDnU);
+      uint4 wd[kDnU];
+      uint32_t sd8[kDnU];
+      const int co = nr * crow + (c0 + j) * 16, so = nr * srow + c0 + j;
+#pragma unroll
+      for (int u = 0; u < kDnU; ++u) {
+        wd[u] = bload16(rd, co + u * 8 * 16);
+        sd8[u] = bload8(rds, so + u * 8);
+      }
+      __syncthreads();
+      stage_rows<f32x4_t>(
+          nt * cn * 8,
+          [&](int idx) {
+            const int t = idx / (cn * 8), q = idx - t * cn * 8;
+            return reinterpret_cast<const f32x4_t*>(a.h + (size_t)(sd.row0 + t0 + t) * I + c0 * 32)[q];
+          },
+          [&](int idx, f32x4_t v) {
+            const int t = idx / (cn * 8), q = idx - t * cn * 8;
+            s_h[t * kStride + (q & 7) * (8 * kDnU) + (q >> 3)] = v;
+          });
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kDnU; ++u) {
+        const int c = 8 * u + j;
+        if (c < cn) {
+          const float fd = e8m0_to_f32(sd8[u]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            if (t < nt) {
+              const f32x4_t* hv = s_h + t * kStride + c;
+              constexpr int P = 8 * kDnU;
+              float pd = dot8_fp4_f32(wd[u].x, hv[0], hv[P], 0.0f);
+              pd = dot8_fp4_f32(wd[u].y, hv[2 * P], hv[3 * P], pd);
+              pd = dot8_fp4_f32(wd[u].z, hv[4 * P], hv[5 * P], pd);
+              pd = dot8_fp4_f32(wd[u].w, hv[6 * P], hv[7 * P], pd);
+              acc[t] = fmaf(pd, fd, acc[t]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float v = group_sum<8>(acc[t]);
+      if (row_ok && j == 0 && t < nt) {
+        float* p = y + (size_t)(sd.row0 + t0 + t) * H + n;
+        if (coherent)
+          cst(p, v);
+        else
+          *p = v;
+      }
+    }
+  }
+}
+
+// Combine of output columns [32c, 32c + 32): the shared row (written by an
+// earlier launch), then the k routed rows in slot order j = 0..k-1 (written
+// in this launch, hence the coherent loads), one fp32 fma each.
+__device__ void combine_column(const DecodeArgs& a, int c) {
+  const int n = c * kDnRows + (threadIdx.x & 31);
+  if (n >= a.H) return;
+  for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
+    float v = a.has_shared ? a.y[(size_t)(a.R + t) * a.H + n] : 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+      const int r = min(max(a.inv_row[t * a.k + j], 0), a.R - 1);
+      v = fmaf(a.route_w[t * a.k + j], cld(a.y + (size_t)r * a.H + n), v);
+    }
+    a.out[(size_t)t * a.H + n] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One token: streaming gate/up and down. Persistent workgroups walk the
+// items b, b + G, b + 2G, ... with two register buffers, so the weights of
+// the next item are in flight while the current one is computed and HBM
+// never waits for a round of workgroups to finish. The single token row and
+// the slot table are staged once per workgroup. (K = H <= 5120 for gate/up
+// and K = I <= 2304 for down, one batch per row; larger shapes take the
+// one-shot kernels.)
+// ---------------------------------------------------------------------------
+constexpr int kStreamBlocks = 768;  // persistent workgroups per streaming kernel
+
+struct GuRegs {
+  uint4 g[kGuU], u[kGuU];
+  uint32_t sg[kGuU], su[kGuU];
+};
+
+__device__ __forceinline__ void gu_issue(const DecodeArgs& a, const int* tab, int it, GuRegs& r) {
+  const int s = it / a.gu_items, rb = it - s * a.gu_items;
+  const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int nr = min(rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes, a.I - 1);
+  const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> 5;
+  const uint8_t* gbase = a.routed.gu_codes + (size_t)e * 2 * a.I * crow;
+  const uint8_t* sbase = a.routed.gu_scales + (size_t)e * 2 * a.I * srow;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, a.I * crow);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, a.I * crow);
+  const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, a.I * srow);
+  const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, a.I * srow);
+  const int co = nr * crow + j * 16, so = nr * srow + j;
+#pragma unroll
+  for (int u = 0; u < kGuU; ++u) {
+    r.g[u] = bload16(rg, co + u * kGuLanes * 16);
+    r.u[u] = bload16(ru, co + u * kGuLanes * 16);
+    r.sg[u] = bload8(rgs, so + u * kGuLanes);
+    r.su[u] = bload8(rus, so + u * kGuLanes);
+  }
+}
+
+__device__ __forceinline__ void gu_compute(const DecodeArgs& a, const int* tab, int it,
+                                           const GuRegs& r, const uint4* s_x) {
+  const int s = it / a.gu_items, rb = it - s * a.gu_items;
+  const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int n = rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes;
+  const int kc = a.H >> 5;
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kGuU; ++u) {
+    const int c = kGuLanes * u + j;
+    if (c < kc) {
+      const uint4* xv = s_x + c;
+      constexpr int P = kGuLanes * kGuU;
+      const uint4 x0 = xv[0], x1 = xv[P], x2 = xv[2 * P], x3 = xv[3 * P];
+      float pg = dot8_fp4_bf16(r.g[u].x, x0, 0.0f);
+      pg = dot8_fp4_bf16(r.g[u].y, x1, pg);
+      pg = dot8_fp4_bf16(r.g[u].z, x2, pg);
+      pg = dot8_fp4_bf16(r.g[u].w, x3, pg);
+      float pu = dot8_fp4_bf16(r.u[u].x, x0, 0.0f);
+      pu = dot8_fp4_bf16(r.u[u].y, x1, pu);
+      pu = dot8_fp4_bf16(r.u[u].z, x2, pu);
+      pu = dot8_fp4_bf16(r.u[u].w, x3, pu);
+      ag = fmaf(pg, e8m0_to_f32(r.sg[u]), ag);
+      au = fmaf(pu, e8m0_to_f32(r.su[u]), au);
+    }
+  }
+  const float g = group_sum<kGuLanes>(ag), u = group_sum<kGuLanes>(au);
+  if (j == 0 && n < a.I) a.h[(size_t)row * a.I + n] = silu_mul(g, u);
+}
+
+// Stages the token row and the slot table into LDS; returns the table.
+__device__ __forceinline__ int* stage_token_and_table(const DecodeArgs& a, char* lds) {
+  uint4* s_x = reinterpret_cast<uint4*>(lds);
+  int* s_tab = reinterpret_cast<int*>(lds + a.H * 2);
+  stage_rows<uint4>(
+      a.H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+      [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
+  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
+  __syncthreads();
+  s_tab[0] = min(max(s_tab[0], 0), a.max_slots);
+  return s_tab;
+}
+
+__global__ __launch_bounds__(kThreads) void gateup_stream_kernel(DecodeArgs a, int G) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x >= G) {  // shared expert down rows (one-shot)
+    down_item<1>(a, shared_slot(a), blockIdx.x - G, reinterpret_cast<f32x4_t*>(lds), a.y, false);
+    return;
+  }
+  int* tab = stage_token_and_table(a, lds);
+  const uint4* s_x = reinterpret_cast<const uint4*>(lds);
+  const int n = tab[0] * a.gu_items;
+  const int b = blockIdx.x;
+  if (b >= n) return;
+  // Items b + kG, two per iteration with fixed buffers and no early exit (an
+  // exit between the halves would let the compiler merge them and move the
+  // buffers to scratch). Loads past this workgroup's last item re-read its
+  // current item (cache hits) and are not used.
+  const int mine = (n - b + G - 1) / G;
+  GuRegs A, B;
+  gu_issue(a, tab, b, A);
+  for (int k = 0; k < mine; k += 2) {
+    const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
+    gu_issue(a, tab, i1 < n ? i1 : i0, B);
+    gu_compute(a, tab, i0, A, s_x);
+    gu_issue(a, tab, i2 < n ? i2 : i0, A);
+    if (i1 < n) gu_compute(a, tab, i1, B, s_x);
+  }
+}
+
+struct DnRegs {
+  uint4 w[kDnU];
+  uint32_t sc[kDnU];
+  f32x4_t h[3];  // this workgroup's share of the item's h row (I <= 3072)
+};
+
+__device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, int it, DnRegs& r) {
+  const int s = it / a.dn_items, c = it - s * a.dn_items;
+  const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
+  const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int nr = min(c * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  const __amdgpu_buffer_rsrc_t rd =
+      matrix_rsrc(a.routed.d_codes + (size_t)e * a.H * crow, a.H * crow);
+  const __amdgpu_buffer_rsrc_t rds =
+      matrix_rsrc(a.routed.d_scales + (size_t)e * a.H * srow, a.H * srow);
+  const int co = nr * crow + j * 16, so = nr * srow + j;
+#pragma unroll
+  for (int u = 0; u < kDnU; ++u) {
+    r.w[u] = bload16(rd, co + u * 8 * 16);
+    r.sc[u] = bload8(rds, so + u * 8);
+  }
+  const f32x4_t* hrow = reinterpret_cast<const f32x4_t*>(a.h + (size_t)row * a.I);
+  const int nv = a.I >> 2;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) r.h[i] = hrow[min((int)threadIdx.x + i * kThreads, nv - 1)];
+}
+
+__device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, int it,
+                                           const DnRegs& r, f32x4_t* s_h) {
+  const int nv = a.I >> 2;
+  __syncthreads();  // previous item's reads of s_h are done
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int f = min((int)threadIdx.x + i * kThreads, nv - 1);
+    s_h[(f & 7) * (8 * kDnU) + (f >> 3)] = r.h[i];
+  }
+  __syncthreads();
+  const int s = it / a.dn_items, c = it - s * a.dn_items;
+  const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int n = c * kDnRows + wave * 8 + (lane >> 3);
+  const int kc = a.I >> 5;
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kDnU; ++u) {
+    const int ch = 8 * u + j;
+    if (ch < kc) {
+      const f32x4_t* hv = s_h + ch;
+      constexpr int P = 8 * kDnU;
+      float pd = dot8_fp4_f32(r.w[u].x, hv[0], hv[P], 0.0f);
+      pd = dot8_fp4_f32(r.w[u].y, hv[2 * P], hv[3 * P], pd);
+      pd = dot8_fp4_f32(r.w[u].z, hv[4 * P], hv[5 * P], pd);
+      pd = dot8_fp4_f32(r.w[u].w, hv[6 * P], hv[7 * P], pd);
+      acc = fmaf(pd, e8m0_to_f32(r.sc[u]), acc);
+    }
+  }
+  const float v = group_sum<8>(acc);
+  if (j == 0 && n < a.H) cst(a.y + (size_t)row * a.H + n, v);
+}
+
+// `combine`: after its last item each workgroup drains its y stores and bumps
+// the counter of every column it wrote; the workgroup that completes a
+// column combines it.
+__global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int G, int combine) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ int s_last;
+  int* tab = reinterpret_cast<int*>(lds);
+  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int));
+  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) tab[i] = a.tab[i];
+  __syncthreads();
+  const int ns = min(max(tab[0], 0), a.max_slots);
+  const int n = ns * a.dn_items;
+  const int b = blockIdx.x;
+  if (b >= n) return;
+  const int mine = (n - b + G - 1) / G;
+  DnRegs A, B;
+  dn_issue(a, tab, b, A);
+  for (int k = 0; k < mine; k += 2) {
+    const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
+    dn_issue(a, tab, i1 < n ? i1 : i0, B);
+    dn_compute(a, tab, i0, A, s_h);
+    dn_issue(a, tab, i2 < n ? i2 : i0, A);
+    if (i1 < n) dn_compute(a, tab, i1, B, s_h);
+  }
+  if (!combine) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = blockIdx.x; i < n; i += G) {
+    const int c = i % a.dn_items;
+    if (threadIdx.x == 0)
+      s_last =
+          __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          ns - 1;
+    __syncthreads();
+    if (s_last) combine_column(a, c);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ __launch_bounds__(kThreads) void route_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const int b = blockIdx.x;
+  if (b < a.nb_router) {
+    router_rows(a, b);
+  } else if (b == a.nb_router) {
+    routing(a, lds);
+  } else {
+    gateup_item<MT>(a, shared_slot(a), b - a.nb_router - 1, reinterpret_cast<uint4*>(lds), nullptr);
+  }
+}
+
+// Items are slot-minor (item = rb * max_slots + s), so workgroups of slots
+// that turn out empty are spread over the grid instead of trailing it.
+template <int MT>
+__global__ __launch_bounds__(kThreads) void gateup_kernel(DecodeArgs a, int routed_items,
+                                                          const int32_t* rtok) {
+  extern __shared__ __align__(16) char lds[];
+  const int b = blockIdx.x;
+  if (b < routed_items) {
+    const int s = b % a.max_slots, rb = b / a.max_slots;
+    if (s >= load_nslots(a)) return;
+    gateup_item<MT>(a, load_slot(a, s), rb, reinterpret_cast<uint4*>(lds), rtok);
+  } else {
+    down_item<MT>(a, shared_slot(a), b - routed_items, reinterpret_cast<f32x4_t*>(lds), a.y, false);
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int combine) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ int s_last;
+  const int b = blockIdx.x;
+  const int s = b % a.max_slots, c = b / a.max_slots;
+  const int ns = load_nslots(a);
+  if (s >= ns) return;
+  down_item<MT>(a, load_slot(a, s), c, reinterpret_cast<f32x4_t*>(lds), a.y, combine != 0);
+  if (!combine) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             ns - 1;
+  __syncthreads();
+  if (s_last) combine_column(a, c);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+namespace {
+uint64_t next_epoch() {
+  // 64-bit tags unique per launch: the high bits come from the start time of
+  // the process, so stale flags left in a reused workspace never match.
+  static std::atomic<uint64_t> counter{0};
+  static const uint64_t base = [] {
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (t << 20) ^ ((uint64_t)getpid() << 44);
+  }();
+  uint64_t v = base + (++counter);
+  return v == 0 ? 1 : v;
+}
+
+struct DecodeLayout {
+  int max_slots, rows, gu_items, dn_items, nb_router;
+  size_t off_flags, off_cnt, off_status, off_tab, off_rt, off_inv, off_logits, off_w, off_h, off_y,
+      bytes;
+};
+
+size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
+
+DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool shared) {
+  DecodeLayout L{};
+  L.max_slots = E < R ? E : R;
+  L.rows = R + (shared && !ffn ? T : 0);
+  L.gu_items = (I + kGuRows - 1) / kGuRows;
+  L.dn_items = (H + kDnRows - 1) / kDnRows;
+  L.nb_router = ffn ? 0 : (E + 3) / 4;
+  size_t o = 0;
+  L.off_flags = o;
+  o += al(sizeof(uint64_t) * (L.nb_router + 1));
+  L.off_cnt = o;
+  o += al(sizeof(int32_t) * (size_t)L.dn_items);
+  L.off_status = o;
+  o += al(sizeof(int32_t));
+  L.off_tab = o;
+  o += al(sizeof(int32_t) * (1 + 3 * (size_t)L.max_slots));
+  L.off_rt = o;
+  o += al(sizeof(int32_t) * (size_t)L.rows);
+  L.off_inv = o;
+  o += al(sizeof(int32_t) * (size_t)R);
+  L.off_logits = o;
+  o += al(sizeof(float) * (size_t)T * E);
+  L.off_w = o;
+  o += al(sizeof(float) * (size_t)R);
+  L.off_h = o;
+  o += al(sizeof(float) * (size_t)L.rows * I);
+  L.off_y = o;
+  o += al(ffn ? 0 : sizeof(float) * (size_t)L.rows * H);
+  L.bytes = o;
+  return L;
+}
+}  // namespace
+
+size_t decode_ws_bytes(int T, int H, int I, int E, int k, int R, bool ffn, bool shared) {
+  return layout(T, H, I, E, k, R, ffn, shared).bytes;
+}
+
+template <int MT>
+void launch_chain(const DecodeArgs& a, const DecodeLayout& L, bool ffn, bool shared, int routed_gu,
+                  int shared_dn, const int32_t* rtok, hipStream_t s) {
+  if (!ffn) {
+    const int grid = L.nb_router + 1 + (shared ? L.gu_items : 0);
+    hipLaunchKernelGGL(route_kernel<MT>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
+  }
+  hipLaunchKernelGGL(gateup_kernel<MT>, dim3(routed_gu + shared_dn), dim3(kThreads), kLdsBytes, s,
+                     a, routed_gu, rtok);
+  hipLaunchKernelGGL(down_kernel<MT>, dim3(L.max_slots * L.dn_items), dim3(kThreads), kLdsBytes, s,
+                     a, ffn ? 0 : 1);
+}
+
+void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
+  const bool ffn = d.ffn_mode != 0;
+  const bool shared = d.has_shared && !ffn;
+  const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, ffn, shared);
+  char* w = static_cast<char*>(ws);
+  DecodeArgs a{};
+  a.x = d.x;
+  a.wr = d.wr;
+  a.bias = d.bias;
+  a.routed = d.routed;
+  a.shared = d.shared;
+  a.has_shared = shared;
+  a.T = d.T;
+  a.H = d.H;
+  a.I = d.I;
+  a.E = d.E;
+  a.k = d.k;
+  a.R = d.R;
+  a.offsets_in = d.offsets;
+  a.row_token_in = d.row_token;
+  a.out = d.out;
+  a.ids_out = d.ids_out;
+  a.w_out = d.w_out;
+  a.flags = reinterpret_cast<uint64_t*>(w + L.off_flags);
+  a.cnt_dn = reinterpret_cast<int32_t*>(w + L.off_cnt);
+  a.status = reinterpret_cast<int32_t*>(w + L.off_status);
+  a.tab = reinterpret_cast<int32_t*>(w + L.off_tab);
+  a.row_token = reinterpret_cast<int32_t*>(w + L.off_rt);
+  a.inv_row = reinterpret_cast<int32_t*>(w + L.off_inv);
+  a.logits = reinterpret_cast<float*>(w + L.off_logits);
+  a.route_w = reinterpret_cast<float*>(w + L.off_w);
+  a.h = reinterpret_cast<float*>(w + L.off_h);
+  a.y = ffn ? d.y_rows : reinterpret_cast<float*>(w + L.off_y);
+  a.epoch = next_epoch();
+  a.max_slots = L.max_slots;
+  a.rows = L.rows;
+  a.nb_router = L.nb_router;
+  a.gu_items = L.gu_items;
+  a.dn_items = L.dn_items;
+
+  const int routed_gu = L.max_slots * L.gu_items;
+  const int shared_dn = shared ? L.dn_items : 0;
+  if (ffn) {
+    hipLaunchKernelGGL(ffn_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  }
+  // One token (or one row per expert): every slot holds a single row, and a
+  // kernel built for one staged row needs far fewer registers.
+  const bool one = d.T == 1 || (ffn && d.R <= 1);
+  const bool stream = d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
+                      (d.I >> 5) <= 8 * kDnU && d.I <= 3 * 4 * kThreads &&
+                      1 + 3 * L.max_slots <= 1024;
+  if (stream) {
+    const int grid = L.nb_router + 1 + (shared ? L.gu_items : 0);
+    hipLaunchKernelGGL(route_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
+    const int gg = routed_gu < kStreamBlocks ? routed_gu : kStreamBlocks;
+    hipLaunchKernelGGL(gateup_stream_kernel, dim3(gg + shared_dn), dim3(kThreads), kLdsBytes, s,
+                       a, gg);
+    const int nd = L.max_slots * L.dn_items;
+    const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
+    hipLaunchKernelGGL(down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a, gd, 1);
+  } else if (one)
+    launch_chain<1>(a, L, ffn, shared, routed_gu, shared_dn, ffn ? d.row_token : a.row_token, s);
+  else
+    launch_chain<kMT>(a, L, ffn, shared, routed_gu, shared_dn, ffn ? d.row_token : a.row_token, s);
+}
+
+}  // namespace moe

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(FfnProblem p)
 // down: y[row][n] = W_d[n] . h[row], K = I, h in fp32.
 template <int U>
 __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(FfnProblem p) {
-  extern __shared__ __align__(16) float4 s_h[];  // [kGemvMT][I/4] fp32
+  extern __shared__ __align__(16) f32x4_t s_h[];  // [kGemvMT][I/4] fp32
   const SlotInfo si = resolve_slot(p, blockIdx.y);
   if (si.e < 0 || si.m <= 0) return;
   const BankView bk = si.shared ? p.shared : p.routed;
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(FfnProblem p) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * vpr; idx += kGemvThreads) {
       const int t = idx / vpr, c = idx - t * vpr;
-      s_h[idx] = reinterpret_cast<const float4*>(hin + (size_t)(si.row0 + t0 + t) * I)[c];
+      s_h[idx] = reinterpret_cast<const f32x4_t*>(hin + (size_t)(si.row0 + t0 + t) * I)[c];
     }
     __syncthreads();
     float acc[kGemvMT];
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(FfnProblem p) {
 #pragma unroll
           for (int t = 0; t < kGemvMT; ++t) {
             if (t < nt) {
-              const float4* hv = s_h + t * vpr + c * 8;
+              const f32x4_t* hv = s_h + t * vpr + c * 8;
               float pd = dot8_fp4_f32(wd[u].x, hv[0], hv[1], 0.0f);
               pd = dot8_fp4_f32(wd[u].y, hv[2], hv[3], pd);
               pd = dot8_fp4_f32(wd[u].z, hv[4], hv[5], pd);

@@ -59,7 +59,7 @@ __device__ __forceinline__ float dot8_fp4_bf16(uint32_t w, uint4 x, float acc) {
 }
 
 // 8 E2M1 codes of a word times 8 fp32 values, fp32 fused multiply-adds.
-__device__ __forceinline__ float dot8_fp4_f32(uint32_t w, float4 a, float4 b, float acc) {
+__device__ __forceinline__ float dot8_fp4_f32(uint32_t w, f32x4_t a, f32x4_t b, float acc) {
   f32x2_t p0 = fp4x2_to_f32<0>(w), p1 = fp4x2_to_f32<1>(w);
   f32x2_t p2 = fp4x2_to_f32<2>(w), p3 = fp4x2_to_f32<3>(w);
   acc = fmaf(p0.x, a.x, acc); acc = fmaf(p0.y, a.y, acc);

@@ -55,6 +55,30 @@ struct FfnProblem {
 size_t ffn_ws_bytes(int T, int H, int I, int R, bool shared);
 void launch_expert_ffn(const FfnProblem& p, hipStream_t s);
 
+// The persistent few-token kernel (layer mode: router..combine in one
+// launch; FFN mode: bucketed rows given by offsets, writes y_rows).
+constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeFfnMaxR = 128;
+
+struct DecodeLaunch {
+  int ffn_mode;
+  const uint16_t* x;
+  const uint16_t* wr;
+  const float* bias;
+  BankView routed, shared;
+  bool has_shared;
+  int T, H, I, E, k, R;
+  const int32_t* offsets;    // FFN mode
+  const int32_t* row_token;  // FFN mode
+  float* out;
+  int32_t* ids_out;
+  float* w_out;
+  float* y_rows;             // FFN mode output
+};
+
+size_t decode_ws_bytes(int T, int H, int I, int E, int k, int R, bool ffn, bool shared);
+void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s);
+
 void launch_combine(const float* y_rows, const int32_t* inv_row, const float* w,
                     const float* y_shared, int T, int k, int H, int R, float* out,
                     hipStream_t s);

@@ -66,8 +66,9 @@ def test_layer_forward_validation_codes():
     assert _fwd(_bank(H=16384)) == M.MOE_ERR_UNSUPPORTED
     assert _fwd(_bank(), shared=_bank(E=2)) == M.MOE_ERR_INVALID_ARG      # shared must be E=1
     assert _fwd(_bank(), shared=_bank(E=1, I=64)) == M.MOE_ERR_INVALID_ARG
-    need = M.moe_workspace_bytes(8, 256, 128, 16, 2)
-    assert _fwd(_bank(), ws_bytes=need - 1) == M.MOE_ERR_WORKSPACE
+    assert _fwd(_bank(), ws_bytes=100) == M.MOE_ERR_WORKSPACE
+    assert _fwd(_bank(), T=64, ws_bytes=M.moe_workspace_bytes(64, 256, 128, 16, 2) // 2) \
+        == M.MOE_ERR_WORKSPACE
     assert _fwd(_bank(), ws=None) == M.MOE_ERR_INVALID_ARG
     assert _fwd(_bank(), T=0) == M.MOE_OK                                  # no-op
 

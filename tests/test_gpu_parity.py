@@ -146,7 +146,8 @@ def run_ffn(x_bits, bank_np, offsets, row_token, R):
     off = None if offsets is None else HP.to_dev(np.asarray(offsets, np.int32))
     rt = None if row_token is None else HP.to_dev(np.asarray(row_token, np.int32))
     y = torch.full((max(R, 1), bank.H), float("nan"), dtype=torch.float32, device=HP.dev())
-    ws = torch.empty(R * bank.I * 4 + 256, dtype=torch.uint8, device=HP.dev())
+    T = x.shape[0]
+    ws = M.workspace(T, bank.H, bank.I, bank.E, max(1, -(-R // T)), HP.dev())
     M.moe_expert_ffn_mxfp4(x, bank, off, rt, R, y, ws)
     return _np(y)[:R]
 
@@ -360,8 +361,59 @@ def test_abi_zero_tokens_is_a_noop_and_small_workspace_is_rejected():
     ws = M.workspace(w.T, w.H, w.I, w.E, w.k, HP.dev())
     M.moe_layer_forward(x[:0], wr, None, rd, sd, w.k, out[:0], ws=ws)
     assert torch.all(out == 3.0)
-    small = ws[: M.moe_workspace_bytes(w.T, w.H, w.I, w.E, w.k) - 256]
+    small = ws[:512]
     with pytest.raises(M.MoeError) as ei:
         M.moe_layer_forward(x, wr, None, rd, sd, w.k, out, ws=small)
     assert ei.value.status == M.MOE_ERR_WORKSPACE
     assert torch.all(out == 3.0)
+
+
+# ---------------------------------------------------------------------------
+# The persistent few-token kernel: token counts, reused and garbage workspace
+# ---------------------------------------------------------------------------
+
+def test_layer_token_counts_share_one_workspace():
+    # T from 1 to past the few-token limit, all through one workspace whose
+    # flags and tables are left over from the previous (differently shaped) call
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    rd, sd = HP.bank_to_dev(d["routed"]), HP.bank_to_dev(d["shared"])
+    wr = HP.to_dev(d["w_router"])
+    ws = M.workspace(64, w.H, w.I, w.E, w.k, HP.dev())
+    for T in (1, 2, 3, 5, 8, 15, 16, 17, 40, 3):
+        x_bits = S.gen_tokens(w, 5, call=T, T=T)
+        out = torch.empty((T, w.H), dtype=torch.float32, device=HP.dev())
+        ids = torch.empty((T, w.k), dtype=torch.int32, device=HP.dev())
+        wt = torch.empty((T, w.k), dtype=torch.float32, device=HP.dev())
+        M.moe_layer_forward(HP.to_dev(x_bits), wr, None, rd, sd, w.k, out, ids, wt, ws)
+        ref = O.layer(x_bits, d["w_router"], None, d["routed"], d["shared"], w.k)
+        alt = HP.check_routing(ref, _np(ids), _np(wt), w.k)
+        err = HP.rel_l2(_np(out), HP.reference_rows(ref, d["routed"], d["shared"],
+                                                      ref["tokens"], alt))
+        assert err < 1e-5, (T, err)
+
+
+def test_layer_with_garbage_workspace():
+    w = S.get("spec5")
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    routed, _ = _selected_bank(w, x, wr, None)
+    shared = S.gen_bank(w, 0, shared=True)
+    rd, sd = HP.bank_to_dev(routed), HP.bank_to_dev(shared)
+    ws = M.workspace(w.T, w.H, w.I, w.E, w.k, HP.dev())
+    g = torch.Generator(device=HP.dev()).manual_seed(1)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=HP.dev(), generator=g))
+    out = torch.empty((w.T, w.H), dtype=torch.float32, device=HP.dev())
+    M.moe_layer_forward(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, ws=ws)
+    ref = O.layer(x, wr, None, routed, shared, w.k)
+    assert HP.rel_l2(_np(out), ref["out"]) < 1e-5
+
+
+@pytest.mark.parametrize("T,k", [(64, 2), (100, 3)])
+def test_ffn_rows_above_the_few_row_path(T, k):
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    x = S.gen_tokens(w, 7, T=T)
+    r = O.route(x, d["w_router"], None, k)
+    y = run_ffn(x, d["routed"], r["offsets"], r["row_token"], T * k)
+    ref = O.expert_rows(r["x"], d["routed"], r["offsets"], r["row_token"])
+    assert HP.rel_l2(y, ref) < 1e-5
