@@ -67,6 +67,7 @@ struct LayerWs {
   int32_t* row_token;
   int32_t* inv_row;
   void* perm;
+  void* ffn;  // FFN scratch: the GEMV path's fp32 h and h_sh, or the GEMM's
   float* h;
   float* h_sh;
   float* y;
@@ -86,8 +87,12 @@ LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
   L.row_token = c.take<int32_t>(R);
   L.inv_row = c.take<int32_t>(R);
   L.perm = c.take<char>(permute_ws_bytes(T, k, E));
-  L.h = c.take<float>(R * I);
-  L.h_sh = c.take<float>((size_t)T * I);
+  const size_t gemv = align_up(R * I * sizeof(float)) + align_up((size_t)T * I * sizeof(float));
+  const size_t gemm = gemm_ws_bytes(T, H, I, E, (int)R, true);
+  char* ffn = c.take<char>(gemv > gemm ? gemv : gemm);
+  L.ffn = ffn;
+  L.h = reinterpret_cast<float*>(ffn);
+  L.h_sh = reinterpret_cast<float*>(ffn ? ffn + align_up(R * I * sizeof(float)) : nullptr);
   L.y = c.take<float>(R * H);
   L.y_sh = c.take<float>((size_t)T * H);
   L.bytes = c.off;
@@ -171,8 +176,11 @@ int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
   if (!expert_offsets && bank->E != 1) return MOE_ERR_INVALID_ARG;
   if (!row_token && R > T) return MOE_ERR_INVALID_ARG;
   const bool few = R <= kDecodeFfnMaxR;
-  const size_t need = few ? decode_ws_bytes(T, bank->H, bank->I, bank->E, 1, R, true, false)
-                          : ffn_ws_bytes(T, bank->H, bank->I, R, false);
+  const bool mfma = !few && gemm_supported(T, bank->H, bank->I, R, false);
+  const int E = expert_offsets ? bank->E : 1;
+  const size_t need = few    ? decode_ws_bytes(T, bank->H, bank->I, bank->E, 1, R, true, false)
+                      : mfma ? gemm_ws_bytes(T, bank->H, bank->I, E, R, false)
+                             : ffn_ws_bytes(T, bank->H, bank->I, R, false);
   if (need && (!ws || !aligned16(ws))) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (few) {
@@ -206,7 +214,10 @@ int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
   p.h = static_cast<float*>(ws);
   p.y = y_rows;
   p.has_shared = false;
-  launch_expert_ffn(p, stream);
+  if (mfma)
+    launch_expert_gemm(p, ws, stream);
+  else
+    launch_expert_ffn(p, stream);
   return launch_status();
 }
 
@@ -299,7 +310,10 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float
     p.h_sh = L.h_sh;
     p.y_sh = L.y_sh;
   }
-  launch_expert_ffn(p, stream);
+  if (gemm_supported(T, H, I, R, shared != nullptr))
+    launch_expert_gemm(p, L.ffn, stream);
+  else
+    launch_expert_ffn(p, stream);
   launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
   return launch_status();
 }

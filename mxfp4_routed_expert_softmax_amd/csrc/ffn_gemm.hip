@@ -1,0 +1,390 @@
+// Expert FFN for many rows (prefill): a grouped GEMM over the experts'
+// buckets on gfx950 MFMA, with the MXFP4 weights dequantised exactly in
+// registers.
+//
+// A prefill chunk of a few hundred tokens or more touches nearly every
+// expert (FreeToken issue #444, janit's comment, section 3), so the bank is
+// read once per 128 bucket rows and the arithmetic sits on the matrix cores:
+//
+//   gate/up:  h = silu(X_e W_gate[e]^T) * (X_e W_up[e]^T)   bf16 MFMA, h -> fp16
+//   down:     y = h_e W_down[e]^T                            fp16 MFMA, y -> fp32
+//
+// X_e are the token rows of expert e's bucket, gathered through row_token;
+// the shared expert is one more bucket over all T tokens. Every bucket is
+// cut into 128-row blocks (listed by a one-workgroup plan kernel); the grid
+// walks (row block, column block) pairs with the column block fastest.
+//
+// Per workgroup (512 threads, one per CU): 128 rows x 256 weight rows (for
+// gate/up: 128 gate + the 128 up rows of the same output columns), 8 waves
+// of 64 x 64 built from v_mfma_f32_16x16x32_bf16 / _f16. K advances 128 per
+// step through a 3-stage LDS pipeline filled by direct global -> LDS loads:
+//  * A: 128 rows x 128 K (bf16 x or fp16 h), each row's 16-byte pieces
+//    permuted (piece p at slot p ^ (row & 15)) so fragment reads are
+//    conflict-free;
+//  * B: 256 weight rows x 64 bytes of packed E2M1 codes (piece p of row r
+//    at slot p ^ ((r / 4) & 3)) and their 4 E8M0 bytes per row.
+// Lane (column c, lane group g) of a wave takes the 32 codes of K range
+// [32 g, 32 g + 32) of its weight row, one E8M0 block, and converts them
+// with the gfx950 scaled FP4 conversion (exact: an E2M1 value times a power
+// of two in range is representable in bf16 and fp16). MFMA sub-step s uses
+// K values 32 g + 8 s .. + 7 of lane group g for both operands; an MFMA dot
+// product only needs A and B to agree on that assignment.
+//
+// Precision: x and the dequantised weights are exact in bf16; h is rounded
+// once to fp16 (relative 2^-11; |h| < 65504), the down weights are exact in
+// fp16 for E8M0 exponents in [-23, 13]; every sum is fp32.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 128;        // bucket rows per tile
+constexpr int kBK = 128;        // K per pipeline step
+constexpr int kWRows = 256;     // weight rows per tile
+constexpr int kThreads = 512;   // 8 waves: 2 (rows) x 4 (weight rows)
+constexpr int kStages = 3;
+constexpr int kAPieces = kBM * kBK / 8;       // 16-byte pieces of A per stage (2048)
+constexpr int kBPieces = kWRows * kBK / 32;   // 16-byte pieces of codes per stage (1024)
+constexpr int kABytes = kAPieces * 16;        // 32 KB
+constexpr int kBBytes = kBPieces * 16;        // 16 KB
+constexpr int kSBytes = kWRows * 4;           // 1 KB of E8M0 bytes
+constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+constexpr int kALoads = kAPieces / kThreads;  // 4 per thread per stage
+constexpr int kBLoads = kBPieces / kThreads;  // 2 per thread per stage
+
+struct GemmArgs {
+  const uint16_t* x;  // [T][H] bf16
+  int T, H, I, E, R;
+  BankView routed, shared;
+  int has_shared;
+  const int32_t* offsets;    // [E+1] routed buckets, or null (one expert, rows [0, R))
+  const int32_t* row_token;  // [R] or null (row r is token r)
+  int32_t* tile_expert;
+  int32_t* tile_m0;
+  int32_t* tile_total;
+  int max_tiles;
+  _Float16* h;    // [R + T][I]: routed rows, then the shared expert's T rows
+  float* y;       // [R][H]
+  float* y_sh;    // [T][H]
+};
+
+struct Bucket {
+  int e;        // slot in its bank
+  int begin;    // first row (into h; routed rows also index row_token and y)
+  int count;    // rows
+  bool shared;
+};
+
+// Bucket b: routed expert b for b < E, the shared expert for b == E.
+__device__ __forceinline__ Bucket bucket_of(const GemmArgs& g, int b) {
+  if (b >= g.E) return Bucket{0, g.R, g.T, true};
+  if (!g.offsets) return Bucket{0, 0, g.R, false};
+  const int lo = min(max(g.offsets[b], 0), g.R);
+  const int hi = min(max(g.offsets[b + 1], lo), g.R);
+  return Bucket{b, lo, hi - lo, false};
+}
+
+// The list of 128-row blocks of every bucket, routed experts by id, then
+// the shared expert. One workgroup of 1024 threads (at most 1025 buckets).
+__global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
+  __shared__ int s_tmp[32];
+  const int nb = g.E + (g.has_shared ? 1 : 0);
+  int cnt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int b = threadIdx.x + q * 1024;
+    cnt[q] = b < nb ? (bucket_of(g, b).count + kBM - 1) / kBM : 0;
+  }
+  int total0 = 0, total1 = 0;
+  const int base0 = block_exclusive_scan(cnt[0], s_tmp, &total0);
+  const int base1 = total0 + block_exclusive_scan(cnt[1], s_tmp, &total1);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int b = threadIdx.x + q * 1024;
+    const int base = q == 0 ? base0 : base1;
+    for (int m = 0; m < cnt[q] && base + m < g.max_tiles; ++m) {
+      g.tile_expert[base + m] = b;
+      g.tile_m0[base + m] = m * kBM;
+    }
+  }
+  if (threadIdx.x == 0) *g.tile_total = min(total0 + total1, g.max_tiles);
+}
+
+// 8 E2M1 codes (one word) times `sc` -> 8 bf16 / fp16
+__device__ __forceinline__ bf16x8_t fp4x8_bf16(uint32_t w, float sc) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+__device__ __forceinline__ f16x8_t fp4x8_f16(uint32_t w, float sc) {
+  const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
+  const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
+  const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
+  const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
+  return f16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// Direct global -> LDS loads: lane l's 16 (4) bytes at base + voff land at
+// LDS byte address lds + 16 l (4 l); lds is wave-uniform. Written as inline
+// asm so the compiler does not guard every later LDS read with a wait for
+// them: the kernel waits explicitly (vmcnt + barrier) before reading a
+// stage. The compiler's own waits for register loads stay correct, as
+// vector loads complete in issue order.
+__device__ __forceinline__ void lds_load16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+               :
+               : "v"(voff), "s"(lds), "s"(base)
+               : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, %2"
+               :
+               : "v"(voff), "s"(lds), "s"(base)
+               : "memory");
+}
+
+// Weight-row tiling of a workgroup's 256 rows r, and the output columns
+// (n0 = tile column offset): gate/up: r < 128 -> gate row n0 + r, else the
+// up row n0 + r - 128 (128 output columns per tile); down: row n0 + r (256
+// output columns). Wave (wm, wn) with lane column c owns fragment j:
+//   gate/up: r = 32 wn + 16 (j % 2) + c + 128 (j / 2)
+//   down:    r = 64 wn + 16 j + c
+template <bool GU>
+__device__ __forceinline__ int frag_row(int wn, int j, int c) {
+  return GU ? 32 * wn + 16 * (j & 1) + c + 128 * (j >> 1) : 64 * wn + 16 * j + c;
+}
+
+template <bool GU>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
+  __shared__ __align__(16) char lds[kStages * kStageBytes];
+  constexpr int kBN = GU ? kWRows / 2 : kWRows;  // output columns per tile
+  const int N = GU ? g.I : g.H;
+  const int K = GU ? g.H : g.I;
+  const int ncol = N / kBN;
+  const int mt = blockIdx.x / ncol, nt = blockIdx.x - mt * ncol;
+  if (mt >= *g.tile_total) return;
+  const int nb = g.E + (g.has_shared ? 1 : 0);
+  const Bucket bk = bucket_of(g, min(max(g.tile_expert[mt], 0), nb - 1));
+  const int m0 = g.tile_m0[mt];
+  if (m0 < 0 || m0 >= bk.count) return;
+  const int n0 = nt * kBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3, c = lane & 15, grp = lane >> 4;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+
+  // A: thread tid fills slot (row 32 u + tid / 16, piece tid % 16), which
+  // holds K piece (tid % 16) ^ (row % 16) of that row.
+  const void* a_src = GU ? static_cast<const void*>(g.x) : static_cast<const void*>(g.h);
+  uint32_t a_off[kALoads];
+  {
+    const int piece = (tid & 15) ^ ((tid >> 4) & 15);
+#pragma unroll
+    for (int u = 0; u < kALoads; ++u) {
+      const int m = min(m0 + 32 * u + (tid >> 4), bk.count - 1);
+      int row;
+      if (GU) {
+        row = bk.shared ? m : (g.row_token ? g.row_token[bk.begin + m] : bk.begin + m);
+        row = min(max(row, 0), g.T - 1);
+      } else {
+        row = bk.begin + m;
+      }
+      a_off[u] = ((uint32_t)row * (uint32_t)K + (uint32_t)(piece * 8)) * 2u;
+    }
+  }
+
+  // B: thread tid fills code slot (r = 128 u + tid / 4, piece tid % 4),
+  // which holds piece (tid % 4) ^ ((r / 4) % 4) of weight row r; threads
+  // tid < 256 also load the 4 E8M0 bytes of weight row tid.
+  const BankView bv = bk.shared ? g.shared : g.routed;
+  const uint32_t crow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
+  const size_t mat_rows = GU ? 2 * (size_t)g.I : (size_t)g.H;
+  const uint8_t* cbase = (GU ? bv.gu_codes : bv.d_codes) + (size_t)bk.e * mat_rows * crow;
+  const uint8_t* sbase = (GU ? bv.gu_scales : bv.d_scales) + (size_t)bk.e * mat_rows * srow;
+  auto wrow = [&](int r) -> uint32_t {  // tile weight row -> row of the expert's matrix
+    return GU ? (uint32_t)(r < 128 ? n0 + r : g.I + n0 + r - 128) : (uint32_t)(n0 + r);
+  };
+  uint32_t b_off[kBLoads];
+#pragma unroll
+  for (int u = 0; u < kBLoads; ++u) {
+    const int r = 128 * u + (tid >> 2);
+    b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
+  }
+  const uint32_t s_off = wrow(tid & 255) * srow;
+
+  // Stage `st` <- K step `ks`.
+  auto issue = [&](int st, int ks) {
+    const uint32_t base = lds_base + (uint32_t)(st * kStageBytes);
+    const uint32_t k0 = (uint32_t)(ks * kBK);
+#pragma unroll
+    for (int u = 0; u < kALoads; ++u)
+      lds_load16(a_src, a_off[u] + 2u * k0, base + (uint32_t)((u * kThreads + 64 * wave) * 16));
+#pragma unroll
+    for (int u = 0; u < kBLoads; ++u)
+      lds_load16(cbase, b_off[u] + k0 / 2,
+                 base + kABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
+    if (wave < 4) lds_load4(sbase, s_off + k0 / 32, base + kABytes + kBBytes + 256u * wave);
+  };
+  // Wait until at most one stage's loads are outstanding (or none).
+  auto wait_stage = [&](bool keep_one) {
+    if (keep_one) {
+      if (wave < 4)
+        asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // rows of this wave beyond the bucket need no arithmetic
+  const bool active = m0 + 64 * wm < bk.count;
+
+  auto compute = [&](int st) {
+    const char* sb = lds + st * kStageBytes;
+    const uint4* sa = reinterpret_cast<const uint4*>(sb);
+    const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABytes);
+    const uint8_t* ss = reinterpret_cast<const uint8_t*>(sb + kABytes + kBBytes);
+    uint4 bc[4];
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = frag_row<GU>(wn, j, c);
+      bc[j] = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
+      sc[j] = e8m0_to_f32(ss[r * 4 + grp]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // A row 64 wm + 16 i + c, K values 32 grp + 8 s: piece 4 grp + s
+      uint4 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = sa[(64 * wm + 16 * i + c) * 16 + ((4 * grp + s) ^ c)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
+        if constexpr (GU) {
+          const bf16x8_t bf = fp4x8_bf16(w, sc[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, af[i]), bf, acc[i][j], 0, 0, 0);
+        } else {
+          const f16x8_t bf = fp4x8_f16(w, sc[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8_t, af[i]), bf, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Pipeline: before step ks the stages of ks and ks + 1 are in flight.
+  // Wait for ks's, then one barrier makes it visible to every wave and
+  // guarantees that stage (ks + 2) % 3, read at step ks - 1, is free.
+  const int steps = K / kBK;
+  issue(0, 0);
+  if (steps > 1) issue(1, 1);
+  for (int ks = 0; ks < steps; ++ks) {
+    wait_stage(ks + 1 < steps);
+    __syncthreads();
+    if (ks + 2 < steps) issue((ks + 2) % kStages, ks + 2);
+    if (active) compute(ks % kStages);
+  }
+
+  // D layout: lane (c, grp), element v -> row 4 grp + v, column c
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * grp + v;
+      if (m >= bk.count) continue;
+      if constexpr (GU) {
+        _Float16* hr = g.h + (size_t)(bk.begin + m) * g.I + n0 + 32 * wn + c;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) hr[16 * j] = (_Float16)silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+      } else {
+        float* yr = (bk.shared ? g.y_sh + (size_t)m * g.H : g.y + (size_t)(bk.begin + m) * g.H) +
+                    n0 + 64 * wn + c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][v];
+      }
+    }
+  }
+}
+
+struct GemmLayout {
+  _Float16* h;
+  int32_t* tiles;
+  int max_tiles;
+  size_t bytes;
+};
+
+GemmLayout gemm_layout(void* ws, int T, int I, int E, int R, bool shared) {
+  GemmLayout L;
+  const size_t rows = (size_t)R + (shared ? T : 0);
+  L.max_tiles = (R + kBM - 1) / kBM + E + (shared ? (T + kBM - 1) / kBM + 1 : 0);
+  const size_t hb = (rows * I * sizeof(_Float16) + 255) & ~(size_t)255;
+  char* w = static_cast<char*>(ws);
+  L.h = reinterpret_cast<_Float16*>(w);
+  L.tiles = reinterpret_cast<int32_t*>(w ? w + hb : nullptr);
+  L.bytes = hb + (((2 * (size_t)L.max_tiles + 1) * sizeof(int32_t) + 255) & ~(size_t)255);
+  return L;
+}
+
+}  // namespace
+
+bool gemm_supported(int T, int H, int I, int R, bool shared) {
+  // 32-bit byte offsets of the activation rows
+  const size_t rows = (size_t)R + (shared ? T : 0);
+  return H % kBK == 0 && I % kBK == 0 && I % (kWRows / 2) == 0 && H % kWRows == 0 &&
+         (size_t)T * H * 2 < (1ull << 31) && rows * I * 2 < (1ull << 31);
+}
+
+size_t gemm_ws_bytes(int T, int H, int I, int E, int R, bool shared) {
+  (void)H;
+  return gemm_layout(nullptr, T, I, E, R, shared).bytes;
+}
+
+void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
+  const int E = p.offsets ? p.routed.E : 1;
+  const GemmLayout L = gemm_layout(ws, p.T, p.I, E, p.R, p.has_shared);
+  GemmArgs g{};
+  g.x = p.x;
+  g.T = p.T;
+  g.H = p.H;
+  g.I = p.I;
+  g.E = E;
+  g.R = p.R;
+  g.routed = p.routed;
+  g.shared = p.shared;
+  g.has_shared = p.has_shared;
+  g.offsets = p.offsets;
+  g.row_token = p.row_token;
+  g.tile_expert = L.tiles;
+  g.tile_m0 = L.tiles + L.max_tiles;
+  g.tile_total = L.tiles + 2 * L.max_tiles;
+  g.max_tiles = L.max_tiles;
+  g.h = L.h;
+  g.y = p.y;
+  g.y_sh = p.y_sh;
+  hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  hipLaunchKernelGGL(gemm_kernel<true>, dim3(L.max_tiles * (p.I / (kWRows / 2))),
+                     dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL(gemm_kernel<false>, dim3(L.max_tiles * (p.H / kWRows)), dim3(kThreads), 0,
+                     s, g);
+}
+
+}  // namespace moe

@@ -55,6 +55,12 @@ struct FfnProblem {
 size_t ffn_ws_bytes(int T, int H, int I, int R, bool shared);
 void launch_expert_ffn(const FfnProblem& p, hipStream_t s);
 
+// The MFMA grouped GEMM for many rows (h in fp16 in its own workspace; the
+// FfnProblem's h / h_sh are unused). Call only where gemm_supported().
+bool gemm_supported(int T, int H, int I, int R, bool shared);
+size_t gemm_ws_bytes(int T, int H, int I, int E, int R, bool shared);
+void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s);
+
 // The persistent few-token kernel (layer mode: router..combine in one
 // launch; FFN mode: bucketed rows given by offsets, writes y_rows).
 constexpr int kDecodeMaxT = 16;
