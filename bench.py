@@ -13,11 +13,12 @@ pool of distinct tokens and over several copies of the expert bank and router
 at distinct addresses (the cache keys on address, so identical contents at a
 new address still miss).
 
-Prints one JSON line. `roofline` covers the expert FFN (the kernel that moves
-~97 % of the bytes), timed with HIP events on the launch stream in a loop of
-moe_expert_ffn_mxfp4 calls that do exactly the layer's expert work (routed
-experts plus the shared expert laid out as expert E of one allocation).
-`cpu_baseline` times the fp64 oracle on the host on a bounded token sample.
+Prints one JSON line. `roofline` covers the layer's dominant kernel: a
+second loop of the same calls sets the library's timing hook, which attaches
+HIP start / stop events to every kernel launch, and the kernel with the
+largest mean duration is reported against its algorithmic bytes (HBM-bound)
+or flops (MFMA-bound) per launch. `cpu_baseline` times the fp64 oracle on the
+host on a bounded token sample.
 """
 
 from __future__ import annotations
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-loop", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 3 plain device copies of BYTES bytes (the reference "
+                         "reading for the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -68,6 +72,17 @@ def main() -> int:
 
     import mxfp4_routed_expert_softmax_amd as M
     import synthetic as S
+
+    if args.copy_probe:
+        n = args.copy_probe
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return 0
 
     w = S.get(args.config)
     small = w.T <= 16
@@ -144,67 +159,17 @@ def main() -> int:
     tokens_s = K * w.T / (ms / 1e3)
     log(f"[bench] layer: {ms_step * 1e3:.2f} us/step, {tokens_s:,.0f} tokens/s")
 
-    # Touched experts per call (routed union + shared) for the byte count.
-    def expert_bytes():
-        n = 3 * w.H * w.I
-        return n // 2 + n // 32
-
-    # ---- roofline loop: the expert FFN alone ------------------------------
+    # ---- roofline: the dominant kernel, timed with HIP events --------------
+    # A second loop makes the same calls as the timed one with the library's
+    # timing hook set: every kernel launch then carries a start and a stop
+    # event that the runtime stamps at that kernel's dispatch begin and end
+    # on the launch stream. The kernel with the largest mean duration is the
+    # one reported, against its algorithmic bytes (HBM-bound kernels) or
+    # flops (MFMA-bound kernels) per launch.
     roof = None
     if not args.no_roofline_loop:
-        R = w.T * w.k
-        ffn_args, touched = [], []
-        keep = []
-        for i in range(n_args):
-            xi = x_pool[i % P]
-            M.moe_router_topk(xi, wrs[i % C], bias, w.k, ids, wts, None, ws)
-            off = torch.empty(w.E + 2, dtype=torch.int32, device=dev)
-            rt = torch.empty(R + w.T, dtype=torch.int32, device=dev)
-            inv = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
-            M.moe_permute(ids, w.E, off[: w.E + 1], rt[:R], inv, ws)
-            off[w.E + 1] = R + w.T                       # shared expert = bucket E
-            rt[R:] = torch.arange(w.T, dtype=torch.int32, device=dev)
-            torch.cuda.synchronize()
-            counts = (off[1:] - off[:-1]).cpu().numpy()
-            touched.append(int((counts > 0).sum()))
-            keep.append((off, rt, inv))
-            ffn_args.append((xi.data_ptr(), ctypes.byref(banks[i % C]["both"].struct),
-                             off.data_ptr(), rt.data_ptr(), w.T, R + w.T))
-        y = torch.empty((R + w.T, w.H), dtype=torch.float32, device=dev)
-        ffn = lib.moe_expert_ffn_mxfp4
-
-        def fstep(i):
-            a = ffn_args[i % n_args]
-            st = ffn(*a, y.data_ptr(), ws.data_ptr(), ws_n, sh)
-            if st != 0:
-                raise M.MoeError("moe_expert_ffn_mxfp4", st, M.status_str(st))
-
-        for i in range(W):
-            fstep(i)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(K):
-            fstep(W + i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        f_ms = ev0.elapsed_time(ev1) / K
-        mean_touched = float(np.mean([touched[(W + i) % n_args] for i in range(K)]))
-        if small:
-            by = mean_touched * expert_bytes() + w.T * w.H * 2 + (R + w.T) * w.H * 4
-            ach = by / (f_ms / 1e3) / 1e9
-            roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
-            log(f"[bench] expert FFN: {f_ms * 1e3:.2f} us/call, {mean_touched:.2f} experts "
-                f"touched, {by / 1e6:.1f} MB -> {ach:,.0f} GB/s")
-        else:
-            fl = (R + w.T) * 2.0 * 3 * w.H * w.I
-            ach = fl / (f_ms / 1e3) / 1e12
-            roof = dict(bound="mfma", achieved=round(ach, 1), peak=MFMA_16BIT_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(ach / MFMA_16BIT_PEAK_TFLOPS, 4),
-                        traffic=None)
-            log(f"[bench] expert FFN: {f_ms:.3f} ms/call, {fl / 1e12:.3f} TFLOP -> "
-                f"{ach:,.1f} TFLOP/s ({mean_touched:.0f} experts touched)")
-
+        roof = kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bias,
+                               ids, wts, ws, P, C, W, K, stream)
     # ---- CPU baseline: the fp64 oracle on the host -------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -252,6 +217,142 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     return 0
 
+
+
+# Algorithmic work per launch of each kernel, from the call's shape and the
+# number U of distinct routed experts it touched. Bytes count every array a
+# kernel must read or write once (weights at 17/32 byte per weight: codes plus
+# one E8M0 byte per 32); flops count 2 per multiply-add of the expert FFN.
+def kernel_work(name, w, U, shared=True):
+    H, I, T, R = w.H, w.I, w.T, w.T * w.k
+    gu_expert = 2 * I * H * 17 // 32       # gate + up of one expert
+    dn_expert = I * H * 17 // 32           # down of one expert
+    if name in ("gateup_stream_kernel", "gateup_kernel"):
+        # routed gate/up of the U experts (+ the shared expert's down rows)
+        b = U * gu_expert + T * H * 2 + R * I * 4
+        if shared:
+            b += dn_expert + T * I * 4 + T * H * 4
+        return "hbm", b
+    if name in ("down_stream_kernel", "down_kernel"):
+        # routed down of the U experts, then the combine
+        return "hbm", U * dn_expert + R * I * 4 + R * H * 4 + (T * H * 4 if shared else 0) \
+            + T * H * 4 + T * w.k * 8
+    if name == "route_kernel":
+        # router GEMV, top-k, bucketing (+ the shared expert's gate/up)
+        b = w.E * w.H * 2 + T * H * 2 + T * w.E * 4
+        if shared:
+            b += gu_expert + T * I * 4
+        return "hbm", b
+    rows = R + (T if shared else 0)
+    if name == "gemm_gateup_kernel":
+        return "mfma", rows * 2.0 * 2 * H * I
+    if name == "gemm_down_kernel":
+        return "mfma", rows * 2.0 * H * I
+    if name == "router_mfma_kernel":
+        return "mfma", T * 2.0 * w.E * H
+    return None, None
+
+
+def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bias, ids, wts,
+                    ws, P, C, W, K, stream):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch already loaded
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+
+    def new_event():
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    # distinct routed experts per token batch (same routing for every bank copy)
+    U = []
+    for p in range(P):
+        M.moe_router_topk(x_pool[p], wrs[0], bias, w.k, ids, wts, None, ws)
+        U.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+
+    step(0)
+    torch.cuda.synchronize()
+    n_launch = M.moe_last_call_launches()
+    names = [M.moe_launch_name(i) for i in range(n_launch)]
+    evs = [(ctypes.c_void_p * (2 * n_launch))(*[new_event() for _ in range(2 * n_launch)])
+           for _ in range(K)]
+    try:
+        for i in range(W):
+            step(i)
+        for i in range(K):
+            M.moe_set_kernel_events(evs[i], n_launch)
+            step(W + i)
+        M.moe_set_kernel_events(None, 0)
+        torch.cuda.synchronize()
+        dur = np.zeros((K, n_launch))
+        f = ctypes.c_float()
+        for i in range(K):
+            for j in range(n_launch):
+                if hip.hipEventElapsedTime(ctypes.byref(f), evs[i][2 * j],
+                                           evs[i][2 * j + 1]) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                dur[i, j] = f.value
+    finally:
+        M.moe_set_kernel_events(None, 0)
+        for a in evs:
+            for e in a:
+                hip.hipEventDestroy(e)
+    mean_ms = dur.mean(axis=0)
+    per = ", ".join(f"{n} {m * 1e3:.2f} us" for n, m in zip(names, mean_ms))
+    log(f"[bench] kernels (event-timed, mean of {K}): {per}")
+    j = int(np.argmax(mean_ms))
+    name, t_ms = names[j], float(mean_ms[j])
+    bound, _ = kernel_work(name, w, 1)
+    if bound is None:
+        log(f"[bench] dominant kernel {name}: no algorithmic work model, roofline omitted")
+        return None
+    # per-launch work averaged over the calls the timed loop made
+    work = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1] for i in range(K)]))
+    if bound == "hbm":
+        ach = work / (t_ms / 1e3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+        log(f"[bench] {name}: {t_ms * 1e3:.2f} us/launch, {work / 1e6:.2f} MB algorithmic "
+            f"(mean {np.mean([U[(W + i) % P] for i in range(K)]):.2f} routed experts) -> "
+            f"{ach:,.0f} GB/s")
+    else:
+        ach = work / (t_ms / 1e3) / 1e12
+        peak, unit = MFMA_16BIT_PEAK_TFLOPS, "TFLOP/s"
+        log(f"[bench] {name}: {t_ms:.3f} ms/launch, {work / 1e12:.3f} TFLOP -> "
+            f"{ach:,.1f} TFLOP/s")
+    return dict(bound=bound, achieved=round(ach, 1), peak=peak, unit=unit,
+                frac=round(ach / peak, 4), traffic=recorded_traffic(name, w.name), kernel=name,
+                kernel_us=round(t_ms * 1e3, 2))
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the counter summaries
+    under profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by a copy kernel's
+    reading), or None when none is recorded or the kernel's source file has
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        text = open(path).read()
+        f = dict(re.findall(r"^(kernel|workload|traffic_bytes_per_launch|kernel_source|"
+                            r"kernel_source_sha256): (\S+)$", text, flags=re.M))
+        if f.get("kernel") != kernel or f.get("workload") != workload:
+            continue
+        src = os.path.join(ROOT, f.get("kernel_source", ""))
+        if not os.path.isfile(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != f.get("kernel_source_sha256"):
+            log(f"[bench] {os.path.basename(path)}: kernel source changed since the counters "
+                "were taken; traffic not reported")
+            return None
+        return int(f["traffic_bytes_per_launch"])
+    return None
 
 if __name__ == "__main__":
     sys.exit(main())

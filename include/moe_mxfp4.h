@@ -92,6 +92,25 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int k);
 const char* moe_status_str(int status);
 
 /*
+ * Kernel timing hook (measurement only; no step of the layer depends on it).
+ * While set, the i-th kernel launch (i < n) of every call below made from
+ * the same host thread carries events[2i] and events[2i+1] as its start and
+ * stop events, which the runtime stamps when that kernel's dispatch begins
+ * and ends, so hipEventElapsedTime(events[2i], events[2i+1]) is the kernel's
+ * own duration. The array holds 2n caller-created events (hipEventCreate)
+ * that must outlive their use. moe_set_kernel_events(NULL, 0) turns the hook
+ * off. Returns MOE_OK, or MOE_ERR_INVALID_ARG for n < 0 or a NULL array with
+ * n > 0.
+ */
+int moe_set_kernel_events(hipEvent_t* events, int n);
+
+/* Number of kernels the last call from this host thread launched. */
+int moe_last_call_launches(void);
+
+/* Name of launch i of that call (static string), or NULL if out of range. */
+const char* moe_launch_name(int i);
+
+/*
  * Router: logits, softmax, top-k with renormalised weights.
  * The gate picks k experts per token (ai.rs article, "How 502 GB runs on a
  * 32 GB card": 6 of 384 per layer) and is a discrete switch (same article,

@@ -18,9 +18,12 @@ from ._lib import (  # noqa: F401
     lib,
     moe_combine,
     moe_expert_ffn_mxfp4,
+    moe_last_call_launches,
+    moe_launch_name,
     moe_layer_forward,
     moe_permute,
     moe_router_topk,
+    moe_set_kernel_events,
     moe_workspace_bytes,
     status_str,
     workspace,

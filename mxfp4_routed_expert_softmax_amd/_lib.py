@@ -56,6 +56,9 @@ _SIGS = {
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_layer_forward": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank), _I, _I,
                                 _P, _P, _P, _P, _SZ, _P]),
+    "moe_set_kernel_events": (_I, [_P, _I]),
+    "moe_last_call_launches": (_I, []),
+    "moe_launch_name": (ctypes.c_char_p, [_I]),
 }
 
 _lib = None
@@ -253,3 +256,18 @@ def moe_layer_forward(x, w_router, logit_bias, routed: BankTensors, shared: Bank
         _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, x))
     _check("moe_layer_forward", st)
+
+
+def moe_set_kernel_events(events, n: int) -> None:
+    """Timing hook: `events` is a ctypes array of n hipEvent_t handles (or
+    None with n = 0 to turn the hook off)."""
+    _check("moe_set_kernel_events", lib().moe_set_kernel_events(events, n))
+
+
+def moe_last_call_launches() -> int:
+    return int(lib().moe_last_call_launches())
+
+
+def moe_launch_name(i: int) -> str | None:
+    r = lib().moe_launch_name(i)
+    return None if r is None else r.decode()

@@ -99,9 +99,46 @@ LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
   return L;
 }
 
+// Launch log of the last entry-point call on this host thread.
+constexpr int kMaxLogged = 32;
+struct LaunchLog {
+  hipEvent_t* events = nullptr;
+  int cap = 0;
+  int n = 0;
+  const char* names[kMaxLogged];
+};
+thread_local LaunchLog g_log;
+
+void begin_call() { g_log.n = 0; }
+
 }  // namespace
 
+namespace moe {
+void next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  const bool on = g_log.events && g_log.n < g_log.cap;
+  *start = on ? g_log.events[2 * g_log.n] : nullptr;
+  *stop = on ? g_log.events[2 * g_log.n + 1] : nullptr;
+}
+void log_launch(const char* name) {
+  if (g_log.n < kMaxLogged) g_log.names[g_log.n] = name;
+  ++g_log.n;
+}
+}  // namespace moe
+
 extern "C" {
+
+int moe_set_kernel_events(hipEvent_t* events, int n) {
+  if (n < 0 || (n > 0 && !events)) return MOE_ERR_INVALID_ARG;
+  g_log.events = n > 0 ? events : nullptr;
+  g_log.cap = n;
+  return MOE_OK;
+}
+
+int moe_last_call_launches(void) { return g_log.n; }
+
+const char* moe_launch_name(int i) {
+  return (i >= 0 && i < g_log.n && i < kMaxLogged) ? g_log.names[i] : nullptr;
+}
 
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k) {
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0) return 0;
@@ -127,6 +164,7 @@ const char* moe_status_str(int status) {
 int moe_router_topk(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
                     int T, int H, int E, int k, int32_t* topk_ids, float* topk_w,
                     float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  begin_call();
   int st = check_dims(T, H, E, k, 32);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -148,6 +186,7 @@ int moe_router_topk(const void* x_bf16, const void* w_router_bf16, const float* 
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
                 int32_t* row_token, int32_t* inv_row, void* ws, size_t ws_bytes,
                 hipStream_t stream) {
+  begin_call();
   int st = check_dims(T, 32, E, k, 32);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -165,6 +204,7 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_of
 int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
                          const int32_t* expert_offsets, const int32_t* row_token, int T, int R,
                          float* y_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  begin_call();
   int st = check_bank(bank);
   if (st != MOE_OK) return st;
   st = check_dims(T, bank->H, bank->E, 1, bank->I);
@@ -224,6 +264,7 @@ int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
 int moe_combine(const float* y_rows, const int32_t* inv_row, const float* topk_w,
                 const float* y_shared, int T, int k, int H, int R, float* out,
                 hipStream_t stream) {
+  begin_call();
   int st = check_dims(T, H, k, k, 32);
   if (st != MOE_OK) return st;
   if (R < 0) return MOE_ERR_INVALID_ARG;
@@ -239,6 +280,7 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float
                       const moe_mxfp4_bank* routed, const moe_mxfp4_bank* shared, int T, int k,
                       float* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                       size_t ws_bytes, hipStream_t stream) {
+  begin_call();
   int st = check_bank(routed);
   if (st != MOE_OK) return st;
   const int E = routed->E, H = routed->H, I = routed->I;

@@ -44,7 +44,7 @@ void launch_combine(const float* y_rows, const int32_t* inv_row, const float* w,
                     const float* y_shared, int T, int k, int H, int R, float* out,
                     hipStream_t s) {
   const int nv = H >> 2;
-  hipLaunchKernelGGL(combine_kernel, dim3(T, (nv + 255) / 256), dim3(256), 0, s, y_rows,
+  launch("combine_kernel", combine_kernel, dim3(T, (nv + 255) / 256), dim3(256), 0, s, y_rows,
                      inv_row, w, y_shared, T, k, H, R, out);
 }
 

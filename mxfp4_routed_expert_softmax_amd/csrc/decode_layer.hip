@@ -583,7 +583,10 @@ struct GuRegs {
   uint32_t sg[kGuU], su[kGuU];
 };
 
-__device__ __forceinline__ void gu_issue(const DecodeArgs& a, const int* tab, int it, GuRegs& r) {
+// `live` false: a padding issue of the fixed-trip loop. Its weight loads go
+// through empty buffer resources, which return zeros without a memory access.
+__device__ __forceinline__ void gu_issue(const DecodeArgs& a, const int* tab, int it, GuRegs& r,
+                                         bool live = true) {
   const int s = it / a.gu_items, rb = it - s * a.gu_items;
   const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -592,10 +595,11 @@ __device__ __forceinline__ void gu_issue(const DecodeArgs& a, const int* tab, in
   const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> 5;
   const uint8_t* gbase = a.routed.gu_codes + (size_t)e * 2 * a.I * crow;
   const uint8_t* sbase = a.routed.gu_scales + (size_t)e * 2 * a.I * srow;
-  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, a.I * crow);
-  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, a.I * crow);
-  const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, a.I * srow);
-  const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, a.I * srow);
+  const uint32_t cb = live ? a.I * crow : 0u, sb = live ? a.I * srow : 0u;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, cb);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, cb);
+  const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, sb);
+  const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, sb);
   const int co = nr * crow + j * 16, so = nr * srow + j;
 #pragma unroll
   for (int u = 0; u < kGuU; ++u) {
@@ -664,16 +668,16 @@ __global__ __launch_bounds__(kThreads) void gateup_stream_kernel(DecodeArgs a, i
   if (b >= n) return;
   // Items b + kG, two per iteration with fixed buffers and no early exit (an
   // exit between the halves would let the compiler merge them and move the
-  // buffers to scratch). Loads past this workgroup's last item re-read its
-  // current item (cache hits) and are not used.
+  // buffers to scratch). Issues past this workgroup's last item are padding:
+  // their weight loads read nothing (empty resources) and are not used.
   const int mine = (n - b + G - 1) / G;
   GuRegs A, B;
   gu_issue(a, tab, b, A);
   for (int k = 0; k < mine; k += 2) {
     const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
-    gu_issue(a, tab, i1 < n ? i1 : i0, B);
+    gu_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
     gu_compute(a, tab, i0, A, s_x);
-    gu_issue(a, tab, i2 < n ? i2 : i0, A);
+    gu_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
     if (i1 < n) gu_compute(a, tab, i1, B, s_x);
   }
 }
@@ -684,7 +688,8 @@ struct DnRegs {
   f32x4_t h[3];  // this workgroup's share of the item's h row (I <= 3072)
 };
 
-__device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, int it, DnRegs& r) {
+__device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, int it, DnRegs& r,
+                                         bool live = true) {
   const int s = it / a.dn_items, c = it - s * a.dn_items;
   const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
   const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
@@ -693,9 +698,9 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, in
   const int nr = min(c * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
   const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
   const __amdgpu_buffer_rsrc_t rd =
-      matrix_rsrc(a.routed.d_codes + (size_t)e * a.H * crow, a.H * crow);
+      matrix_rsrc(a.routed.d_codes + (size_t)e * a.H * crow, live ? a.H * crow : 0u);
   const __amdgpu_buffer_rsrc_t rds =
-      matrix_rsrc(a.routed.d_scales + (size_t)e * a.H * srow, a.H * srow);
+      matrix_rsrc(a.routed.d_scales + (size_t)e * a.H * srow, live ? a.H * srow : 0u);
   const int co = nr * crow + j * 16, so = nr * srow + j;
 #pragma unroll
   for (int u = 0; u < kDnU; ++u) {
@@ -761,9 +766,9 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
   dn_issue(a, tab, b, A);
   for (int k = 0; k < mine; k += 2) {
     const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
-    dn_issue(a, tab, i1 < n ? i1 : i0, B);
+    dn_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
     dn_compute(a, tab, i0, A, s_h);
-    dn_issue(a, tab, i2 < n ? i2 : i0, A);
+    dn_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
     if (i1 < n) dn_compute(a, tab, i1, B, s_h);
   }
   if (!combine) return;
@@ -901,11 +906,11 @@ void launch_chain(const DecodeArgs& a, const DecodeLayout& L, bool ffn, bool sha
                   int shared_dn, const int32_t* rtok, hipStream_t s) {
   if (!ffn) {
     const int grid = L.nb_router + 1 + (shared ? L.gu_items : 0);
-    hipLaunchKernelGGL(route_kernel<MT>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
+    launch("route_kernel", route_kernel<MT>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
   }
-  hipLaunchKernelGGL(gateup_kernel<MT>, dim3(routed_gu + shared_dn), dim3(kThreads), kLdsBytes, s,
+  launch("gateup_kernel", gateup_kernel<MT>, dim3(routed_gu + shared_dn), dim3(kThreads), kLdsBytes, s,
                      a, routed_gu, rtok);
-  hipLaunchKernelGGL(down_kernel<MT>, dim3(L.max_slots * L.dn_items), dim3(kThreads), kLdsBytes, s,
+  launch("down_kernel", down_kernel<MT>, dim3(L.max_slots * L.dn_items), dim3(kThreads), kLdsBytes, s,
                      a, ffn ? 0 : 1);
 }
 
@@ -952,7 +957,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   const int routed_gu = L.max_slots * L.gu_items;
   const int shared_dn = shared ? L.dn_items : 0;
   if (ffn) {
-    hipLaunchKernelGGL(ffn_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    launch("ffn_table_kernel", ffn_table_kernel, dim3(1), dim3(kThreads), 0, s, a);
   }
   // One token (or one row per expert): every slot holds a single row, and a
   // kernel built for one staged row needs far fewer registers.
@@ -962,13 +967,13 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
                       1 + 3 * L.max_slots <= 1024;
   if (stream) {
     const int grid = L.nb_router + 1 + (shared ? L.gu_items : 0);
-    hipLaunchKernelGGL(route_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
+    launch("route_kernel", route_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
     const int gg = routed_gu < kStreamBlocks ? routed_gu : kStreamBlocks;
-    hipLaunchKernelGGL(gateup_stream_kernel, dim3(gg + shared_dn), dim3(kThreads), kLdsBytes, s,
+    launch("gateup_stream_kernel", gateup_stream_kernel, dim3(gg + shared_dn), dim3(kThreads), kLdsBytes, s,
                        a, gg);
     const int nd = L.max_slots * L.dn_items;
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
-    hipLaunchKernelGGL(down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a, gd, 1);
+    launch("down_stream_kernel", down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a, gd, 1);
   } else if (one)
     launch_chain<1>(a, L, ffn, shared, routed_gu, shared_dn, ffn ? d.row_token : a.row_token, s);
   else

@@ -380,10 +380,10 @@ void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   g.h = L.h;
   g.y = p.y;
   g.y_sh = p.y_sh;
-  hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
-  hipLaunchKernelGGL(gemm_kernel<true>, dim3(L.max_tiles * (p.I / (kWRows / 2))),
+  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  launch("gemm_gateup_kernel", gemm_kernel<true>, dim3(L.max_tiles * (p.I / (kWRows / 2))),
                      dim3(kThreads), 0, s, g);
-  hipLaunchKernelGGL(gemm_kernel<false>, dim3(L.max_tiles * (p.H / kWRows)), dim3(kThreads), 0,
+  launch("gemm_down_kernel", gemm_kernel<false>, dim3(L.max_tiles * (p.H / kWRows)), dim3(kThreads), 0,
                      s, g);
 }
 

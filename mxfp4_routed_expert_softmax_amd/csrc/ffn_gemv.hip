@@ -243,10 +243,10 @@ void launch_expert_ffn(const FfnProblem& p, hipStream_t s) {
   if (slots == 0) return;
   const size_t lds_gu = (size_t)kGemvMT * p.H * sizeof(uint16_t);
   const size_t lds_d = (size_t)kGemvMT * p.I * sizeof(float);
-  hipLaunchKernelGGL(gateup_gemv_kernel<5>,
+  launch("gateup_gemv_kernel", gateup_gemv_kernel<5>,
                      dim3((p.I + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock, slots),
                      dim3(kGemvThreads), lds_gu, s, p);
-  hipLaunchKernelGGL(down_gemv_kernel<9>,
+  launch("down_gemv_kernel", down_gemv_kernel<9>,
                      dim3((p.H + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock, slots),
                      dim3(kGemvThreads), lds_d, s, p);
 }

@@ -3,10 +3,28 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Timing hook state (abi.hip): the start / stop events for the next launch
+// (null when the hook is off), and the log of launch names of the call.
+void next_launch_events(hipEvent_t* start, hipEvent_t* stop);
+void log_launch(const char* name);
+
+// Every kernel launch goes through here. With the hook set, the launch
+// carries the caller's start / stop events, which the runtime stamps at the
+// kernel's own dispatch begin and end (no marker packets between kernels).
+template <typename F, typename... Args>
+inline void launch(const char* name, F kernel, dim3 grid, dim3 block, uint32_t shmem,
+                   hipStream_t s, Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  next_launch_events(&start, &stop);
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, start, stop, 0, args...);
+  log_launch(name);
+}
 
 // Token counts up to this use the GEMV router; above it the MFMA GEMM.
 constexpr int kRouterGemvMaxT = 16;

@@ -143,17 +143,17 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                     hipStream_t s) {
   const int R = T * k;
   if (R <= kPermuteChunk) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, R, k, E,
+    launch("permute_small_kernel", permute_small_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, R, k, E,
                        offsets, row_token, inv_row, active);
     return;
   }
   const int nchunks = (R + kPermuteChunk - 1) / kPermuteChunk;
   int32_t* counts = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(permute_count_kernel, dim3(nchunks), dim3(kPermThreads), 0, s, ids, R, E,
+  launch("permute_count_kernel", permute_count_kernel, dim3(nchunks), dim3(kPermThreads), 0, s, ids, R, E,
                      counts);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, nchunks, E, counts,
+  launch("permute_scan_kernel", permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, nchunks, E, counts,
                      offsets, active);
-  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kPermThreads), 0, s, ids, R, k,
+  launch("permute_scatter_kernel", permute_scatter_kernel, dim3(nchunks), dim3(kPermThreads), 0, s, ids, R, k,
                      E, counts, row_token, inv_row);
 }
 

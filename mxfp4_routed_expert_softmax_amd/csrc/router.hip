@@ -107,10 +107,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
                           int T, int H, int E, float* logits, hipStream_t s) {
   if (T <= kRouterGemvMaxT) {
-    hipLaunchKernelGGL(router_gemv_kernel, dim3((E + 3) / 4), dim3(256), 0, s,
+    launch("router_gemv_kernel", router_gemv_kernel, dim3((E + 3) / 4), dim3(256), 0, s,
                        x, wr, bias, T, H, E, logits);
   } else {
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((T + 127) / 128, (E + 127) / 128),
+    launch("router_mfma_kernel", router_mfma_kernel, dim3((T + 127) / 128, (E + 127) / 128),
                        dim3(256), 0, s, x, wr, bias, T, H, E, logits);
   }
 }
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                  hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  launch("topk_kernel", topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
 }
 
 }  // namespace moe

@@ -17,7 +17,8 @@ def test_library_exports_every_header_function():
     names = M.header_functions()
     assert set(names) == {"moe_router_topk", "moe_permute", "moe_expert_ffn_mxfp4",
                           "moe_combine", "moe_layer_forward", "moe_workspace_bytes",
-                          "moe_status_str"}
+                          "moe_status_str", "moe_set_kernel_events",
+                          "moe_last_call_launches", "moe_launch_name"}
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -104,6 +105,18 @@ def test_binding_raises_without_a_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         L.lib()
+
+
+def test_kernel_timing_hook_validation():
+    lib = M.lib()
+    assert lib.moe_set_kernel_events(None, -1) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_set_kernel_events(None, 2) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_set_kernel_events(None, 0) == M.MOE_OK
+    # a call rejected by validation launches nothing
+    assert _fwd(_bank(), T=-1) == M.MOE_ERR_INVALID_ARG
+    assert M.moe_last_call_launches() == 0
+    assert M.moe_launch_name(0) is None
+    assert M.moe_launch_name(-1) is None
 
 
 def test_oracle_is_not_imported_by_the_product_path():
