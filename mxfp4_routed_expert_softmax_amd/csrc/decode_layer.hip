@@ -57,6 +57,8 @@ constexpr int kGuRows = 8;      // gate/up rows per item
 constexpr int kGuU = 5;         // gate/up chunks per lane per batch (K = 5120 in one)
 constexpr int kDnRows = 32;     // down: 8 lanes per row, 8 rows per wave
 constexpr int kDnU = 9;         // down chunks per lane per batch (K = 2304 in one)
+constexpr int kReplicas = 16;        // copies of the one-token routing table
+constexpr int kReplicaWords = 512;   // 4 KB apart, so readers spread over channels
 constexpr int kRouterV = 16;    // router: 16-byte vectors per lane (H <= 8192)
 constexpr long kSpinLimit = 1L << 20;  // polls (with s_sleep) before giving up
 
@@ -135,6 +137,9 @@ struct DecodeArgs {
   float* h;            // [rows][I]
   float* y;            // [rows][H]
   uint64_t* flags;     // [nb_router] router flags
+  uint64_t* tagged;    // one-token path: [E] logits, then kReplicas routing tables,
+                       // each word (tag << 32 | 32-bit value)
+  uint32_t tag;        // this launch's tag
   int32_t* cnt_dn;     // [dn_items] routed down items finished per column
   uint64_t epoch;
   int32_t* status;
@@ -236,13 +241,14 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
 }
 
 // Wave-wide top-k of one logit row; lanes < k write ids / weights. Lane l
-// holds experts l, l+64, ... (E <= 1024); each round takes the best untaken
+// holds experts l, l+64, ... (E <= 64 NK); each round takes the best untaken
 // key of every lane and the wave maximum of those.
+template <int NK>
 __device__ void topk_row(const float* L, int E, int k, int* ids, float* w) {
   const int lane = lane_id();
-  uint64_t key[16];
+  uint64_t key[NK];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NK; ++i) {
     const int e = lane + kWave * i;
     key[i] = e < E ? topk_key(cld(L + e), e) : 0;  // 0 is below every real key
   }
@@ -251,14 +257,14 @@ __device__ void topk_row(const float* L, int E, int k, int* ids, float* w) {
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < NK; ++i) best = key[i] > best ? key[i] : best;
     const uint64_t win = wave_max_key(best);
     const int id = (int)(0xffffffffu - (uint32_t)win);
     uint32_t b = (uint32_t)(win >> 32);
     b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
     const float val = __uint_as_float(b);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < NK; ++i)
       if (key[i] == win) key[i] = 0;
     if (lane == j) {
       my_val = val;
@@ -292,7 +298,7 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
   int* s_first = reinterpret_cast<int*>(s_w + R);
   int* s_tmp = s_first + R;
   for (int t = threadIdx.x >> 6; t < a.T; t += kThreads / kWave)
-    topk_row(a.logits + (size_t)t * a.E, a.E, a.k, s_ids + t * a.k, s_w + t * a.k);
+    topk_row<16>(a.logits + (size_t)t * a.E, a.E, a.k, s_ids + t * a.k, s_w + t * a.k);
   __syncthreads();
   // Stable counting sort by ranks, no atomics: pair p (token p / k) of
   // expert e goes to row (#pairs with a smaller expert) + (#earlier pairs
@@ -551,14 +557,14 @@ __device__ void down_item(const DecodeArgs& a, const Slot& sd, int rb, f32x4_t* 
   }
 }
 
-// Combine of output columns [32c, 32c + 32): the shared row (written by an
-// earlier launch), then the k routed rows in slot order j = 0..k-1 (written
-// in this launch, hence the coherent loads), one fp32 fma each.
+// Combine of output columns [32c, 32c + 32): the shared row, then the k
+// routed rows in slot order j = 0..k-1, one fp32 fma each (coherent loads:
+// rows may have been written by other workgroups of this launch).
 __device__ void combine_column(const DecodeArgs& a, int c) {
   const int n = c * kDnRows + (threadIdx.x & 31);
   if (n >= a.H) return;
   for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
-    float v = a.has_shared ? a.y[(size_t)(a.R + t) * a.H + n] : 0.0f;
+    float v = a.has_shared ? cld(a.y + (size_t)(a.R + t) * a.H + n) : 0.0f;
     for (int j = 0; j < a.k; ++j) {
       const int r = min(max(a.inv_row[t * a.k + j], 0), a.R - 1);
       v = fmaf(a.route_w[t * a.k + j], cld(a.y + (size_t)r * a.H + n), v);
@@ -642,39 +648,184 @@ __device__ __forceinline__ void gu_compute(const DecodeArgs& a, const int* tab, 
   if (j == 0 && n < a.I) a.h[(size_t)row * a.I + n] = silu_mul(g, u);
 }
 
-// Stages the token row and the slot table into LDS; returns the table.
-__device__ __forceinline__ int* stage_token_and_table(const DecodeArgs& a, char* lds) {
+// Router rows for one token with x staged in LDS: a wave per expert row,
+// the row's loads issued before the token is staged, so both are in flight
+// together and only the weights live in registers. Each logit is published
+// as one 64-bit word carrying the launch tag, so a reader knows a value is
+// this launch's from the word itself (no flag, no ordering between words).
+__device__ void router_rows_one(const DecodeArgs& a, int b, uint4* s_x) {
+  const int lane = lane_id();
+  const int e = min(b * 4 + (int)(threadIdx.x >> 6), a.E - 1);
+  const int nv = a.H >> 3;
+  const uint4* wrow = reinterpret_cast<const uint4*>(a.wr + (size_t)e * a.H);
+  uint4 wv[kRouterV];
+#pragma unroll
+  for (int i = 0; i < kRouterV; ++i) wv[i] = wrow[min(lane + kWave * i, nv - 1)];
+  stage_rows<uint4>(
+      nv, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+      [&](int idx, uint4 v) { s_x[idx] = v; });
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRouterV; ++i)
+    if (lane + kWave * i < nv) acc = dot8_bf16(wv[i], s_x[lane + kWave * i], acc);
+  acc = wave_sum(acc);
+  if (lane == 0 && b * 4 + (int)(threadIdx.x >> 6) < a.E) {
+    const float v = acc + (a.bias ? a.bias[e] : 0.0f);
+    cst(a.tagged + e, ((uint64_t)a.tag << 32) | __float_as_uint(v));
+  }
+}
+
+// Polls `n` tagged words at `src` (lane i holds words i, i + 64, ...) until
+// every one carries `tag`; returns the values through `out` (NK per lane).
+// Bounded: a timeout sets the status word and returns what was read, which
+// every consumer clamps.
+template <int NK>
+__device__ void poll_tagged(const DecodeArgs& a, const uint64_t* src, int n, uint32_t* out) {
+  const int lane = lane_id();
+  for (long it = 0;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int q = lane + kWave * i;
+      const uint64_t v = q < n ? cld(src + q) : ((uint64_t)a.tag << 32);
+      out[i] = (uint32_t)v;
+      ok &= (uint32_t)(v >> 32) == a.tag;
+    }
+    if (__all(ok)) return;
+    if (it > kSpinLimit) {
+      if (lane == 0) cst(a.status, 2);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// The one-token routing workgroup (wave 0): waits for the tagged logits,
+// takes the top-k (descending logit, ties to the lower id) with weights
+// renormalised over the k, writes the layer outputs and the table the down
+// launch reads, and publishes the chosen ids as tagged words in kReplicas
+// copies for the gate/up workgroups of this launch.
+template <int NK>
+__device__ void route_token_tagged(const DecodeArgs& a) {
+  const int lane = lane_id(), k = a.k, ms = a.max_slots;
+  uint32_t raw[NK];
+  poll_tagged<NK>(a, a.tagged, a.E, raw);
+  uint64_t key[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = e < a.E ? topk_key(__uint_as_float(raw[i]), e) : 0;
+  }
+  float my_val = 0.0f, top = 0.0f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) best = key[i] > best ? key[i] : best;
+    const uint64_t win = wave_max_key(best);
+    const int id = (int)(0xffffffffu - (uint32_t)win);
+    uint32_t bits = (uint32_t)(win >> 32);
+    bits = (bits & 0x80000000u) ? (bits & 0x7fffffffu) : ~bits;
+    const float val = __uint_as_float(bits);
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      if (key[i] == win) key[i] = 0;
+    if (lane == j) {
+      my_val = val;
+      my_id = id;
+    }
+    if (j == 0) top = val;
+  }
+  const float z = lane < k ? expf(my_val - top) : 0.0f;
+  const float wj = z / wave_sum(z);
+  int slot = 0;
+  for (int q = 0; q < k; ++q) slot += __shfl(my_id, q, kWave) < my_id;
+  if (lane < k) {
+    a.tab[1 + slot] = my_id;
+    a.tab[1 + ms + slot] = slot;
+    a.tab[1 + 2 * ms + slot] = 1;
+    a.row_token[slot] = 0;
+    a.inv_row[lane] = slot;
+    a.route_w[lane] = wj;
+    if (a.ids_out) a.ids_out[lane] = my_id;
+    if (a.w_out) a.w_out[lane] = wj;
+    uint64_t* rep0 = a.tagged + a.E;
+    for (int r = 0; r < kReplicas; ++r)
+      cst(rep0 + (size_t)r * kReplicaWords + lane, ((uint64_t)a.tag << 32) | (uint32_t)my_id);
+  }
+  if (lane == 0) a.tab[0] = k;
+  for (int i = lane; i < a.dn_items; i += kWave) a.cnt_dn[i] = 0;
+}
+
+// A gate/up workgroup's copy of the routing: polls replica `r` and builds
+// the slot table in LDS (slot = rank of the expert id among the k, so slots
+// ascend by expert id; one row per slot, row = slot).
+__device__ void load_routing_tagged(const DecodeArgs& a, int r, int* s_tab) {
+  const int k = a.k, ms = a.max_slots;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    uint32_t v[1];
+    poll_tagged<1>(a, a.tagged + a.E + (size_t)r * kReplicaWords, k, v);
+    const int my_id = lane < k ? min(max((int)v[0], 0), a.E - 1) : 0x7fffffff;
+    int slot = 0;
+    for (int q = 0; q < k; ++q) slot += __shfl(my_id, q, kWave) < my_id;
+    if (lane < k) {
+      s_tab[1 + slot] = my_id;
+      s_tab[1 + ms + slot] = slot;
+      s_tab[1 + 2 * ms + slot] = 1;
+    }
+    if (lane == 0) s_tab[0] = k;
+  }
+  __syncthreads();
+}
+
+// Decode gate/up, one launch: [router rows | the routing workgroup |
+// shared expert gate/up items | G routed workgroups]. The routed workgroups
+// stage the token, poll a replica of the routing table and then stream the
+// items b, b + G, b + 2G, ... of the selected experts (items slot-major, 8
+// rows each) with two register buffers, so the weights of the next item are
+// in flight while the current one is computed.
+__global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
+                                                                int G) {
+  extern __shared__ __align__(16) char lds[];
+  const int b0 = blockIdx.x;
+  if (b0 < a.nb_router) {
+    router_rows_one(a, b0, reinterpret_cast<uint4*>(lds));
+    return;
+  }
+  if (b0 == a.nb_router) {
+    if (threadIdx.x < kWave) {
+      if (a.E <= 6 * kWave)
+        route_token_tagged<6>(a);
+      else
+        route_token_tagged<16>(a);
+    }
+    return;
+  }
+  if (b0 <= a.nb_router + n_shared) {
+    gateup_item<1>(a, shared_slot(a), b0 - a.nb_router - 1, reinterpret_cast<uint4*>(lds),
+                   nullptr);
+    return;
+  }
+  const int b = b0 - a.nb_router - 1 - n_shared;
   uint4* s_x = reinterpret_cast<uint4*>(lds);
-  int* s_tab = reinterpret_cast<int*>(lds + a.H * 2);
+  int* tab = reinterpret_cast<int*>(lds + a.H * 2);
   stage_rows<uint4>(
       a.H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
       [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
-  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
-  __syncthreads();
-  s_tab[0] = min(max(s_tab[0], 0), a.max_slots);
-  return s_tab;
-}
-
-__global__ __launch_bounds__(kThreads) void gateup_stream_kernel(DecodeArgs a, int G) {
-  extern __shared__ __align__(16) char lds[];
-  if ((int)blockIdx.x >= G) {  // shared expert down rows (one-shot)
-    down_item<1>(a, shared_slot(a), blockIdx.x - G, reinterpret_cast<f32x4_t*>(lds), a.y, false);
-    return;
-  }
-  int* tab = stage_token_and_table(a, lds);
-  const uint4* s_x = reinterpret_cast<const uint4*>(lds);
+  load_routing_tagged(a, b % kReplicas, tab);
   const int n = tab[0] * a.gu_items;
-  const int b = blockIdx.x;
   if (b >= n) return;
-  // Items b + kG, two per iteration with fixed buffers and no early exit (an
-  // exit between the halves would let the compiler merge them and move the
-  // buffers to scratch). Issues past this workgroup's last item are padding:
-  // their weight loads read nothing (empty resources) and are not used.
+  // Fixed trip over pairs of items with no early exit (an exit between the
+  // halves would let the compiler merge them and move the buffers to
+  // scratch). Issues past this workgroup's last item are padding: their
+  // weight loads read nothing (empty resources) and are not used.
   const int mine = (n - b + G - 1) / G;
   GuRegs A, B;
   gu_issue(a, tab, b, A);
-  for (int k = 0; k < mine; k += 2) {
-    const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
+  for (int kk = 0; kk < mine; kk += 2) {
+    const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
     gu_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
     gu_compute(a, tab, i0, A, s_x);
     gu_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
@@ -688,19 +839,38 @@ struct DnRegs {
   f32x4_t h[3];  // this workgroup's share of the item's h row (I <= 3072)
 };
 
-__device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, int it, DnRegs& r,
-                                         bool live = true) {
+// Down item `it`: items [0, nr) are (routed slot, 32-row group) pairs,
+// slot-major; items [nr, nr + dn_items) are the shared expert's groups.
+struct DnItem {
+  const uint8_t* codes;   // the item's expert's down codes
+  const uint8_t* scales;
+  int row;                // h / y row
+  int c;                  // 32-row group of the output
+};
+
+__device__ __forceinline__ DnItem dn_item(const DecodeArgs& a, const int* tab, int nr, int it) {
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  if (it >= nr) {
+    const int c = min(it - nr, a.dn_items - 1);
+    return DnItem{a.shared.d_codes, a.shared.d_scales, min(a.R, a.rows - 1), c};
+  }
   const int s = it / a.dn_items, c = it - s * a.dn_items;
   const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
   const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  return DnItem{a.routed.d_codes + (size_t)e * a.H * crow, a.routed.d_scales + (size_t)e * a.H * srow,
+                row, c};
+}
+
+__device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, int n_routed, int it,
+                                         DnRegs& r, bool live = true) {
+  const DnItem d = dn_item(a, tab, n_routed, it);
+  const int c = d.c, row = d.row;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & 7;
   const int nr = min(c * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
   const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
-  const __amdgpu_buffer_rsrc_t rd =
-      matrix_rsrc(a.routed.d_codes + (size_t)e * a.H * crow, live ? a.H * crow : 0u);
-  const __amdgpu_buffer_rsrc_t rds =
-      matrix_rsrc(a.routed.d_scales + (size_t)e * a.H * srow, live ? a.H * srow : 0u);
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(d.codes, live ? a.H * crow : 0u);
+  const __amdgpu_buffer_rsrc_t rds = matrix_rsrc(d.scales, live ? a.H * srow : 0u);
   const int co = nr * crow + j * 16, so = nr * srow + j;
 #pragma unroll
   for (int u = 0; u < kDnU; ++u) {
@@ -713,7 +883,7 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, in
   for (int i = 0; i < 3; ++i) r.h[i] = hrow[min((int)threadIdx.x + i * kThreads, nv - 1)];
 }
 
-__device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, int it,
+__device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, int nr, int it,
                                            const DnRegs& r, f32x4_t* s_h) {
   const int nv = a.I >> 2;
   __syncthreads();  // previous item's reads of s_h are done
@@ -723,8 +893,8 @@ __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, 
     s_h[(f & 7) * (8 * kDnU) + (f >> 3)] = r.h[i];
   }
   __syncthreads();
-  const int s = it / a.dn_items, c = it - s * a.dn_items;
-  const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  const DnItem d = dn_item(a, tab, nr, it);
+  const int c = d.c, row = d.row;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & 7;
   const int n = c * kDnRows + wave * 8 + (lane >> 3);
@@ -747,43 +917,74 @@ __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, 
   if (j == 0 && n < a.H) cst(a.y + (size_t)row * a.H + n, v);
 }
 
-// `combine`: after its last item each workgroup drains its y stores and bumps
-// the counter of every column it wrote; the workgroup that completes a
-// column combines it.
-__global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int G, int combine) {
+// Combine of output columns [32c, 32c + 32) of the one token: the shared
+// row, then the k routed rows in order j = 0..k-1, one fp32 fma each. Rows
+// and weights come from LDS; the y rows were written by other workgroups of
+// this launch (coherent loads, all issued together).
+__device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
+                                   const float* s_w) {
+  const int n = c * kDnRows + (int)threadIdx.x;
+  if (threadIdx.x >= kDnRows || n >= a.H) return;
+  float v = a.has_shared ? cld(a.y + (size_t)a.R * a.H + n) : 0.0f;
+  for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
+    float y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = min(max(s_inv[min(j0 + u, a.k - 1)], 0), a.R - 1);
+      y[u] = cld(a.y + (size_t)r * a.H + n);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < a.k) v = fmaf(s_w[j0 + u], y[u], v);
+  }
+  a.out[n] = v;
+}
+
+// One token, down projection: routed (slot, 32-row group) items, then the
+// shared expert's, streamed by persistent workgroups with two register
+// buffers. After its last item a workgroup drains its y stores and bumps
+// the counters of all the columns it wrote at once; the workgroup that
+// completes a column (every routed slot and the shared expert) combines it.
+__global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
-  __shared__ int s_last;
+  __shared__ int s_last[32];
   int* tab = reinterpret_cast<int*>(lds);
+  int* s_inv = tab + 1 + 3 * a.max_slots;
+  float* s_w = reinterpret_cast<float*>(s_inv + a.k);
   f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int));
   for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) tab[i] = a.tab[i];
+  for (int i = threadIdx.x; i < a.k; i += kThreads) {
+    s_inv[i] = a.inv_row[i];
+    s_w[i] = a.route_w[i];
+  }
   __syncthreads();
   const int ns = min(max(tab[0], 0), a.max_slots);
-  const int n = ns * a.dn_items;
+  const int nr = ns * a.dn_items;
+  const int n = nr + (a.has_shared ? a.dn_items : 0);
+  const int parts = ns + (a.has_shared ? 1 : 0);  // contributions per column
   const int b = blockIdx.x;
   if (b >= n) return;
-  const int mine = (n - b + G - 1) / G;
+  const int mine = (n - b + G - 1) / G;  // <= 32 (the grid is at least n / 32)
   DnRegs A, B;
-  dn_issue(a, tab, b, A);
+  dn_issue(a, tab, nr, b, A);
   for (int k = 0; k < mine; k += 2) {
     const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
-    dn_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
-    dn_compute(a, tab, i0, A, s_h);
-    dn_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
-    if (i1 < n) dn_compute(a, tab, i1, B, s_h);
+    dn_issue(a, tab, nr, i1 < n ? i1 : i0, B, i1 < n);
+    dn_compute(a, tab, nr, i0, A, s_h);
+    dn_issue(a, tab, nr, i2 < n ? i2 : i0, A, i2 < n);
+    if (i1 < n) dn_compute(a, tab, nr, i1, B, s_h);
   }
-  if (!combine) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int i = blockIdx.x; i < n; i += G) {
-    const int c = i % a.dn_items;
-    if (threadIdx.x == 0)
-      s_last =
-          __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          ns - 1;
-    __syncthreads();
-    if (s_last) combine_column(a, c);
-    __syncthreads();
+  if ((int)threadIdx.x < min(mine, 32)) {
+    const int c = (b + (int)threadIdx.x * G) % a.dn_items;  // nr is a multiple of dn_items
+    s_last[threadIdx.x] =
+        __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        parts - 1;
   }
+  __syncthreads();
+  for (int t = 0; t < min(mine, 32); ++t)
+    if (s_last[t]) combine_column_one(a, (b + t * G) % a.dn_items, s_inv, s_w);
 }
 
 // ---------------------------------------------------------------------------
@@ -859,7 +1060,7 @@ uint64_t next_epoch() {
 struct DecodeLayout {
   int max_slots, rows, gu_items, dn_items, nb_router;
   size_t off_flags, off_cnt, off_status, off_tab, off_rt, off_inv, off_logits, off_w, off_h, off_y,
-      bytes;
+      off_tagged, bytes;
 };
 
 size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -884,6 +1085,8 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   o += al(sizeof(int32_t) * (size_t)L.rows);
   L.off_inv = o;
   o += al(sizeof(int32_t) * (size_t)R);
+  L.off_tagged = o;
+  o += al(sizeof(uint64_t) * (ffn || T != 1 ? 0 : (size_t)E + kReplicas * kReplicaWords));
   L.off_logits = o;
   o += al(sizeof(float) * (size_t)T * E);
   L.off_w = o;
@@ -938,6 +1141,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.ids_out = d.ids_out;
   a.w_out = d.w_out;
   a.flags = reinterpret_cast<uint64_t*>(w + L.off_flags);
+  a.tagged = reinterpret_cast<uint64_t*>(w + L.off_tagged);
   a.cnt_dn = reinterpret_cast<int32_t*>(w + L.off_cnt);
   a.status = reinterpret_cast<int32_t*>(w + L.off_status);
   a.tab = reinterpret_cast<int32_t*>(w + L.off_tab);
@@ -948,6 +1152,10 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.h = reinterpret_cast<float*>(w + L.off_h);
   a.y = ffn ? d.y_rows : reinterpret_cast<float*>(w + L.off_y);
   a.epoch = next_epoch();
+  // 32-bit tag of the launch: consecutive launches differ in the low bits
+  // of the epoch, hence in the tag; zero (a cleared workspace) is never used.
+  a.tag = (uint32_t)(a.epoch ^ (a.epoch >> 32));
+  if (a.tag == 0) a.tag = 0x9e3779b9u;
   a.max_slots = L.max_slots;
   a.rows = L.rows;
   a.nb_router = L.nb_router;
@@ -964,16 +1172,19 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   const bool one = d.T == 1 || (ffn && d.R <= 1);
   const bool stream = d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
                       (d.I >> 5) <= 8 * kDnU && d.I <= 3 * 4 * kThreads &&
-                      1 + 3 * L.max_slots <= 1024;
+                      d.H * 2 + 4 * (1 + 3 * L.max_slots) <= kLdsBytes &&
+                      1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave &&
+                      d.E <= 16 * kWave &&
+                      (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
   if (stream) {
-    const int grid = L.nb_router + 1 + (shared ? L.gu_items : 0);
-    launch("route_kernel", route_kernel<1>, dim3(grid), dim3(kThreads), kLdsBytes, s, a);
+    const int n_sh = shared ? L.gu_items : 0;
     const int gg = routed_gu < kStreamBlocks ? routed_gu : kStreamBlocks;
-    launch("gateup_stream_kernel", gateup_stream_kernel, dim3(gg + shared_dn), dim3(kThreads), kLdsBytes, s,
-                       a, gg);
-    const int nd = L.max_slots * L.dn_items;
+    launch("gateup_fused_kernel", gateup_fused_kernel, dim3(L.nb_router + 1 + n_sh + gg),
+           dim3(kThreads), kLdsBytes, s, a, n_sh, gg);
+    const int nd = L.max_slots * L.dn_items + shared_dn;
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
-    launch("down_stream_kernel", down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a, gd, 1);
+    launch("down_stream_kernel", down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a,
+           gd);
   } else if (one)
     launch_chain<1>(a, L, ffn, shared, routed_gu, shared_dn, ffn ? d.row_token : a.row_token, s);
   else
