@@ -11,18 +11,21 @@
 //
 // X_e are the token rows of expert e's bucket, gathered through row_token;
 // the shared expert is one more bucket over all T tokens. Every bucket is
-// cut into 128-row blocks (listed by a one-workgroup plan kernel); the grid
-// walks (row block, column block) pairs with the column block fastest.
+// cut into 128-row blocks; a one-workgroup plan kernel lists the (row
+// block, column block) tiles of both GEMMs in an L2-friendly order, and
+// each XCD takes a consecutive stretch of the list.
 //
 // Per workgroup (512 threads, one per CU): 128 rows x 256 weight rows (for
 // gate/up: 128 gate + the 128 up rows of the same output columns), 8 waves
 // of 64 x 64 built from v_mfma_f32_16x16x32_bf16 / _f16. K advances 128 per
-// step through a 3-stage LDS pipeline filled by direct global -> LDS loads:
+// step through a 2-stage LDS pipeline filled by direct global -> LDS loads:
 //  * A: 128 rows x 128 K (bf16 x or fp16 h), each row's 16-byte pieces
-//    permuted (piece p at slot p ^ (row & 15)) so fragment reads are
-//    conflict-free;
+//    permuted (piece p at slot p ^ (row & 15));
 //  * B: 256 weight rows x 64 bytes of packed E2M1 codes (piece p of row r
-//    at slot p ^ ((r / 4) & 3)) and their 4 E8M0 bytes per row.
+//    at slot p ^ ((r / 4) & 3)).
+// The E8M0 scales of the tile's weight rows over all of K (40 KB for
+// gate/up at K = 5120) are loaded once per tile: per step they would be 4
+// bytes per row, one cache line each.
 // Lane (column c, lane group g) of a wave takes the 32 codes of K range
 // [32 g, 32 g + 32) of its weight row, one E8M0 block, and converts them
 // with the gfx950 scaled FP4 conversion (exact: an E2M1 value times a power
@@ -33,6 +36,8 @@
 // Precision: x and the dequantised weights are exact in bf16; h is rounded
 // once to fp16 (relative 2^-11; |h| < 65504), the down weights are exact in
 // fp16 for E8M0 exponents in [-23, 13]; every sum is fp32.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -44,13 +49,15 @@ constexpr int kBM = 128;        // bucket rows per tile
 constexpr int kBK = 128;        // K per pipeline step
 constexpr int kWRows = 256;     // weight rows per tile
 constexpr int kThreads = 512;   // 8 waves: 2 (rows) x 4 (weight rows)
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 constexpr int kAPieces = kBM * kBK / 8;       // 16-byte pieces of A per stage (2048)
 constexpr int kBPieces = kWRows * kBK / 32;   // 16-byte pieces of codes per stage (1024)
 constexpr int kABytes = kAPieces * 16;        // 32 KB
 constexpr int kBBytes = kBPieces * 16;        // 16 KB
-constexpr int kSBytes = kWRows * 4;           // 1 KB of E8M0 bytes
-constexpr int kStageBytes = kABytes + kBBytes + kSBytes;
+constexpr int kStageBytes = kABytes + kBBytes;  // 48 KB
+// E8M0 bytes of the tile's 256 weight rows over all of K (K <= 8192: 64 KB),
+// loaded once per tile
+constexpr int kScaleBytes = kWRows * (8192 / 32);
 constexpr int kALoads = kAPieces / kThreads;  // 4 per thread per stage
 constexpr int kBLoads = kBPieces / kThreads;  // 2 per thread per stage
 
@@ -61,10 +68,10 @@ struct GemmArgs {
   int has_shared;
   const int32_t* offsets;    // [E+1] routed buckets, or null (one expert, rows [0, R))
   const int32_t* row_token;  // [R] or null (row r is token r)
-  int32_t* tile_expert;
-  int32_t* tile_m0;
-  int32_t* tile_total;
-  int max_tiles;
+  int32_t* tile_b[2];    // per GEMM (0 gate/up, 1 down): bucket of tile t
+  int32_t* tile_mn[2];   // (row block << 8) | column block of tile t
+  int32_t* tile_count;   // [2] tiles of each GEMM
+  int max_rb;            // capacity in 128-row blocks
   _Float16* h;    // [R + T][I]: routed rows, then the shared expert's T rows
   float* y;       // [R][H]
   float* y_sh;    // [T][H]
@@ -86,10 +93,22 @@ __device__ __forceinline__ Bucket bucket_of(const GemmArgs& g, int b) {
   return Bucket{b, lo, hi - lo, false};
 }
 
-// The list of 128-row blocks of every bucket, routed experts by id, then
-// the shared expert. One workgroup of 1024 threads (at most 1025 buckets).
+// Tile lists of both GEMMs, in an order that keeps shared data in one L2:
+// buckets in order (routed experts by id, then the shared expert); each
+// bucket's 128-row blocks in chunks of up to `chunk` blocks; inside a chunk
+// the column block outer and the row block inner. So the row blocks of a
+// chunk (A, re-read by every column block) stay in cache while its column
+// blocks go by, and the row blocks sharing a weight tile (B) run together.
+// The GEMMs hand consecutive stretches of this list to each XCD.
+// One workgroup of 1024 threads (at most 1025 buckets).
+__device__ __forceinline__ int plan_chunk(int K) {
+  // row blocks whose activations take about 2.5 MB (L2 is 4 MB per XCD)
+  return min(max((5 << 19) / (kBM * K * 2), 1), 8);
+}
+
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
   __shared__ int s_tmp[32];
+  __shared__ int s_rb[1026];    // exclusive scan of row blocks per bucket
   const int nb = g.E + (g.has_shared ? 1 : 0);
   int cnt[2];
 #pragma unroll
@@ -100,16 +119,35 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
   int total0 = 0, total1 = 0;
   const int base0 = block_exclusive_scan(cnt[0], s_tmp, &total0);
   const int base1 = total0 + block_exclusive_scan(cnt[1], s_tmp, &total1);
+  s_rb[threadIdx.x] = base0;
+  if (threadIdx.x + 1024 < 1026) s_rb[threadIdx.x + 1024] = base1;
+  const int total_rb = min(total0 + total1, g.max_rb);
+  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int b = threadIdx.x + q * 1024;
-    const int base = q == 0 ? base0 : base1;
-    for (int m = 0; m < cnt[q] && base + m < g.max_tiles; ++m) {
-      g.tile_expert[base + m] = b;
-      g.tile_m0[base + m] = m * kBM;
+  for (int kind = 0; kind < 2; ++kind) {
+    const int ncol = kind == 0 ? g.I / (kWRows / 2) : g.H / kWRows;
+    const int chunk = plan_chunk(kind == 0 ? g.H : g.I);
+    const int total = total_rb * ncol;
+    for (int q = threadIdx.x; q < total; q += 1024) {
+      // bucket: the last b with s_rb[b] * ncol <= q (buckets without rows
+      // have equal bases; the search lands on the one that owns q)
+      int lo = 0, hi = nb;  // invariant: s_rb[lo] * ncol <= q < s_rb[hi] * ncol
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_rb[mid] * ncol <= q) lo = mid; else hi = mid;
+      }
+      const int nblk = s_rb[lo + 1] - s_rb[lo];
+      const int local = q - s_rb[lo] * ncol;
+      const int c = local / (chunk * ncol);
+      const int csz = min(chunk, nblk - c * chunk);
+      const int idx = local - c * chunk * ncol;
+      const int nt = idx / csz;
+      const int mt = c * chunk + (idx - nt * csz);
+      g.tile_b[kind][q] = lo;
+      g.tile_mn[kind][q] = (mt << 8) | nt;
     }
+    if (threadIdx.x == 0) g.tile_count[kind] = total;
   }
-  if (threadIdx.x == 0) *g.tile_total = min(total0 + total1, g.max_tiles);
 }
 
 // 8 E2M1 codes (one word) times `sc` -> 8 bf16 / fp16
@@ -126,6 +164,28 @@ __device__ __forceinline__ f16x8_t fp4x8_f16(uint32_t w, float sc) {
   const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
   const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
   return f16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// MFMA operand type, conversion and product of each GEMM: gate/up in bf16,
+// down in fp16 (h is carried in fp16).
+template <bool GU>
+using Op = typename std::conditional<GU, bf16x8_t, f16x8_t>::type;
+template <bool GU>
+__device__ __forceinline__ Op<GU> cvt8(uint32_t w, float sc) {
+  if constexpr (GU)
+    return fp4x8_bf16(w, sc);
+  else
+    return fp4x8_f16(w, sc);
+}
+template <bool GU>
+__device__ __forceinline__ f32x4_t mma(uint4 a, Op<GU> b, f32x4_t c) {
+  if constexpr (GU)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t word_of(uint4 v, int s) {
+  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
 // Direct global -> LDS loads: lane l's 16 (4) bytes at base + voff land at
@@ -160,18 +220,25 @@ __device__ __forceinline__ int frag_row(int wn, int j, int c) {
 
 template <bool GU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __align__(16) char lds[kStages * kStageBytes];
+  __shared__ __align__(16) char lds[kStages * kStageBytes + kScaleBytes];  // 160 KB
   constexpr int kBN = GU ? kWRows / 2 : kWRows;  // output columns per tile
   const int N = GU ? g.I : g.H;
   const int K = GU ? g.H : g.I;
   const int ncol = N / kBN;
-  const int mt = blockIdx.x / ncol, nt = blockIdx.x - mt * ncol;
-  if (mt >= *g.tile_total) return;
+  // Workgroups are dispatched to the 8 XCDs round-robin by index: hand XCD
+  // x (blocks x, x + 8, ...) the consecutive tiles [x * per, (x + 1) * per)
+  // of the list, so the tiles that share data share an L2.
+  const int total = min(g.tile_count[GU ? 0 : 1], g.max_rb * ncol);
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return;
   const int nb = g.E + (g.has_shared ? 1 : 0);
-  const Bucket bk = bucket_of(g, min(max(g.tile_expert[mt], 0), nb - 1));
-  const int m0 = g.tile_m0[mt];
+  const Bucket bk = bucket_of(g, min(max(g.tile_b[GU ? 0 : 1][t], 0), nb - 1));
+  const int mn = g.tile_mn[GU ? 0 : 1][t];
+  const int m0 = (mn >> 8) * kBM;
+  const int n0 = min(mn & 255, ncol - 1) * kBN;
   if (m0 < 0 || m0 >= bk.count) return;
-  const int n0 = nt * kBN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     const int r = 128 * u + (tid >> 2);
     b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
   }
-  const uint32_t s_off = wrow(tid & 255) * srow;
+  const uint32_t s_lds = lds_base + kStages * kStageBytes;
 
   // Stage `st` <- K step `ks`.
   auto issue = [&](int st, int ks) {
@@ -228,17 +295,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     for (int u = 0; u < kBLoads; ++u)
       lds_load16(cbase, b_off[u] + k0 / 2,
                  base + kABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
-    if (wave < 4) lds_load4(sbase, s_off + k0 / 32, base + kABytes + kBBytes + 256u * wave);
+
   };
-  // Wait until at most one stage's loads are outstanding (or none).
-  auto wait_stage = [&](bool keep_one) {
-    if (keep_one) {
-      if (wave < 4)
-        asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The tile's scales: rows r of the tile (gate/up: two runs of 128 rows,
+  // down: one run of 256), srow bytes each, contiguous in the bank and in
+  // LDS ([r][K / 32]); 4-byte pieces, srow is a multiple of 4.
+  auto load_scales = [&]() {
+    const int pieces = kWRows * (int)srow / 4;
+    for (int p0 = 64 * wave; p0 < pieces; p0 += kThreads) {
+      const int p = min(p0 + lane, pieces - 1);
+      const uint32_t b = 4u * (uint32_t)p;
+      const uint32_t r = b / srow;
+      lds_load4(sbase, wrow((int)r) * srow + (b - r * srow), s_lds + 4u * (uint32_t)p0);
     }
   };
 
@@ -251,56 +319,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // rows of this wave beyond the bucket need no arithmetic
   const bool active = m0 + 64 * wm < bk.count;
 
-  auto compute = [&](int st) {
+  // One K step in four MFMA sub-steps, software pipelined: while the 16
+  // MFMAs of sub-step s run, the A fragments of s + 1 are read from LDS and
+  // its B fragments converted, into a second set of registers.
+  auto compute = [&](int st, int st_k) {
     const char* sb = lds + st * kStageBytes;
     const uint4* sa = reinterpret_cast<const uint4*>(sb);
     const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABytes);
-    const uint8_t* ss = reinterpret_cast<const uint8_t*>(sb + kABytes + kBBytes);
+    const uint8_t* ss = reinterpret_cast<const uint8_t*>(lds + kStages * kStageBytes) +
+                        (size_t)st_k * 4;  // this K step's 4 scale bytes of each row
     uint4 bc[4];
     float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = frag_row<GU>(wn, j, c);
       bc[j] = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
-      sc[j] = e8m0_to_f32(ss[r * 4 + grp]);
+      sc[j] = e8m0_to_f32(ss[r * srow + grp]);
     }
+    // A row 64 wm + 16 i + c, K values 32 grp + 8 s: piece 4 grp + s
+    auto a_frag = [&](int i, int s) {
+      return sa[(64 * wm + 16 * i + c) * 16 + ((4 * grp + s) ^ c)];
+    };
+    Op<GU> bcur[4], bnext[4];
+    uint4 acur[4], anext[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acur[i] = a_frag(i, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bcur[j] = cvt8<GU>(word_of(bc[j], 0), sc[j]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      // A row 64 wm + 16 i + c, K values 32 grp + 8 s: piece 4 grp + s
-      uint4 af[4];
+      if (s < 3) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = sa[(64 * wm + 16 * i + c) * 16 + ((4 * grp + s) ^ c)];
+        for (int i = 0; i < 4; ++i) anext[i] = a_frag(i, s + 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = s == 0 ? bc[j].x : s == 1 ? bc[j].y : s == 2 ? bc[j].z : bc[j].w;
-        if constexpr (GU) {
-          const bf16x8_t bf = fp4x8_bf16(w, sc[j]);
+        for (int j = 0; j < 4; ++j) bnext[j] = cvt8<GU>(word_of(bc[j], s + 1), sc[j]);
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, af[i]), bf, acc[i][j], 0, 0, 0);
-        } else {
-          const f16x8_t bf = fp4x8_f16(w, sc[j]);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(f16x8_t, af[i]), bf, acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) acc[i][j] = mma<GU>(acur[i], bcur[j], acc[i][j]);
+      if (s < 3) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acur[q] = anext[q];
+          bcur[q] = bnext[q];
         }
       }
     }
   };
 
-  // Pipeline: before step ks the stages of ks and ks + 1 are in flight.
-  // Wait for ks's, then one barrier makes it visible to every wave and
-  // guarantees that stage (ks + 2) % 3, read at step ks - 1, is free.
+  // Pipeline: stage ks + 1 loads while step ks computes. Each step starts
+  // with a full wait for this wave's loads and one barrier, which makes
+  // stage ks visible to every wave and frees the other buffer (read at
+  // step ks - 1) for ks + 1.
   const int steps = K / kBK;
+  load_scales();
   issue(0, 0);
-  if (steps > 1) issue(1, 1);
   for (int ks = 0; ks < steps; ++ks) {
-    wait_stage(ks + 1 < steps);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (ks + 2 < steps) issue((ks + 2) % kStages, ks + 2);
-    if (active) compute(ks % kStages);
+    if (ks + 1 < steps) issue((ks + 1) % kStages, ks + 1);
+    if (active) compute(ks % kStages, ks);
   }
 
   // D layout: lane (c, grp), element v -> row 4 grp + v, column c
@@ -328,19 +407,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 struct GemmLayout {
   _Float16* h;
   int32_t* tiles;
-  int max_tiles;
+  int max_rb, ncol_gu, ncol_dn;
   size_t bytes;
 };
 
-GemmLayout gemm_layout(void* ws, int T, int I, int E, int R, bool shared) {
+GemmLayout gemm_layout(void* ws, int T, int H, int I, int E, int R, bool shared) {
   GemmLayout L;
   const size_t rows = (size_t)R + (shared ? T : 0);
-  L.max_tiles = (R + kBM - 1) / kBM + E + (shared ? (T + kBM - 1) / kBM + 1 : 0);
+  L.max_rb = (R + kBM - 1) / kBM + E + (shared ? (T + kBM - 1) / kBM + 1 : 0);
+  L.ncol_gu = I / (kWRows / 2);
+  L.ncol_dn = H / kWRows;
   const size_t hb = (rows * I * sizeof(_Float16) + 255) & ~(size_t)255;
+  const size_t nt = 2 * (size_t)L.max_rb * (L.ncol_gu + L.ncol_dn) + 2;
   char* w = static_cast<char*>(ws);
   L.h = reinterpret_cast<_Float16*>(w);
   L.tiles = reinterpret_cast<int32_t*>(w ? w + hb : nullptr);
-  L.bytes = hb + (((2 * (size_t)L.max_tiles + 1) * sizeof(int32_t) + 255) & ~(size_t)255);
+  L.bytes = hb + ((nt * sizeof(int32_t) + 255) & ~(size_t)255);
   return L;
 }
 
@@ -354,13 +436,12 @@ bool gemm_supported(int T, int H, int I, int R, bool shared) {
 }
 
 size_t gemm_ws_bytes(int T, int H, int I, int E, int R, bool shared) {
-  (void)H;
-  return gemm_layout(nullptr, T, I, E, R, shared).bytes;
+  return gemm_layout(nullptr, T, H, I, E, R, shared).bytes;
 }
 
 void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   const int E = p.offsets ? p.routed.E : 1;
-  const GemmLayout L = gemm_layout(ws, p.T, p.I, E, p.R, p.has_shared);
+  const GemmLayout L = gemm_layout(ws, p.T, p.H, p.I, E, p.R, p.has_shared);
   GemmArgs g{};
   g.x = p.x;
   g.T = p.T;
@@ -373,18 +454,21 @@ void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   g.has_shared = p.has_shared;
   g.offsets = p.offsets;
   g.row_token = p.row_token;
-  g.tile_expert = L.tiles;
-  g.tile_m0 = L.tiles + L.max_tiles;
-  g.tile_total = L.tiles + 2 * L.max_tiles;
-  g.max_tiles = L.max_tiles;
+  const size_t n_gu = (size_t)L.max_rb * L.ncol_gu, n_dn = (size_t)L.max_rb * L.ncol_dn;
+  g.tile_b[0] = L.tiles;
+  g.tile_mn[0] = L.tiles + n_gu;
+  g.tile_b[1] = L.tiles + 2 * n_gu;
+  g.tile_mn[1] = L.tiles + 2 * n_gu + n_dn;
+  g.tile_count = L.tiles + 2 * (n_gu + n_dn);
+  g.max_rb = L.max_rb;
   g.h = L.h;
   g.y = p.y;
   g.y_sh = p.y_sh;
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
-  launch("gemm_gateup_kernel", gemm_kernel<true>, dim3(L.max_tiles * (p.I / (kWRows / 2))),
-                     dim3(kThreads), 0, s, g);
-  launch("gemm_down_kernel", gemm_kernel<false>, dim3(L.max_tiles * (p.H / kWRows)), dim3(kThreads), 0,
-                     s, g);
+  // grids: every tile the lists can hold, rounded up to the 8 XCDs
+  const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
+  launch("gemm_gateup_kernel", gemm_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
+  launch("gemm_down_kernel", gemm_kernel<false>, dim3(grid_dn), dim3(kThreads), 0, s, g);
 }
 
 }  // namespace moe
