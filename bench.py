@@ -241,7 +241,7 @@ def kernel_work(name, w, U, shared=True):
         if shared:
             b += dn_expert + T * I * 4 + T * H * 4
         return "hbm", b
-    if name in ("down_stream_kernel", "down_kernel"):
+    if name == "down_kernel":
         # routed down of the U experts, then the combine
         return "hbm", U * dn_expert + R * I * 4 + R * H * 4 + (T * H * 4 if shared else 0) \
             + T * H * 4 + T * w.k * 8

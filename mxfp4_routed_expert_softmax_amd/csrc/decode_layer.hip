@@ -81,6 +81,23 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
+// A whole 32-bit word (`off` a multiple of 4). In a loop whose loads run
+// ahead of their use, byte loads make the compiler widen the byte right
+// after the load, which waits for it; a word needs no widening, and the byte
+// is taken out where it is used.
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// A wave-uniform value the compiler can see is one: buffer resources built
+// from a value it cannot prove uniform become a loop around every load.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 
 // Coherent accessors for data handed between workgroups of one launch.
 template <class V>
@@ -584,6 +601,7 @@ __device__ void combine_column(const DecodeArgs& a, int c) {
 // ---------------------------------------------------------------------------
 constexpr int kStreamBlocks = 768;  // persistent workgroups per streaming kernel
 
+// sg / su: the words holding the lane's scale bytes (byte lane % 4 of each).
 struct GuRegs {
   uint4 g[kGuU], u[kGuU];
   uint32_t sg[kGuU], su[kGuU];
@@ -594,25 +612,28 @@ struct GuRegs {
 __device__ __forceinline__ void gu_issue(const DecodeArgs& a, const int* tab, int it, GuRegs& r,
                                          bool live = true) {
   const int s = it / a.gu_items, rb = it - s * a.gu_items;
-  const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
+  const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + s], 0), a.routed.E - 1));
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & (kGuLanes - 1);
   const int nr = min(rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes, a.I - 1);
   const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> 5;
-  const uint8_t* gbase = a.routed.gu_codes + (size_t)e * 2 * a.I * crow;
-  const uint8_t* sbase = a.routed.gu_scales + (size_t)e * 2 * a.I * srow;
+  const uint8_t* gbase = uniform_ptr(a.routed.gu_codes + (size_t)e * 2 * a.I * crow);
+  const uint8_t* sbase = uniform_ptr(a.routed.gu_scales + (size_t)e * 2 * a.I * srow);
   const uint32_t cb = live ? a.I * crow : 0u, sb = live ? a.I * srow : 0u;
   const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, cb);
   const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, cb);
   const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, sb);
   const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, sb);
-  const int co = nr * crow + j * 16, so = nr * srow + j;
+  // scale byte j + 32 u of a row is byte j % 4 of its word j / 4 + 8 u (rows
+  // start on a word: H % 128 == 0)
+  const int co = nr * crow + j * 16, so = nr * srow + (j & ~3);
 #pragma unroll
   for (int u = 0; u < kGuU; ++u) {
     r.g[u] = bload16(rg, co + u * kGuLanes * 16);
     r.u[u] = bload16(ru, co + u * kGuLanes * 16);
-    r.sg[u] = bload8(rgs, so + u * kGuLanes);
-    r.su[u] = bload8(rus, so + u * kGuLanes);
+    r.sg[u] = bload32(rgs, so + u * kGuLanes);
+    r.su[u] = bload32(rus, so + u * kGuLanes);
   }
 }
 
@@ -624,6 +645,7 @@ __device__ __forceinline__ void gu_compute(const DecodeArgs& a, const int* tab, 
   const int j = lane & (kGuLanes - 1);
   const int n = rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes;
   const int kc = a.H >> 5;
+  const uint32_t sh = 8u * (j & 3);
   float ag = 0.0f, au = 0.0f;
 #pragma unroll
   for (int u = 0; u < kGuU; ++u) {
@@ -640,8 +662,8 @@ __device__ __forceinline__ void gu_compute(const DecodeArgs& a, const int* tab, 
       pu = dot8_fp4_bf16(r.u[u].y, x1, pu);
       pu = dot8_fp4_bf16(r.u[u].z, x2, pu);
       pu = dot8_fp4_bf16(r.u[u].w, x3, pu);
-      ag = fmaf(pg, e8m0_to_f32(r.sg[u]), ag);
-      au = fmaf(pu, e8m0_to_f32(r.su[u]), au);
+      ag = fmaf(pg, e8m0_to_f32(__builtin_amdgcn_ubfe(r.sg[u], sh, 8)), ag);
+      au = fmaf(pu, e8m0_to_f32(__builtin_amdgcn_ubfe(r.su[u], sh, 8)), au);
     }
   }
   const float g = group_sum<kGuLanes>(ag), u = group_sum<kGuLanes>(au);
@@ -833,6 +855,7 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
   }
 }
 
+// sc: the words holding the lane's scale bytes (byte (lane % 8) % 4 of each).
 struct DnRegs {
   uint4 w[kDnU];
   uint32_t sc[kDnU];
@@ -855,7 +878,7 @@ __device__ __forceinline__ DnItem dn_item(const DecodeArgs& a, const int* tab, i
     return DnItem{a.shared.d_codes, a.shared.d_scales, min(a.R, a.rows - 1), c};
   }
   const int s = it / a.dn_items, c = it - s * a.dn_items;
-  const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
+  const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + s], 0), a.routed.E - 1));
   const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
   return DnItem{a.routed.d_codes + (size_t)e * a.H * crow, a.routed.d_scales + (size_t)e * a.H * srow,
                 row, c};
@@ -869,13 +892,17 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, in
   const int j = lane & 7;
   const int nr = min(c * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
   const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
-  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(d.codes, live ? a.H * crow : 0u);
-  const __amdgpu_buffer_rsrc_t rds = matrix_rsrc(d.scales, live ? a.H * srow : 0u);
-  const int co = nr * crow + j * 16, so = nr * srow + j;
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(uniform_ptr(d.codes), live ? a.H * crow : 0u);
+  const __amdgpu_buffer_rsrc_t rds =
+      matrix_rsrc(uniform_ptr(d.scales), live ? a.H * srow : 0u);
+  // scale byte j + 8 u of a row is byte j % 4 of its word j / 4 + 2 u (rows
+  // start on a word: I % 128 == 0)
+  const int co = nr * crow + j * 16, so = nr * srow + 4 * (j >> 2);
 #pragma unroll
   for (int u = 0; u < kDnU; ++u) {
     r.w[u] = bload16(rd, co + u * 8 * 16);
-    r.sc[u] = bload8(rds, so + u * 8);
+    r.sc[u] = bload32(rds, so + u * 8);
   }
   const f32x4_t* hrow = reinterpret_cast<const f32x4_t*>(a.h + (size_t)row * a.I);
   const int nv = a.I >> 2;
@@ -899,6 +926,7 @@ __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, 
   const int j = lane & 7;
   const int n = c * kDnRows + wave * 8 + (lane >> 3);
   const int kc = a.I >> 5;
+  const uint32_t sh = 8u * (j & 3);
   float acc = 0.0f;
 #pragma unroll
   for (int u = 0; u < kDnU; ++u) {
@@ -910,7 +938,7 @@ __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, 
       pd = dot8_fp4_f32(r.w[u].y, hv[2 * P], hv[3 * P], pd);
       pd = dot8_fp4_f32(r.w[u].z, hv[4 * P], hv[5 * P], pd);
       pd = dot8_fp4_f32(r.w[u].w, hv[6 * P], hv[7 * P], pd);
-      acc = fmaf(pd, e8m0_to_f32(r.sc[u]), acc);
+      acc = fmaf(pd, e8m0_to_f32(__builtin_amdgcn_ubfe(r.sc[u], sh, 8)), acc);
     }
   }
   const float v = group_sum<8>(acc);
@@ -1170,7 +1198,8 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   // One token (or one row per expert): every slot holds a single row, and a
   // kernel built for one staged row needs far fewer registers.
   const bool one = d.T == 1 || (ffn && d.R <= 1);
-  const bool stream = d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
+  const bool stream = d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU && d.H % 128 == 0 &&
+                      d.I % 128 == 0 &&
                       (d.I >> 5) <= 8 * kDnU && d.I <= 3 * 4 * kThreads &&
                       d.H * 2 + 4 * (1 + 3 * L.max_slots) <= kLdsBytes &&
                       1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave &&

@@ -322,6 +322,76 @@ def test_layer_decode_token_pool_real_shape():
     shared = S.gen_bank(w, 0, shared=True)
     for x in xs:
         _layer_parity(w, x, wr, None, routed, shared)
+        assert _launches() == ONE_TOKEN_PATH
+
+
+# One token in one launch, at shapes where the worker count, the shared
+# gate/up items per worker (0 to 3) and the byte-balanced split of the routed
+# rows all differ from the real shape's.
+ONE_TOKEN = [
+    S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_small", 92, T=1, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_narrow", 93, T=1, H=256, E=16, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_wide_k", 94, T=1, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+]
+
+
+def _launches():
+    return [M.moe_launch_name(i) for i in range(M.moe_last_call_launches())]
+
+
+# kernels of the one-token path
+ONE_TOKEN_PATH = ["gateup_fused_kernel", "down_stream_kernel"]
+
+
+@pytest.mark.parametrize("variant", ["shared", "no_shared_with_bias"])
+@pytest.mark.parametrize("w", ONE_TOKEN, ids=lambda w: w.name)
+def test_layer_one_token_path(w, variant):
+    d = S.gen_inputs(w, 0)
+    bias, shared = None, d["shared"]
+    if variant == "no_shared_with_bias":
+        bias, shared = np.linspace(-0.5, 0.5, w.E).astype(np.float32), None
+    err = _layer_parity(w, d["x"], d["w_router"], bias, d["routed"], shared)
+    assert _launches() == ONE_TOKEN_PATH
+    assert err < HP.FP32_TOL
+
+
+def test_layer_one_token_shapes_share_a_garbage_workspace():
+    # one workspace, filled with random bytes, then used by every one-token
+    # shape in turn, twice: tags, counters and tables left at other offsets
+    # by the previous shape must not matter
+    big = ONE_TOKEN[-1]
+    ws = M.workspace(1, big.H, big.I, big.E, big.k, HP.dev())
+    g = torch.Generator(device=HP.dev()).manual_seed(2)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=HP.dev(), generator=g))
+    data = {w.name: S.gen_inputs(w, 0) for w in ONE_TOKEN}
+    dev = {w.name: (HP.bank_to_dev(data[w.name]["routed"]), HP.bank_to_dev(data[w.name]["shared"]))
+           for w in ONE_TOKEN}
+    for _ in range(2):
+        for w in ONE_TOKEN:
+            d = data[w.name]
+            rd, sd = dev[w.name]
+            out = torch.empty((1, w.H), dtype=torch.float32, device=HP.dev())
+            ids = torch.empty((1, w.k), dtype=torch.int32, device=HP.dev())
+            wt = torch.empty((1, w.k), dtype=torch.float32, device=HP.dev())
+            M.moe_layer_forward(HP.to_dev(d["x"]), HP.to_dev(d["w_router"]), None, rd, sd, w.k,
+                                out, ids, wt, ws)
+            assert _launches() == ONE_TOKEN_PATH
+            ref = O.layer(d["x"], d["w_router"], None, d["routed"], d["shared"], w.k)
+            alt = HP.check_routing(ref, _np(ids), _np(wt), w.k)
+            err = HP.rel_l2(_np(out), HP.reference_rows(ref, d["routed"], d["shared"],
+                                                          ref["tokens"], alt))
+            assert err < HP.FP32_TOL, (w.name, err)
+
+
+def test_layer_one_token_is_bitwise_deterministic():
+    w = ONE_TOKEN[0]
+    d = S.gen_inputs(w, 0)
+    rd, sd = HP.bank_to_dev(d["routed"]), HP.bank_to_dev(d["shared"])
+    a = run_layer(d["x"], d["w_router"], None, rd, sd, w.k)
+    b = run_layer(d["x"], d["w_router"], None, rd, sd, w.k)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
 def test_layer_is_bitwise_deterministic():
