@@ -400,7 +400,8 @@ __global__ __launch_bounds__(kThreads) void ffn_table_kernel(DecodeArgs a) {
 // activations are staged. h is written with plain stores (read by a later
 // launch).
 // ---------------------------------------------------------------------------
-template <int MT>
+// kCoherent: h is stored write-through, for readers in this same launch.
+template <int MT, bool kCoherent = false>
 __device__ void gateup_item(const DecodeArgs& a, const Slot& sd, int rb, uint4* s_x,
                             const int32_t* rtok) {
   const BankView bk = sd.shared ? a.shared : a.routed;
@@ -486,7 +487,13 @@ __device__ void gateup_item(const DecodeArgs& a, const Slot& sd, int rb, uint4* 
     for (int t = 0; t < MT; ++t) {
       const float g = group_sum<kGuLanes>(ag[t]);
       const float u = group_sum<kGuLanes>(au[t]);
-      if (row_ok && j == 0 && t < nt) a.h[(size_t)(sd.row0 + t0 + t) * I + n] = silu_mul(g, u);
+      if (row_ok && j == 0 && t < nt) {
+        float* p = a.h + (size_t)(sd.row0 + t0 + t) * I + n;
+        if (kCoherent)
+          cst(p, silu_mul(g, u));
+        else
+          *p = silu_mul(g, u);
+      }
     }
   }
 }
@@ -723,6 +730,57 @@ __device__ void poll_tagged(const DecodeArgs& a, const uint64_t* src, int n, uin
   }
 }
 
+// Key of (logit, expert) that orders like (logit descending, id ascending)
+// and whose bits, read as an fp64, are a positive normal number (or +0 for
+// an empty slot), so fp64 max picks the larger key: the order-preserving
+// 32-bit image of the logit in bits 62..31, 2^31 - 1 - e below. NaN logits
+// rank as -inf, so no key is an fp64 NaN, infinity or subnormal.
+__device__ __forceinline__ uint64_t topk_key_f64(float v, int e) {
+  v = (v != v) ? -INFINITY : v;
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 31) | (uint32_t)(0x7fffffffu - (uint32_t)e);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_max_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL,
+                                                            0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32),
+                                                            (int)(uint32_t)(u >> 32), CTRL, 0xf,
+                                                            0xf, false);
+  return fmax(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
+}
+
+// Wave-wide maximum of such keys, in every lane, without leaving the vector
+// unit: DPP within each row of 16 lanes (xor 1, xor 2, half-row mirror, row
+// mirror), then lane swaps across rows (16, then 32 apart).
+__device__ __forceinline__ uint64_t wave_max_key_f64(uint64_t k) {
+  double v = __longlong_as_double((long long)k);
+  v = dpp_max_f64<0xB1>(v);
+  v = dpp_max_f64<0x4E>(v);
+  v = dpp_max_f64<0x141>(v);
+  v = dpp_max_f64<0x140>(v);
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false,
+                                                     false);
+    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
+             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
+  }
+  u = (uint64_t)__double_as_longlong(v);
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false,
+                                                     false);
+    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
+             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
+  }
+  return (uint64_t)__double_as_longlong(v);
+}
+
 // The one-token routing workgroup (wave 0): waits for the tagged logits,
 // takes the top-k (descending logit, ties to the lower id) with weights
 // renormalised over the k, writes the layer outputs and the table the down
@@ -733,36 +791,44 @@ __device__ void route_token_tagged(const DecodeArgs& a) {
   const int lane = lane_id(), k = a.k, ms = a.max_slots;
   uint32_t raw[NK];
   poll_tagged<NK>(a, a.tagged, a.E, raw);
-  uint64_t key[NK];
+  // k rounds of: each lane's best remaining key, the wave's best of those
+  // (fp64 max on the keys' bits), and that key taken out
+  double key[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     const int e = lane + kWave * i;
-    key[i] = e < a.E ? topk_key(__uint_as_float(raw[i]), e) : 0;
+    key[i] = __longlong_as_double(e < a.E ? (long long)topk_key_f64(__uint_as_float(raw[i]), e) : 0);
   }
   float my_val = 0.0f, top = 0.0f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    double best = key[0];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) best = key[i] > best ? key[i] : best;
-    const uint64_t win = wave_max_key(best);
-    const int id = (int)(0xffffffffu - (uint32_t)win);
-    uint32_t bits = (uint32_t)(win >> 32);
+    for (int i = 1; i < NK; ++i) best = fmax(best, key[i]);
+    const uint64_t win = wave_max_key_f64((uint64_t)__double_as_longlong(best));
+    const uint32_t id = 0x7fffffffu - (uint32_t)(win & 0x7fffffffu);
+    uint32_t bits = (uint32_t)(win >> 31);
     bits = (bits & 0x80000000u) ? (bits & 0x7fffffffu) : ~bits;
     const float val = __uint_as_float(bits);
 #pragma unroll
     for (int i = 0; i < NK; ++i)
-      if (key[i] == win) key[i] = 0;
+      if ((uint64_t)__double_as_longlong(key[i]) == win) key[i] = 0.0;
     if (lane == j) {
       my_val = val;
-      my_id = id;
+      my_id = (int)min(id, (uint32_t)(a.E - 1));
     }
     if (j == 0) top = val;
   }
+  // weights and slots from the k chosen lanes, read lane by lane (cheaper
+  // than shuffles through LDS); the sum runs over j = 0..k-1 in order
   const float z = lane < k ? expf(my_val - top) : 0.0f;
-  const float wj = z / wave_sum(z);
+  float zsum = 0.0f;
   int slot = 0;
-  for (int q = 0; q < k; ++q) slot += __shfl(my_id, q, kWave) < my_id;
+  for (int q = 0; q < k; ++q) {
+    zsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), q));
+    slot += __builtin_amdgcn_readlane(my_id, q) < my_id;
+  }
+  const float wj = z / zsum;
   if (lane < k) {
     a.tab[1 + slot] = my_id;
     a.tab[1 + ms + slot] = slot;
@@ -802,59 +868,6 @@ __device__ void load_routing_tagged(const DecodeArgs& a, int r, int* s_tab) {
   __syncthreads();
 }
 
-// Decode gate/up, one launch: [router rows | the routing workgroup |
-// shared expert gate/up items | G routed workgroups]. The routed workgroups
-// stage the token, poll a replica of the routing table and then stream the
-// items b, b + G, b + 2G, ... of the selected experts (items slot-major, 8
-// rows each) with two register buffers, so the weights of the next item are
-// in flight while the current one is computed.
-__global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
-                                                                int G) {
-  extern __shared__ __align__(16) char lds[];
-  const int b0 = blockIdx.x;
-  if (b0 < a.nb_router) {
-    router_rows_one(a, b0, reinterpret_cast<uint4*>(lds));
-    return;
-  }
-  if (b0 == a.nb_router) {
-    if (threadIdx.x < kWave) {
-      if (a.E <= 6 * kWave)
-        route_token_tagged<6>(a);
-      else
-        route_token_tagged<16>(a);
-    }
-    return;
-  }
-  if (b0 <= a.nb_router + n_shared) {
-    gateup_item<1>(a, shared_slot(a), b0 - a.nb_router - 1, reinterpret_cast<uint4*>(lds),
-                   nullptr);
-    return;
-  }
-  const int b = b0 - a.nb_router - 1 - n_shared;
-  uint4* s_x = reinterpret_cast<uint4*>(lds);
-  int* tab = reinterpret_cast<int*>(lds + a.H * 2);
-  stage_rows<uint4>(
-      a.H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
-      [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
-  load_routing_tagged(a, b % kReplicas, tab);
-  const int n = tab[0] * a.gu_items;
-  if (b >= n) return;
-  // Fixed trip over pairs of items with no early exit (an exit between the
-  // halves would let the compiler merge them and move the buffers to
-  // scratch). Issues past this workgroup's last item are padding: their
-  // weight loads read nothing (empty resources) and are not used.
-  const int mine = (n - b + G - 1) / G;
-  GuRegs A, B;
-  gu_issue(a, tab, b, A);
-  for (int kk = 0; kk < mine; kk += 2) {
-    const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
-    gu_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
-    gu_compute(a, tab, i0, A, s_x);
-    gu_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
-    if (i1 < n) gu_compute(a, tab, i1, B, s_x);
-  }
-}
-
 // sc: the words holding the lane's scale bytes (byte (lane % 8) % 4 of each).
 struct DnRegs {
   uint4 w[kDnU];
@@ -884,8 +897,30 @@ __device__ __forceinline__ DnItem dn_item(const DecodeArgs& a, const int* tab, i
                 row, c};
 }
 
+// The item's h row (I <= 3072: three float4 a thread). kCoherent: written
+// by other workgroups of this launch, so read with coherent loads.
+template <bool kCoherent>
+__device__ __forceinline__ void dn_issue_h(const DecodeArgs& a, int row, DnRegs& r) {
+  const int nv = a.I >> 2;
+  if (kCoherent) {
+    const uint64_t* hrow = reinterpret_cast<const uint64_t*>(a.h + (size_t)row * a.I);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = min((int)threadIdx.x + i * kThreads, nv - 1);
+      const uint64_t lo = cld(hrow + 2 * f), hi = cld(hrow + 2 * f + 1);
+      r.h[i] = f32x4_t{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                       __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+    }
+  } else {
+    const f32x4_t* hrow = reinterpret_cast<const f32x4_t*>(a.h + (size_t)row * a.I);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) r.h[i] = hrow[min((int)threadIdx.x + i * kThreads, nv - 1)];
+  }
+}
+
+// The item's weights and (with_h) its h row; `live` false reads no weights.
 __device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, int n_routed, int it,
-                                         DnRegs& r, bool live = true) {
+                                         DnRegs& r, bool live = true, bool with_h = true) {
   const DnItem d = dn_item(a, tab, n_routed, it);
   const int c = d.c, row = d.row;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -904,10 +939,7 @@ __device__ __forceinline__ void dn_issue(const DecodeArgs& a, const int* tab, in
     r.w[u] = bload16(rd, co + u * 8 * 16);
     r.sc[u] = bload32(rds, so + u * 8);
   }
-  const f32x4_t* hrow = reinterpret_cast<const f32x4_t*>(a.h + (size_t)row * a.I);
-  const int nv = a.I >> 2;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) r.h[i] = hrow[min((int)threadIdx.x + i * kThreads, nv - 1)];
+  if (with_h) dn_issue_h<false>(a, row, r);
 }
 
 __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, int nr, int it,
@@ -968,6 +1000,90 @@ __device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
   a.out[n] = v;
 }
 
+// Decode gate/up, one launch: [router rows | the routing workgroup |
+// shared expert gate/up items | G routed workgroups]. The routed workgroups
+// stage the token, poll a replica of the routing table and then stream the
+// items b, b + G, b + 2G, ... of the selected experts (items slot-major, 8
+// rows each) with two register buffers, so the weights of the next item are
+// in flight while the current one is computed.
+// Completion flags of the shared expert's gate/up items in the one-token
+// launch: one tagged word per item, after the routing copies.
+__device__ __forceinline__ uint64_t* shared_flags(const DecodeArgs& a) {
+  return a.tagged + a.E + (size_t)kReplicas * kReplicaWords;
+}
+
+// The shared expert's down item c (32 output rows) inside the one-token
+// gate/up launch. These workgroups come last in the grid, so they start as
+// the routed gate/up workers leave and use the bandwidth of that tail: by
+// then the shared gate/up items are long done (their flags are checked
+// all the same) and the shared h row is read coherently with the weights.
+// The next launch is left with only the routed experts' down rows.
+__device__ void shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
+  if (threadIdx.x < kWave) {
+    uint32_t v[6];
+    poll_tagged<6>(a, shared_flags(a), n_sh, v);
+  }
+  __syncthreads();
+  DnRegs A;
+  dn_issue(a, nullptr, 0, c, A, true, false);
+  dn_issue_h<true>(a, min(a.R, a.rows - 1), A);
+  dn_compute(a, nullptr, 0, c, A, reinterpret_cast<f32x4_t*>(lds));
+}
+
+__global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
+                                                                int n_sd, int G) {
+  extern __shared__ __align__(16) char lds[];
+  const int b0 = blockIdx.x;
+  if (b0 < a.nb_router) {
+    router_rows_one(a, b0, reinterpret_cast<uint4*>(lds));
+    return;
+  }
+  if (b0 == a.nb_router) {
+    if (threadIdx.x < kWave) {
+      if (a.E <= 6 * kWave)
+        route_token_tagged<6>(a);
+      else
+        route_token_tagged<16>(a);
+    }
+    return;
+  }
+  if (b0 <= a.nb_router + n_shared) {
+    // a shared gate/up item, then its flag once its h stores have landed
+    const int item = b0 - a.nb_router - 1;
+    gateup_item<1, true>(a, shared_slot(a), item, reinterpret_cast<uint4*>(lds), nullptr);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) cst(shared_flags(a) + item, ((uint64_t)a.tag << 32) | 1u);
+    return;
+  }
+  if (b0 >= a.nb_router + 1 + n_shared + G) {
+    shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
+    return;
+  }
+  const int b = b0 - a.nb_router - 1 - n_shared;
+  uint4* s_x = reinterpret_cast<uint4*>(lds);
+  int* tab = reinterpret_cast<int*>(lds + a.H * 2);
+  stage_rows<uint4>(
+      a.H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+      [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
+  load_routing_tagged(a, b % kReplicas, tab);
+  const int n = tab[0] * a.gu_items;
+  // Fixed trip over pairs of items with no early exit (an exit between the
+  // halves would let the compiler merge them and move the buffers to
+  // scratch). Issues past this workgroup's last item are padding: their
+  // weight loads read nothing (empty resources) and are not used.
+  const int mine = b < n ? (n - b + G - 1) / G : 0;
+  GuRegs A, B;
+  gu_issue(a, tab, b < n ? b : 0, A, b < n);
+  for (int kk = 0; kk < mine; kk += 2) {
+    const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
+    gu_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
+    gu_compute(a, tab, i0, A, s_x);
+    gu_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
+    if (i1 < n) gu_compute(a, tab, i1, B, s_x);
+  }
+}
+
 // One token, down projection: routed (slot, 32-row group) items, then the
 // shared expert's, streamed by persistent workgroups with two register
 // buffers. After its last item a workgroup drains its y stores and bumps
@@ -988,8 +1104,8 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
   __syncthreads();
   const int ns = min(max(tab[0], 0), a.max_slots);
   const int nr = ns * a.dn_items;
-  const int n = nr + (a.has_shared ? a.dn_items : 0);
-  const int parts = ns + (a.has_shared ? 1 : 0);  // contributions per column
+  const int n = nr;       // the shared expert's rows were done in the gate/up launch
+  const int parts = ns;   // routed contributions per column
   const int b = blockIdx.x;
   if (b >= n) return;
   const int mine = (n - b + G - 1) / G;  // <= 32 (the grid is at least n / 32)
@@ -1114,7 +1230,9 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   L.off_inv = o;
   o += al(sizeof(int32_t) * (size_t)R);
   L.off_tagged = o;
-  o += al(sizeof(uint64_t) * (ffn || T != 1 ? 0 : (size_t)E + kReplicas * kReplicaWords));
+  // [E] tagged logits, kReplicas routing copies, the shared items' flags
+  o += al(sizeof(uint64_t) *
+          (ffn || T != 1 ? 0 : (size_t)E + kReplicas * kReplicaWords + L.gu_items));
   L.off_logits = o;
   o += al(sizeof(float) * (size_t)T * E);
   L.off_w = o;
@@ -1207,10 +1325,12 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
                       (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
   if (stream) {
     const int n_sh = shared ? L.gu_items : 0;
+    const int n_sd = shared ? L.dn_items : 0;
     const int gg = routed_gu < kStreamBlocks ? routed_gu : kStreamBlocks;
-    launch("gateup_fused_kernel", gateup_fused_kernel, dim3(L.nb_router + 1 + n_sh + gg),
-           dim3(kThreads), kLdsBytes, s, a, n_sh, gg);
-    const int nd = L.max_slots * L.dn_items + shared_dn;
+    launch("gateup_fused_kernel", gateup_fused_kernel,
+           dim3(L.nb_router + 1 + n_sh + gg + n_sd), dim3(kThreads), kLdsBytes, s, a, n_sh, n_sd,
+           gg);
+    const int nd = L.max_slots * L.dn_items;
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
     launch("down_stream_kernel", down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a,
            gd);
