@@ -228,13 +228,18 @@ def kernel_work(name, w, U, shared=True):
     gu_expert = 2 * I * H * 17 // 32       # gate + up of one expert
     dn_expert = I * H * 17 // 32           # down of one expert
     if name == "gateup_fused_kernel":
-        # one token: router rows, routing, shared + routed gate/up
-        return "hbm", w.E * H * 2 + T * H * 2 + T * w.E * 4 + (U + (1 if shared else 0)) \
-            * gu_expert + (R + (T if shared else 0)) * I * 4
+        # one token: router rows, routing, shared + routed gate/up, and the
+        # shared expert's down rows (its h read back, its y row written)
+        b = w.E * H * 2 + T * H * 2 + T * w.E * 4 + (U + (1 if shared else 0)) * gu_expert \
+            + (R + (T if shared else 0)) * I * 4
+        if shared:
+            b += dn_expert + T * I * 4 + T * H * 4
+        return "hbm", b
     if name == "down_stream_kernel":
-        # one token: routed + shared down rows, then the combine
-        return "hbm", (U + (1 if shared else 0)) * dn_expert \
-            + (R + (T if shared else 0)) * I * 4 + T * H * 4 + T * w.k * 8
+        # one token: the routed experts' down rows, then the combine (which
+        # reads the shared expert's y row)
+        return "hbm", U * dn_expert + R * I * 4 + R * H * 4 + (T * H * 4 if shared else 0) \
+            + T * H * 4 + T * w.k * 8
     if name in ("gateup_stream_kernel", "gateup_kernel"):
         # routed gate/up of the U experts (+ the shared expert's down rows)
         b = U * gu_expert + T * H * 2 + R * I * 4
