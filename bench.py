@@ -240,6 +240,20 @@ def kernel_work(name, w, U, shared=True):
         # reads the shared expert's y row)
         return "hbm", U * dn_expert + R * I * 4 + R * H * 4 + (T * H * 4 if shared else 0) \
             + T * H * 4 + T * w.k * 8
+    if name == "route_block_kernel":
+        # block of tokens: router rows and the routing
+        return "hbm", w.E * H * 2 + T * H * 2 + T * w.E * 4
+    if name == "gateup_block_kernel":
+        # gate/up of the U routed experts and the shared one, each read once
+        # for all the block's tokens routed to it; h rows written
+        return "hbm", (U + (1 if shared else 0)) * gu_expert + T * H * 2 \
+            + (R + (T if shared else 0)) * I * 4
+    if name == "down_block_kernel":
+        # down of the U routed experts and the shared one, h rows read, y rows
+        # written and read back by the combine, the output written
+        rows = R + (T if shared else 0)
+        return "hbm", (U + (1 if shared else 0)) * dn_expert + rows * I * 4 + 2 * rows * H * 4 \
+            + T * H * 4 + T * w.k * 8
     if name in ("gateup_stream_kernel", "gateup_kernel"):
         # routed gate/up of the U experts (+ the shared expert's down rows)
         b = U * gu_expert + T * H * 2 + R * I * 4

@@ -220,80 +220,138 @@ __device__ void router_rows(const DecodeArgs& a, int b) {
 // Routing: top-k per token (one wave per token) and atomic-free bucketing.
 // ---------------------------------------------------------------------------
 
-// Order-preserving key of (logit, expert): a larger key is a larger logit,
-// and among equal logits the lower expert id. NaN ranks as -inf.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+// Key of (logit, expert) that orders like (logit descending, id ascending)
+// and whose bits, read as an fp64, are a positive normal number (or +0 for
+// an empty slot), so fp64 max picks the larger key: the order-preserving
+// 32-bit image of the logit in bits 62..31, 2^31 - 1 - e below. NaN logits
+// rank as -inf, so no key is an fp64 NaN, infinity or subnormal.
+__device__ __forceinline__ uint64_t topk_key_f64(float v, int e) {
   v = (v != v) ? -INFINITY : v;
   uint32_t b = __float_as_uint(v);
   b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+  return ((uint64_t)b << 31) | (uint32_t)(0x7fffffffu - (uint32_t)e);
 }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, CTRL, 0xf, 0xf, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, CTRL, 0xf, 0xf, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > v ? o : v;
+__device__ __forceinline__ double dpp_max_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL,
+                                                            0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32),
+                                                            (int)(uint32_t)(u >> 32), CTRL, 0xf,
+                                                            0xf, false);
+  return fmax(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
 }
 
-// Wave-wide maximum of a 64-bit key, returned to every lane: DPP exchanges
-// within each row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror),
-// then the four row maxima through readlane.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = dpp_max_step<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max_step<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max_step<0x141>(v);  // row_half_mirror
-  v = dpp_max_step<0x140>(v);  // row_mirror
-  uint64_t m = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
-    const uint64_t x = ((uint64_t)hi << 32) | lo;
-    m = x > m ? x : m;
+// Wave-wide maximum of such keys, in every lane, without leaving the vector
+// unit: DPP within each row of 16 lanes (xor 1, xor 2, half-row mirror, row
+// mirror), then lane swaps across rows (16, then 32 apart).
+__device__ __forceinline__ uint64_t wave_max_key_f64(uint64_t k) {
+  double v = __longlong_as_double((long long)k);
+  v = dpp_max_f64<0xB1>(v);
+  v = dpp_max_f64<0x4E>(v);
+  v = dpp_max_f64<0x141>(v);
+  v = dpp_max_f64<0x140>(v);
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false,
+                                                     false);
+    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
+             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
   }
-  return m;
+  u = (uint64_t)__double_as_longlong(v);
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false,
+                                                     false);
+    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
+             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
+  }
+  return (uint64_t)__double_as_longlong(v);
 }
 
-// Wave-wide top-k of one logit row; lanes < k write ids / weights. Lane l
-// holds experts l, l+64, ... (E <= 64 NK); each round takes the best untaken
-// key of every lane and the wave maximum of those.
-template <int NK>
-__device__ void topk_row(const float* L, int E, int k, int* ids, float* w) {
+// Wave-wide top-k of one logit row; lanes < k write ids / weights, in
+// selection order (logit descending, ties to the lower id), with fp64-max
+// keys (one v_max_f64 per exchange); lane l holds experts l, l + 64, ...
+// (E <= 64 NK). Weights: softmax over the k chosen logits, summed over
+// j = 0..k-1 in order.
+template <int NK, int NR>
+__device__ void topk_rows_f64(const float* const* L, int E, int k, int* const* ids,
+                              float* const* w) {
+  // NR rows at once (independent exchanges interleave, so two rows cost
+  // little more than one)
   const int lane = lane_id();
-  uint64_t key[NK];
+  double key[NR][NK];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = e < E ? topk_key(cld(L + e), e) : 0;  // 0 is below every real key
-  }
-  float my_val = 0.0f, top = 0.0f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int i = 0; i < NK; ++i) best = key[i] > best ? key[i] : best;
-    const uint64_t win = wave_max_key(best);
-    const int id = (int)(0xffffffffu - (uint32_t)win);
-    uint32_t b = (uint32_t)(win >> 32);
-    b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
-    const float val = __uint_as_float(b);
-#pragma unroll
-    for (int i = 0; i < NK; ++i)
-      if (key[i] == win) key[i] = 0;
-    if (lane == j) {
-      my_val = val;
-      my_id = id;
+    for (int i = 0; i < NK; ++i) {
+      const int e = lane + kWave * i;
+      key[r][i] = __longlong_as_double(e < E ? (long long)topk_key_f64(cld(L[r] + e), e) : 0);
     }
-    if (j == 0) top = val;
+  float my_val[NR], top[NR];
+  int my_id[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    my_val[r] = top[r] = 0.0f;
+    my_id[r] = 0;
   }
-  const float z = (lane < k) ? expf(my_val - top) : 0.0f;
-  const float sum = wave_sum(z);
-  if (lane < k) {
-    ids[lane] = my_id;
-    w[lane] = z / sum;
+  for (int j = 0; j < k; ++j) {
+    uint64_t win[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      double best = key[r][0];
+#pragma unroll
+      for (int i = 1; i < NK; ++i) best = fmax(best, key[r][i]);
+      win[r] = wave_max_key_f64((uint64_t)__double_as_longlong(best));
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t id = 0x7fffffffu - (uint32_t)(win[r] & 0x7fffffffu);
+      uint32_t bits = (uint32_t)(win[r] >> 31);
+      bits = (bits & 0x80000000u) ? (bits & 0x7fffffffu) : ~bits;
+      const float val = __uint_as_float(bits);
+#pragma unroll
+      for (int i = 0; i < NK; ++i)
+        if ((uint64_t)__double_as_longlong(key[r][i]) == win[r]) key[r][i] = 0.0;
+      if (lane == j) {
+        my_val[r] = val;
+        my_id[r] = (int)min(id, (uint32_t)(E - 1));
+      }
+      if (j == 0) top[r] = val;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float z = lane < k ? expf(my_val[r] - top[r]) : 0.0f;
+    float zsum = 0.0f;
+    for (int q = 0; q < k; ++q)
+      zsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), q));
+    if (lane < k) {
+      ids[r][lane] = my_id[r];
+      w[r][lane] = z / zsum;
+    }
+  }
+}
+
+template <int NK>
+__device__ void topk_block_rows(const DecodeArgs& a, int* s_ids, float* s_w) {
+  // wave w: token w, and token w + 4 alongside it when there is one
+  const int w = threadIdx.x >> 6;
+  for (int t = w; t < a.T; t += 2 * (kThreads / kWave)) {
+    const int t2 = t + kThreads / kWave;
+    if (t2 < a.T) {
+      const float* L[2] = {a.logits + (size_t)t * a.E, a.logits + (size_t)t2 * a.E};
+      int* ids[2] = {s_ids + t * a.k, s_ids + t2 * a.k};
+      float* ws[2] = {s_w + t * a.k, s_w + t2 * a.k};
+      topk_rows_f64<NK, 2>(L, a.E, a.k, ids, ws);
+    } else {
+      const float* L[1] = {a.logits + (size_t)t * a.E};
+      int* ids[1] = {s_ids + t * a.k};
+      float* ws[1] = {s_w + t * a.k};
+      topk_rows_f64<NK, 1>(L, a.E, a.k, ids, ws);
+    }
   }
 }
 
@@ -314,8 +372,10 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
   float* s_w = reinterpret_cast<float*>(s_ids + R);
   int* s_first = reinterpret_cast<int*>(s_w + R);
   int* s_tmp = s_first + R;
-  for (int t = threadIdx.x >> 6; t < a.T; t += kThreads / kWave)
-    topk_row<16>(a.logits + (size_t)t * a.E, a.E, a.k, s_ids + t * a.k, s_w + t * a.k);
+  if (a.E <= 6 * kWave)
+    topk_block_rows<6>(a, s_ids, s_w);
+  else
+    topk_block_rows<16>(a, s_ids, s_w);
   __syncthreads();
   // Stable counting sort by ranks, no atomics: pair p (token p / k) of
   // expert e goes to row (#pairs with a smaller expert) + (#earlier pairs
@@ -324,6 +384,7 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
   for (int p = threadIdx.x; p < R; p += kThreads) {
     const int e = s_ids[p];
     int less = 0, before = 0, same = 0;
+#pragma unroll 8
     for (int q = 0; q < R; ++q) {
       const int f = s_ids[q];
       less += f < e;
@@ -347,6 +408,7 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
     if (fp < 0) continue;
     const int e = s_ids[p];
     int slot = 0;
+#pragma unroll 8
     for (int q = 0; q < R; ++q) slot += (s_first[q] >= 0) & (s_ids[q] < e);
     tex[slot] = e;
     tex[a.max_slots + slot] = fp >> 11;
@@ -589,9 +651,16 @@ __device__ void combine_column(const DecodeArgs& a, int c) {
   if (n >= a.H) return;
   for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
     float v = a.has_shared ? cld(a.y + (size_t)(a.R + t) * a.H + n) : 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-      const int r = min(max(a.inv_row[t * a.k + j], 0), a.R - 1);
-      v = fmaf(a.route_w[t * a.k + j], cld(a.y + (size_t)r * a.H + n), v);
+    for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
+      float yv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = min(max(a.inv_row[t * a.k + min(j0 + u, a.k - 1)], 0), a.R - 1);
+        yv[u] = cld(a.y + (size_t)r * a.H + n);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < a.k) v = fmaf(a.route_w[t * a.k + j0 + u], yv[u], v);
     }
     a.out[(size_t)t * a.H + n] = v;
   }
@@ -728,57 +797,6 @@ __device__ void poll_tagged(const DecodeArgs& a, const uint64_t* src, int n, uin
     }
     __builtin_amdgcn_s_sleep(1);
   }
-}
-
-// Key of (logit, expert) that orders like (logit descending, id ascending)
-// and whose bits, read as an fp64, are a positive normal number (or +0 for
-// an empty slot), so fp64 max picks the larger key: the order-preserving
-// 32-bit image of the logit in bits 62..31, 2^31 - 1 - e below. NaN logits
-// rank as -inf, so no key is an fp64 NaN, infinity or subnormal.
-__device__ __forceinline__ uint64_t topk_key_f64(float v, int e) {
-  v = (v != v) ? -INFINITY : v;
-  uint32_t b = __float_as_uint(v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 31) | (uint32_t)(0x7fffffffu - (uint32_t)e);
-}
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_max_f64(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL,
-                                                            0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32),
-                                                            (int)(uint32_t)(u >> 32), CTRL, 0xf,
-                                                            0xf, false);
-  return fmax(v, __longlong_as_double((long long)(((uint64_t)hi << 32) | lo)));
-}
-
-// Wave-wide maximum of such keys, in every lane, without leaving the vector
-// unit: DPP within each row of 16 lanes (xor 1, xor 2, half-row mirror, row
-// mirror), then lane swaps across rows (16, then 32 apart).
-__device__ __forceinline__ uint64_t wave_max_key_f64(uint64_t k) {
-  double v = __longlong_as_double((long long)k);
-  v = dpp_max_f64<0xB1>(v);
-  v = dpp_max_f64<0x4E>(v);
-  v = dpp_max_f64<0x141>(v);
-  v = dpp_max_f64<0x140>(v);
-  uint64_t u = (uint64_t)__double_as_longlong(v);
-  {
-    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false,
-                                                     false);
-    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
-             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
-  }
-  u = (uint64_t)__double_as_longlong(v);
-  {
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false,
-                                                     false);
-    v = fmax(__longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0])),
-             __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1])));
-  }
-  return (uint64_t)__double_as_longlong(v);
 }
 
 // The one-token routing workgroup (wave 0): waits for the tagged logits,
@@ -1132,6 +1150,377 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
 }
 
 // ---------------------------------------------------------------------------
+// A block of a few tokens (2 <= T <= kBlockT, a verification block): the
+// one-token streaming design over the union of the block's experts. A
+// verification step pays for the union of its tokens' experts (ai.rs
+// article, "The draft head that works and does not pay"), so each selected
+// expert's rows are read once per call and used for every token routed to
+// it. Launch 1 is the router and the routing (route_kernel without shared
+// items); launch 2 streams the gate/up items of the shared expert and of
+// every routed slot, each item's weights in registers while the slot's
+// tokens are taken from the block staged in LDS; launch 3 streams the down
+// items the same way, and the workgroup that completes a column group
+// combines it for every token.
+// ---------------------------------------------------------------------------
+constexpr int kBlockT = 5;
+constexpr int kXRow = 4 * kGuLanes * kGuU;  // uint4 per staged token row (H <= 5120)
+constexpr int kBlockXLoads = 16;            // router: T * H / 8 <= 16 * kThreads
+
+// Gate/up item `it` of the block: items [0, n_sh) are the shared expert's
+// 8-row groups (all T tokens), then (routed slot, 8-row group) pairs,
+// slot-major. Every field is clamped to the bank and rows that exist.
+struct BlkItem {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int rb;     // row group
+  int row0;   // first h / y row of the slot
+  int m;      // the slot's rows (tokens)
+  bool shared;
+};
+
+__device__ __forceinline__ BlkItem blk_item(const DecodeArgs& a, const int* tab, int n_sh, int it,
+                                            int per, bool gu) {
+  const uint32_t crow = (uint32_t)(gu ? a.H : a.I) >> 1, srow = (uint32_t)(gu ? a.H : a.I) >> 5;
+  const size_t mat = gu ? 2 * (size_t)a.I : (size_t)a.H;
+  const uint8_t* c0 = gu ? a.routed.gu_codes : a.routed.d_codes;
+  const uint8_t* s0 = gu ? a.routed.gu_scales : a.routed.d_scales;
+  if (it < n_sh)
+    return BlkItem{gu ? a.shared.gu_codes : a.shared.d_codes,
+                   gu ? a.shared.gu_scales : a.shared.d_scales, it, a.R, min(a.T, kBlockT), true};
+  const int q = it - n_sh, sl = q / per, rb = q - sl * per;
+  const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + sl], 0), a.routed.E - 1));
+  const int row0 = min(max(tab[1 + a.max_slots + sl], 0), a.R);
+  const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, kBlockT));
+  return BlkItem{c0 + (size_t)e * mat * crow, s0 + (size_t)e * mat * srow, rb, row0, m, false};
+}
+
+__device__ __forceinline__ void gu_issue_blk(const DecodeArgs& a, const BlkItem& d, GuRegs& r,
+                                             bool live) {
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int nr = min(d.rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes, a.I - 1);
+  const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> 5;
+  const uint8_t* gbase = uniform_ptr(d.codes);
+  const uint8_t* sbase = uniform_ptr(d.scales);
+  const uint32_t cb = live ? a.I * crow : 0u, sb = live ? a.I * srow : 0u;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, cb);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, cb);
+  const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, sb);
+  const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, sb);
+  const int co = nr * crow + j * 16, so = nr * srow + (j & ~3);
+#pragma unroll
+  for (int u = 0; u < kGuU; ++u) {
+    r.g[u] = bload16(rg, co + u * kGuLanes * 16);
+    r.u[u] = bload16(ru, co + u * kGuLanes * 16);
+    r.sg[u] = bload32(rgs, so + u * kGuLanes);
+    r.su[u] = bload32(rus, so + u * kGuLanes);
+  }
+}
+
+// One item's rows for each of the slot's tokens: each 16-byte chunk of
+// weights is converted to bf16 once and used for every token, whose row
+// comes from the staged block at s_x + t * kXRow. Unrolled over the block
+// (no loop-carried store, so the waits for this item's weights do not also
+// wait for the next item's).
+__device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkItem& d,
+                                               const int* s_rt, const GuRegs& r,
+                                               const uint4* s_x) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int n = d.rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes;
+  const int kc = a.H >> 5;
+  const uint32_t sh = 8u * (j & 3);
+  constexpr int P = kGuLanes * kGuU;
+  const uint4* xt[kBlockT];
+  float ag[kBlockT], au[kBlockT];
+#pragma unroll
+  for (int i = 0; i < kBlockT; ++i) {
+    const int t = i >= d.m ? 0 : d.shared ? i : min(max(s_rt[d.row0 + i], 0), a.T - 1);
+    xt[i] = s_x + t * kXRow;
+    ag[i] = au[i] = 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < kGuU; ++u) {
+    const int c = kGuLanes * u + j;
+    if (c < kc) {
+      const float fg = e8m0_to_f32(__builtin_amdgcn_ubfe(r.sg[u], sh, 8));
+      const float fu = e8m0_to_f32(__builtin_amdgcn_ubfe(r.su[u], sh, 8));
+      const uint32_t gw[4] = {r.g[u].x, r.g[u].y, r.g[u].z, r.g[u].w};
+      const uint32_t uw[4] = {r.u[u].x, r.u[u].y, r.u[u].z, r.u[u].w};
+      bf16x2_t wg[16], wu[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wg[4 * q + 0] = fp4x2_to_bf16<0>(gw[q]);
+        wg[4 * q + 1] = fp4x2_to_bf16<1>(gw[q]);
+        wg[4 * q + 2] = fp4x2_to_bf16<2>(gw[q]);
+        wg[4 * q + 3] = fp4x2_to_bf16<3>(gw[q]);
+        wu[4 * q + 0] = fp4x2_to_bf16<0>(uw[q]);
+        wu[4 * q + 1] = fp4x2_to_bf16<1>(uw[q]);
+        wu[4 * q + 2] = fp4x2_to_bf16<2>(uw[q]);
+        wu[4 * q + 3] = fp4x2_to_bf16<3>(uw[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < kBlockT; ++i) {
+        if (i < d.m) {
+          const uint4* xv = xt[i] + c;
+          float pg = 0.0f, pu = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 xq = xv[q * P];
+            const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              pg = __builtin_amdgcn_fdot2_f32_bf16(wg[4 * q + p], as_bf16x2(xw[p]), pg, false);
+              pu = __builtin_amdgcn_fdot2_f32_bf16(wu[4 * q + p], as_bf16x2(xw[p]), pu, false);
+            }
+          }
+          ag[i] = fmaf(pg, fg, ag[i]);
+          au[i] = fmaf(pu, fu, au[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kBlockT; ++i) {
+    if (i < d.m) {
+      const float g = group_sum<kGuLanes>(ag[i]), u = group_sum<kGuLanes>(au[i]);
+      if (j == 0 && n < a.I) a.h[(size_t)(d.row0 + i) * a.I + n] = silu_mul(g, u);
+    }
+  }
+}
+
+// Block router rows: a wave per expert row, the row's loads issued before
+// the block's T token rows are staged in LDS, then T dot products.
+__device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
+  const int lane = lane_id();
+  const int e0 = b * 4 + (int)(threadIdx.x >> 6);
+  const int e = min(e0, a.E - 1);
+  const int nv = a.H >> 3;
+  const uint4* wrow = reinterpret_cast<const uint4*>(a.wr + (size_t)e * a.H);
+  // the block's rows first (L2, all loads in flight together: T * H / 8 <=
+  // 16 * 256), then the weight row (HBM), so staging waits for the rows only
+  const int total = a.T * nv;
+  const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+  uint4 v[kBlockXLoads];
+#pragma unroll
+  for (int i = 0; i < kBlockXLoads; ++i) v[i] = xs[min((int)threadIdx.x + i * kThreads, total - 1)];
+  uint4 wv[kRouterV];
+#pragma unroll
+  for (int i = 0; i < kRouterV; ++i) wv[i] = wrow[min(lane + kWave * i, nv - 1)];
+#pragma unroll
+  for (int i = 0; i < kBlockXLoads; ++i)
+    if ((int)threadIdx.x + i * kThreads < total) s_x[threadIdx.x + i * kThreads] = v[i];
+  __syncthreads();
+  const float bb = a.bias ? a.bias[e] : 0.0f;
+  for (int t = 0; t < a.T; ++t) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRouterV; ++i)
+      if (lane + kWave * i < nv) acc = dot8_bf16(wv[i], s_x[t * nv + lane + kWave * i], acc);
+    acc = wave_sum(acc);
+    if (lane == 0 && e0 < a.E) cst(a.logits + (size_t)t * a.E + e, acc + bb);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) cst(a.flags + b, a.epoch);
+}
+
+// Block launch 1: [router rows | the routing workgroup].
+__global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x < a.nb_router)
+    router_rows_blk(a, blockIdx.x, reinterpret_cast<uint4*>(lds));
+  else
+    routing(a, lds);
+}
+
+// Block gate/up: G persistent workgroups stage the T token rows and the
+// slot table, then stream their items with two register buffers.
+__global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
+  extern __shared__ __align__(16) char lds[];
+  uint4* s_x = reinterpret_cast<uint4*>(lds);
+  const int T = min(a.T, kBlockT);
+  int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
+  int* s_rt = s_tab + 1 + 3 * a.max_slots;
+  const int nv = a.H >> 3;
+  stage_rows<uint4>(
+      T * nv, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+      [&](int idx, uint4 v) {
+        const int t = idx / nv, q = idx - t * nv;
+        s_x[t * kXRow + (q & 3) * (kGuLanes * kGuU) + (q >> 2)] = v;
+      });
+  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
+  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
+  __syncthreads();
+  const int ns = min(max(s_tab[0], 0), a.max_slots);
+  const int n_sh = a.has_shared ? a.gu_items : 0;
+  const int n = n_sh + ns * a.gu_items;
+  const int b = blockIdx.x;
+  // fixed trip over pairs of items; padding issues read nothing
+  const int mine = b < n ? (n - b + G - 1) / G : 0;
+  GuRegs A, B;
+  gu_issue_blk(a, blk_item(a, s_tab, n_sh, b < n ? b : 0, a.gu_items, true), A, b < n);
+  for (int kk = 0; kk < mine; kk += 2) {
+    const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
+    gu_issue_blk(a, blk_item(a, s_tab, n_sh, i1 < n ? i1 : i0, a.gu_items, true), B, i1 < n);
+    gu_compute_blk(a, blk_item(a, s_tab, n_sh, i0, a.gu_items, true), s_rt, A, s_x);
+    gu_issue_blk(a, blk_item(a, s_tab, n_sh, i2 < n ? i2 : i0, a.gu_items, true), A, i2 < n);
+    if (i1 < n) gu_compute_blk(a, blk_item(a, s_tab, n_sh, i1, a.gu_items, true), s_rt, B, s_x);
+  }
+}
+
+struct DnW {
+  uint4 w[kDnU];
+  uint32_t sc[kDnU];
+};
+__device__ __forceinline__ void dn_issue_blk(const DecodeArgs& a, const BlkItem& d, DnW& r,
+                                             bool live) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int nr = min(d.rb * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(uniform_ptr(d.codes), live ? a.H * crow : 0u);
+  const __amdgpu_buffer_rsrc_t rds = matrix_rsrc(uniform_ptr(d.scales), live ? a.H * srow : 0u);
+  const int co = nr * crow + j * 16, so = nr * srow + 4 * (j >> 2);
+#pragma unroll
+  for (int u = 0; u < kDnU; ++u) {
+    r.w[u] = bload16(rd, co + u * 8 * 16);
+    r.sc[u] = bload32(rds, so + u * 8);
+  }
+}
+
+// One down item for each of the slot's rows, y rows stored write-through
+// for the combine in this launch. The slot's h rows (written by the previous
+// launch) are staged in LDS when the slot differs from the last item's:
+// a workgroup's items are a contiguous stretch, so that happens once or
+// twice per workgroup.
+__device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkItem& d, int slot,
+                                               int& staged, const DnW& r, f32x4_t* s_h) {
+  const int nv = a.I >> 2;
+  constexpr int kHRow = 8 * kDnU * 8;  // f32x4_t per staged h row (I <= 2304)
+  if (slot != staged) {
+    __syncthreads();  // reads of the previous slot's rows are done
+    stage_rows<f32x4_t>(
+        d.m * nv,
+        [&](int idx) {
+          const int i = idx / nv, f = idx - i * nv;
+          return reinterpret_cast<const f32x4_t*>(a.h + (size_t)(d.row0 + i) * a.I)[f];
+        },
+        [&](int idx, f32x4_t v) {
+          const int i = idx / nv, f = idx - i * nv;
+          s_h[i * kHRow + (f & 7) * (8 * kDnU) + (f >> 3)] = v;
+        });
+    __syncthreads();
+    staged = slot;
+  }
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int n = d.rb * kDnRows + wave * 8 + (lane >> 3);
+  const int kc = a.I >> 5;
+  const uint32_t sh = 8u * (j & 3);
+  constexpr int P = 8 * kDnU;
+  float acc[kBlockT];
+#pragma unroll
+  for (int i = 0; i < kBlockT; ++i) acc[i] = 0.0f;
+  // each 16-byte chunk of weights converted to fp32 once, used by every row
+#pragma unroll
+  for (int u = 0; u < kDnU; ++u) {
+    const int ch = 8 * u + j;
+    if (ch < kc) {
+      const float fd = e8m0_to_f32(__builtin_amdgcn_ubfe(r.sc[u], sh, 8));
+      const uint32_t ww[4] = {r.w[u].x, r.w[u].y, r.w[u].z, r.w[u].w};
+      f32x2_t wf[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wf[4 * q + 0] = fp4x2_to_f32<0>(ww[q]);
+        wf[4 * q + 1] = fp4x2_to_f32<1>(ww[q]);
+        wf[4 * q + 2] = fp4x2_to_f32<2>(ww[q]);
+        wf[4 * q + 3] = fp4x2_to_f32<3>(ww[q]);
+      }
+#pragma unroll
+      for (int i = 0; i < kBlockT; ++i) {
+        if (i < d.m) {
+          const f32x4_t* hv = s_h + i * kHRow + ch;
+          float pd = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t ha = hv[2 * q * P], hb = hv[(2 * q + 1) * P];
+            pd = fmaf(wf[4 * q + 0].x, ha.x, pd);
+            pd = fmaf(wf[4 * q + 0].y, ha.y, pd);
+            pd = fmaf(wf[4 * q + 1].x, ha.z, pd);
+            pd = fmaf(wf[4 * q + 1].y, ha.w, pd);
+            pd = fmaf(wf[4 * q + 2].x, hb.x, pd);
+            pd = fmaf(wf[4 * q + 2].y, hb.y, pd);
+            pd = fmaf(wf[4 * q + 3].x, hb.z, pd);
+            pd = fmaf(wf[4 * q + 3].y, hb.w, pd);
+          }
+          acc[i] = fmaf(pd, fd, acc[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kBlockT; ++i) {
+    if (i < d.m) {
+      const float v = group_sum<8>(acc[i]);
+      if (j == 0 && n < a.H) cst(a.y + (size_t)(d.row0 + i) * a.H + n, v);
+    }
+  }
+}
+
+// Block down: routed (slot, 32-row group) items slot-major, then the shared
+// expert's groups; workgroup b takes the contiguous stretch
+// [n b / G, n (b + 1) / G) with two register buffers for the weights. It then
+// drains its y stores and bumps the counter of each item's column group;
+// the workgroup that brings a column group to (slots + shared) parts
+// combines it for every token.
+__global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, int G) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ int s_last[32];
+  int* tab = reinterpret_cast<int*>(lds);
+  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int));
+  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) tab[i] = a.tab[i];
+  __syncthreads();
+  const int ns = min(max(tab[0], 0), a.max_slots);
+  const int nr = ns * a.dn_items;
+  const int n = nr + (a.has_shared ? a.dn_items : 0);
+  const int parts = ns + (a.has_shared ? 1 : 0);
+  const int b = blockIdx.x;
+  const int lo = (int)((long)n * b / G), hi = (int)((long)n * (b + 1) / G);  // hi - lo <= 32
+  if (lo >= hi) return;
+  // item it: routed items first, so the shared groups follow at offset nr
+  auto item = [&](int it) {
+    return it < nr ? blk_item(a, tab, 0, it, a.dn_items, false)
+                   : blk_item(a, tab, a.dn_items, it - nr, a.dn_items, false);
+  };
+  auto slot_of = [&](int it) { return it < nr ? it / a.dn_items : ns; };
+  int staged = -1;
+  DnW A, B;
+  dn_issue_blk(a, item(lo), A, true);
+  for (int i0 = lo; i0 < hi; i0 += 2) {
+    const int i1 = i0 + 1, i2 = i0 + 2;
+    dn_issue_blk(a, item(i1 < hi ? i1 : i0), B, i1 < hi);
+    dn_compute_blk(a, item(i0), slot_of(i0), staged, A, s_h);
+    dn_issue_blk(a, item(i2 < hi ? i2 : i0), A, i2 < hi);
+    if (i1 < hi) dn_compute_blk(a, item(i1), slot_of(i1), staged, B, s_h);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int mine = hi - lo;
+  if ((int)threadIdx.x < mine) {
+    const int c = (lo + (int)threadIdx.x) % a.dn_items;  // nr is a multiple of dn_items
+    s_last[threadIdx.x] =
+        __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        parts - 1;
+  }
+  __syncthreads();
+  for (int t = 0; t < mine; ++t)
+    if (s_last[t]) combine_column(a, (lo + t) % a.dn_items);
+}
+
+// ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
 template <int MT>
@@ -1334,7 +1723,31 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
     launch("down_stream_kernel", down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a,
            gd);
-  } else if (one)
+    return;
+  }
+  // A block of 2..kBlockT tokens: router + routing, then the streaming
+  // gate/up and down launches over the union of the block's experts.
+  const bool block = d.T >= 2 && d.T <= kBlockT && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
+                     d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU &&
+                     d.E <= 16 * kWave && 1 + 3 * L.max_slots <= 1024 &&
+                     d.T * (d.H >> 3) <= kBlockXLoads * kThreads &&
+                     (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
+  if (block) {
+    const uint32_t lds_rt = (uint32_t)(d.T * d.H * 2 > kLdsBytes ? d.T * d.H * 2 : kLdsBytes);
+    launch("route_block_kernel", route_block_kernel, dim3(L.nb_router + 1), dim3(kThreads), lds_rt,
+           s, a);
+    const int ng = (shared ? L.gu_items : 0) + L.max_slots * L.gu_items;
+    const int gg = ng < kStreamBlocks ? ng : kStreamBlocks;
+    const uint32_t lds_gu =
+        (uint32_t)(d.T * kXRow * 16 + sizeof(int) * (1 + 3 * L.max_slots + d.R));
+    launch("gateup_block_kernel", gateup_block_kernel, dim3(gg), dim3(kThreads), lds_gu, s, a, gg);
+    const int nd = (L.max_slots + (shared ? 1 : 0)) * L.dn_items;
+    const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
+    const uint32_t lds_dn = (uint32_t)(1024 * sizeof(int) + d.T * 8 * kDnU * 8 * 16);
+    launch("down_block_kernel", down_block_kernel, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
+    return;
+  }
+  if (one)
     launch_chain<1>(a, L, ffn, shared, routed_gu, shared_dn, ffn ? d.row_token : a.row_token, s);
   else
     launch_chain<kMT>(a, L, ffn, shared, routed_gu, shared_dn, ffn ? d.row_token : a.row_token, s);

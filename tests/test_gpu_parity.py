@@ -356,6 +356,47 @@ def test_layer_one_token_path(w, variant):
     assert err < HP.FP32_TOL
 
 
+# Blocks of 2..5 tokens (verification blocks): router + routing, then the
+# streaming gate/up and down launches over the union of the block's experts,
+# at shapes where slots hold 1..T tokens, the shared expert's items and the
+# per-workgroup item ranges differ from the real shape's.
+BLOCKS = [
+    S.Workload("blk_small", 95, T=2, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_narrow", 97, T=4, H=256, E=16, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_five_wide", 98, T=5, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+]
+
+# kernels of the block path
+BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_kernel"]
+
+
+@pytest.mark.parametrize("variant", ["shared", "no_shared_with_bias"])
+@pytest.mark.parametrize("w", BLOCKS, ids=lambda w: w.name)
+def test_layer_block_path(w, variant):
+    d = S.gen_inputs(w, 0)
+    bias, shared = None, d["shared"]
+    if variant == "no_shared_with_bias":
+        bias, shared = np.linspace(-0.5, 0.5, w.E).astype(np.float32), None
+    err = _layer_parity(w, d["x"], d["w_router"], bias, d["routed"], shared)
+    assert _launches() == BLOCK_PATH
+    assert err < HP.FP32_TOL
+
+
+def test_layer_block_path_correlated_tokens_share_experts():
+    # tokens drawn as one base plus small noise pick mostly the same
+    # experts, so slots hold several tokens each
+    w = S.Workload("blk_corr", 99, T=5, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3,
+                   block=5, noise=0.05)
+    d = S.gen_inputs(w, 0)
+    r = O.route(d["x"], d["w_router"], None, w.k)
+    union = set(r["ids"].reshape(-1).tolist())
+    assert len(union) < w.T * w.k  # experts are shared between tokens
+    err = _layer_parity(w, d["x"], d["w_router"], None, d["routed"], d["shared"])
+    assert _launches() == BLOCK_PATH
+    assert err < HP.FP32_TOL
+
+
 def test_layer_one_token_shapes_share_a_garbage_workspace():
     # one workspace, filled with random bytes, then used by every one-token
     # shape in turn, twice: tags, counters and tables left at other offsets
