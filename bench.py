@@ -250,10 +250,12 @@ def kernel_work(name, w, U, shared=True):
             + (R + (T if shared else 0)) * I * 4
     if name == "down_block_kernel":
         # down of the U routed experts and the shared one, h rows read, y rows
-        # written and read back by the combine, the output written
+        # written
         rows = R + (T if shared else 0)
-        return "hbm", (U + (1 if shared else 0)) * dn_expert + rows * I * 4 + 2 * rows * H * 4 \
-            + T * H * 4 + T * w.k * 8
+        return "hbm", (U + (1 if shared else 0)) * dn_expert + rows * I * 4 + rows * H * 4
+    if name == "combine_block_kernel":
+        rows = R + (T if shared else 0)
+        return "hbm", rows * H * 4 + T * H * 4 + T * w.k * 8
     if name in ("gateup_stream_kernel", "gateup_kernel"):
         # routed gate/up of the U experts (+ the shared expert's down rows)
         b = U * gu_expert + T * H * 2 + R * I * 4

@@ -1391,29 +1391,45 @@ __device__ __forceinline__ void dn_issue_blk(const DecodeArgs& a, const BlkItem&
   }
 }
 
-// One down item for each of the slot's rows, y rows stored write-through
-// for the combine in this launch. The slot's h rows (written by the previous
-// launch) are staged in LDS when the slot differs from the last item's:
-// a workgroup's items are a contiguous stretch, so that happens once or
-// twice per workgroup.
-__device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkItem& d, int slot,
-                                               int& staged, const DnW& r, f32x4_t* s_h) {
+// Direct global -> LDS copy: lane l's 16 bytes at base + voff land at LDS
+// byte address lds + 16 l (lds wave-uniform). Invisible to the compiler's
+// wait counting: the caller waits for it explicitly.
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+               :
+               : "v"(voff), "s"(lds), "s"(base)
+               : "memory");
+}
+
+constexpr int kHRow = 8 * kDnU * 8;    // f32x4_t per staged h row (I <= 2304)
+constexpr int kDnIssueLoads = 2 * kDnU;  // vector loads of one dn_issue_blk
+
+// Copy the h rows of down item d's slot (written by the previous launch)
+// into LDS: slot q of row i holds float4 f = (q % 72) * 8 + q / 72 of the
+// row, the transposed order the compute reads without bank conflicts.
+__device__ __forceinline__ void dn_copy_h(const DecodeArgs& a, const BlkItem& d, uint32_t s_h_lds) {
   const int nv = a.I >> 2;
-  constexpr int kHRow = 8 * kDnU * 8;  // f32x4_t per staged h row (I <= 2304)
-  if (slot != staged) {
-    __syncthreads();  // reads of the previous slot's rows are done
-    stage_rows<f32x4_t>(
-        d.m * nv,
-        [&](int idx) {
-          const int i = idx / nv, f = idx - i * nv;
-          return reinterpret_cast<const f32x4_t*>(a.h + (size_t)(d.row0 + i) * a.I)[f];
-        },
-        [&](int idx, f32x4_t v) {
-          const int i = idx / nv, f = idx - i * nv;
-          s_h[i * kHRow + (f & 7) * (8 * kDnU) + (f >> 3)] = v;
-        });
+  const int total = d.m * kHRow;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  for (int q0 = 0; q0 < total; q0 += kThreads) {
+    const int q = q0 + (int)threadIdx.x;
+    const int i = min(q / kHRow, max(d.m - 1, 0)), qq = q - (q / kHRow) * kHRow;
+    const int f = min((qq % (8 * kDnU)) * 8 + qq / (8 * kDnU), nv - 1);
+    if (q < total)
+      lds_copy16(a.h, (uint32_t)(((size_t)(d.row0 + i) * a.I + 4 * f) * 4),
+                 s_h_lds + (uint32_t)((q0 + 64 * wave) * 16));
+  }
+}
+
+// One down item for each of the slot's rows, y rows stored write-through
+// for the combine in this launch. `fresh`: the slot's h rows were just
+// copied (before the kDnIssueLoads loads of the next item's weights), so
+// wait for the copies and make them visible to every wave first.
+__device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkItem& d, bool fresh,
+                                               const DnW& r, const f32x4_t* s_h) {
+  if (fresh) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDnIssueLoads) : "memory");
     __syncthreads();
-    staged = slot;
   }
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & 7;
@@ -1472,13 +1488,11 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
 
 // Block down: routed (slot, 32-row group) items slot-major, then the shared
 // expert's groups; workgroup b takes the contiguous stretch
-// [n b / G, n (b + 1) / G) with two register buffers for the weights. It then
-// drains its y stores and bumps the counter of each item's column group;
-// the workgroup that brings a column group to (slots + shared) parts
-// combines it for every token.
+// [n b / G, n (b + 1) / G) with two register buffers for the weights. The
+// combine is a launch of its own: combining in the last workgroup to finish
+// a column group put the combine's coherent loads on the tail of this one.
 __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
-  __shared__ int s_last[32];
   int* tab = reinterpret_cast<int*>(lds);
   f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int));
   for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) tab[i] = a.tab[i];
@@ -1486,9 +1500,8 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
   const int ns = min(max(tab[0], 0), a.max_slots);
   const int nr = ns * a.dn_items;
   const int n = nr + (a.has_shared ? a.dn_items : 0);
-  const int parts = ns + (a.has_shared ? 1 : 0);
   const int b = blockIdx.x;
-  const int lo = (int)((long)n * b / G), hi = (int)((long)n * (b + 1) / G);  // hi - lo <= 32
+  const int lo = (int)((long)n * b / G), hi = (int)((long)n * (b + 1) / G);
   if (lo >= hi) return;
   // item it: routed items first, so the shared groups follow at offset nr
   auto item = [&](int it) {
@@ -1496,28 +1509,47 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
                    : blk_item(a, tab, a.dn_items, it - nr, a.dn_items, false);
   };
   auto slot_of = [&](int it) { return it < nr ? it / a.dn_items : ns; };
+  // The slot's h rows are copied into LDS when an item's slot differs from
+  // the one staged (once or twice per workgroup: its items are a contiguous
+  // stretch), each copy issued between the item's weights and the next
+  // item's, so waiting for it never waits for the next item's weights.
+  const uint32_t s_h_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds +
+                           1024 * sizeof(int);
+  auto restage = [&](int it, int& staged) {
+    __syncthreads();  // every wave is done reading the staged rows
+    dn_copy_h(a, item(it), s_h_lds);
+    staged = slot_of(it);
+  };
   int staged = -1;
   DnW A, B;
   dn_issue_blk(a, item(lo), A, true);
+  restage(lo, staged);
+  bool fresh = true;
   for (int i0 = lo; i0 < hi; i0 += 2) {
     const int i1 = i0 + 1, i2 = i0 + 2;
     dn_issue_blk(a, item(i1 < hi ? i1 : i0), B, i1 < hi);
-    dn_compute_blk(a, item(i0), slot_of(i0), staged, A, s_h);
+    dn_compute_blk(a, item(i0), fresh, A, s_h);
+    fresh = false;
+    if (i1 < hi && slot_of(i1) != staged) {
+      restage(i1, staged);
+      fresh = true;
+    }
     dn_issue_blk(a, item(i2 < hi ? i2 : i0), A, i2 < hi);
-    if (i1 < hi) dn_compute_blk(a, item(i1), slot_of(i1), staged, B, s_h);
+    if (i1 < hi) {
+      dn_compute_blk(a, item(i1), fresh, B, s_h);
+      fresh = false;
+      if (i2 < hi && slot_of(i2) != staged) {
+        restage(i2, staged);
+        fresh = true;
+      }
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const int mine = hi - lo;
-  if ((int)threadIdx.x < mine) {
-    const int c = (lo + (int)threadIdx.x) % a.dn_items;  // nr is a multiple of dn_items
-    s_last[threadIdx.x] =
-        __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        parts - 1;
-  }
-  __syncthreads();
-  for (int t = 0; t < mine; ++t)
-    if (s_last[t]) combine_column(a, (lo + t) % a.dn_items);
+}
+
+// Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
+// token in fixed order (shared row, then j = 0..k-1).
+__global__ __launch_bounds__(kThreads) void combine_block_kernel(DecodeArgs a) {
+  combine_column(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1730,8 +1762,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   const bool block = d.T >= 2 && d.T <= kBlockT && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
                      d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU &&
                      d.E <= 16 * kWave && 1 + 3 * L.max_slots <= 1024 &&
-                     d.T * (d.H >> 3) <= kBlockXLoads * kThreads &&
-                     (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
+                     d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
   if (block) {
     const uint32_t lds_rt = (uint32_t)(d.T * d.H * 2 > kLdsBytes ? d.T * d.H * 2 : kLdsBytes);
     launch("route_block_kernel", route_block_kernel, dim3(L.nb_router + 1), dim3(kThreads), lds_rt,
@@ -1745,6 +1776,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
     const uint32_t lds_dn = (uint32_t)(1024 * sizeof(int) + d.T * 8 * kDnU * 8 * 16);
     launch("down_block_kernel", down_block_kernel, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
+    launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
     return;
   }
   if (one)

@@ -368,7 +368,8 @@ BLOCKS = [
 ]
 
 # kernels of the block path
-BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_kernel"]
+BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_kernel",
+              "combine_block_kernel"]
 
 
 @pytest.mark.parametrize("variant", ["shared", "no_shared_with_bias"])
