@@ -241,13 +241,16 @@ def kernel_work(name, w, U, shared=True):
         return "hbm", U * dn_expert + R * I * 4 + R * H * 4 + (T * H * 4 if shared else 0) \
             + T * H * 4 + T * w.k * 8
     if name == "route_block_kernel":
-        # block of tokens: router rows and the routing
-        return "hbm", w.E * H * 2 + T * H * 2 + T * w.E * 4
+        # block of tokens: router rows, the routing, the shared expert's
+        # gate/up for every token of the block
+        b = w.E * H * 2 + T * H * 2 + T * w.E * 4
+        if shared:
+            b += gu_expert + T * I * 4
+        return "hbm", b
     if name == "gateup_block_kernel":
-        # gate/up of the U routed experts and the shared one, each read once
-        # for all the block's tokens routed to it; h rows written
-        return "hbm", (U + (1 if shared else 0)) * gu_expert + T * H * 2 \
-            + (R + (T if shared else 0)) * I * 4
+        # gate/up of the U routed experts, each read once for all the block's
+        # tokens routed to it; h rows written
+        return "hbm", U * gu_expert + T * H * 2 + R * I * 4
     if name == "down_block_kernel":
         # down of the U routed experts and the shared one, h rows read, y rows
         # written

@@ -1326,23 +1326,10 @@ __device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
   if (threadIdx.x == 0) cst(a.flags + b, a.epoch);
 }
 
-// Block launch 1: [router rows | the routing workgroup].
-__global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a) {
-  extern __shared__ __align__(16) char lds[];
-  if ((int)blockIdx.x < a.nb_router)
-    router_rows_blk(a, blockIdx.x, reinterpret_cast<uint4*>(lds));
-  else
-    routing(a, lds);
-}
-
-// Block gate/up: G persistent workgroups stage the T token rows and the
-// slot table, then stream their items with two register buffers.
-__global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
-  extern __shared__ __align__(16) char lds[];
-  uint4* s_x = reinterpret_cast<uint4*>(lds);
+// The block's T token rows into LDS (row t at s_x + t * kXRow, chunk-
+// transposed like the one-token row).
+__device__ __forceinline__ void stage_block_rows(const DecodeArgs& a, uint4* s_x) {
   const int T = min(a.T, kBlockT);
-  int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
-  int* s_rt = s_tab + 1 + 3 * a.max_slots;
   const int nv = a.H >> 3;
   stage_rows<uint4>(
       T * nv, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
@@ -1350,13 +1337,13 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
         const int t = idx / nv, q = idx - t * nv;
         s_x[t * kXRow + (q & 3) * (kGuLanes * kGuU) + (q >> 2)] = v;
       });
-  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
-  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
-  __syncthreads();
-  const int ns = min(max(s_tab[0], 0), a.max_slots);
-  const int n_sh = a.has_shared ? a.gu_items : 0;
-  const int n = n_sh + ns * a.gu_items;
-  const int b = blockIdx.x;
+}
+
+// Streams gate/up items b, b + G, ... < n (item numbering of blk_item with
+// n_sh shared items first) with two register buffers.
+__device__ __forceinline__ void gateup_block_items(const DecodeArgs& a, const int* s_tab,
+                                                   const int* s_rt, const uint4* s_x, int n_sh,
+                                                   int n, int b, int G) {
   // fixed trip over pairs of items; padding issues read nothing
   const int mine = b < n ? (n - b + G - 1) / G : 0;
   GuRegs A, B;
@@ -1369,6 +1356,42 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
     if (i1 < n) gu_compute_blk(a, blk_item(a, s_tab, n_sh, i1, a.gu_items, true), s_rt, B, s_x);
   }
 }
+
+// Block launch 1: [router rows | the routing workgroup | n_sw workgroups
+// streaming the shared expert's gate/up items, which need no routing and
+// use the bandwidth the router and the routing leave idle].
+__global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int n_sw) {
+  extern __shared__ __align__(16) char lds[];
+  const int b = blockIdx.x;
+  if (b < a.nb_router) {
+    router_rows_blk(a, b, reinterpret_cast<uint4*>(lds));
+  } else if (b == a.nb_router) {
+    routing(a, lds);
+  } else {
+    uint4* s_x = reinterpret_cast<uint4*>(lds);
+    stage_block_rows(a, s_x);
+    __syncthreads();
+    gateup_block_items(a, nullptr, nullptr, s_x, a.gu_items, a.gu_items, b - a.nb_router - 1,
+                       n_sw);
+  }
+}
+
+// Block gate/up: G persistent workgroups stage the T token rows and the
+// slot table, then stream the routed items with two register buffers.
+__global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
+  extern __shared__ __align__(16) char lds[];
+  uint4* s_x = reinterpret_cast<uint4*>(lds);
+  const int T = min(a.T, kBlockT);
+  int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
+  int* s_rt = s_tab + 1 + 3 * a.max_slots;
+  stage_block_rows(a, s_x);
+  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
+  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
+  __syncthreads();
+  const int ns = min(max(s_tab[0], 0), a.max_slots);
+  gateup_block_items(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
+}
+
 
 struct DnW {
   uint4 w[kDnU];
@@ -1764,10 +1787,12 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
                      d.E <= 16 * kWave && 1 + 3 * L.max_slots <= 1024 &&
                      d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
   if (block) {
-    const uint32_t lds_rt = (uint32_t)(d.T * d.H * 2 > kLdsBytes ? d.T * d.H * 2 : kLdsBytes);
-    launch("route_block_kernel", route_block_kernel, dim3(L.nb_router + 1), dim3(kThreads), lds_rt,
-           s, a);
-    const int ng = (shared ? L.gu_items : 0) + L.max_slots * L.gu_items;
+    const uint32_t lds_x = (uint32_t)(d.T * kXRow * 16);
+    const uint32_t lds_rt = lds_x > (uint32_t)kLdsBytes ? lds_x : (uint32_t)kLdsBytes;
+    const int n_sw = shared ? (L.gu_items < 256 ? L.gu_items : 256) : 0;
+    launch("route_block_kernel", route_block_kernel, dim3(L.nb_router + 1 + n_sw), dim3(kThreads),
+           lds_rt, s, a, n_sw);
+    const int ng = L.max_slots * L.gu_items;
     const int gg = ng < kStreamBlocks ? ng : kStreamBlocks;
     const uint32_t lds_gu =
         (uint32_t)(d.T * kXRow * 16 + sizeof(int) * (1 + 3 * L.max_slots + d.R));
