@@ -249,13 +249,15 @@ def kernel_work(name, w, U, shared=True):
         return "hbm", b
     if name == "gateup_block_kernel":
         # gate/up of the U routed experts, each read once for all the block's
-        # tokens routed to it; h rows written
-        return "hbm", U * gu_expert + T * H * 2 + R * I * 4
+        # tokens routed to it, h rows written; then the shared expert's down
+        # rows for every token
+        b = U * gu_expert + T * H * 2 + R * I * 4
+        if shared:
+            b += dn_expert + T * I * 4 + T * H * 4
+        return "hbm", b
     if name == "down_block_kernel":
-        # down of the U routed experts and the shared one, h rows read, y rows
-        # written
-        rows = R + (T if shared else 0)
-        return "hbm", (U + (1 if shared else 0)) * dn_expert + rows * I * 4 + rows * H * 4
+        # down of the U routed experts, h rows read, y rows written
+        return "hbm", U * dn_expert + R * I * 4 + R * H * 4
     if name == "combine_block_kernel":
         rows = R + (T if shared else 0)
         return "hbm", rows * H * 4 + T * H * 4 + T * w.k * 8

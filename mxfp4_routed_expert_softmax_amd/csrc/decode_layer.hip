@@ -1376,27 +1376,11 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int
   }
 }
 
-// Block gate/up: G persistent workgroups stage the T token rows and the
-// slot table, then stream the routed items with two register buffers.
-__global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
-  extern __shared__ __align__(16) char lds[];
-  uint4* s_x = reinterpret_cast<uint4*>(lds);
-  const int T = min(a.T, kBlockT);
-  int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
-  int* s_rt = s_tab + 1 + 3 * a.max_slots;
-  stage_block_rows(a, s_x);
-  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
-  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
-  __syncthreads();
-  const int ns = min(max(s_tab[0], 0), a.max_slots);
-  gateup_block_items(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
-}
-
-
 struct DnW {
   uint4 w[kDnU];
   uint32_t sc[kDnU];
 };
+
 __device__ __forceinline__ void dn_issue_blk(const DecodeArgs& a, const BlkItem& d, DnW& r,
                                              bool live) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -1509,8 +1493,8 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
   }
 }
 
-// Block down: routed (slot, 32-row group) items slot-major, then the shared
-// expert's groups; workgroup b takes the contiguous stretch
+// Block down: routed (slot, 32-row group) items slot-major; workgroup b
+// takes the contiguous stretch
 // [n b / G, n (b + 1) / G) with two register buffers for the weights. The
 // combine is a launch of its own: combining in the last workgroup to finish
 // a column group put the combine's coherent loads on the tail of this one.
@@ -1522,7 +1506,7 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
   __syncthreads();
   const int ns = min(max(tab[0], 0), a.max_slots);
   const int nr = ns * a.dn_items;
-  const int n = nr + (a.has_shared ? a.dn_items : 0);
+  const int n = nr;  // the shared expert's rows were done in the gate/up launch
   const int b = blockIdx.x;
   const int lo = (int)((long)n * b / G), hi = (int)((long)n * (b + 1) / G);
   if (lo >= hi) return;
@@ -1567,6 +1551,35 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
       }
     }
   }
+}
+
+// Block gate/up: G persistent workgroups stage the T token rows and the
+// slot table, then stream the routed items with two register buffers. The
+// last n_sd workgroups of the grid each take one 32-row group of the shared
+// expert's down rows (its h rows came from the previous launch); dispatched
+// last, they run in the tail of the routed stream.
+__global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
+  extern __shared__ __align__(16) char lds[];
+  if ((int)blockIdx.x >= G) {
+    const BlkItem d = blk_item(a, nullptr, a.dn_items, (int)blockIdx.x - G, a.dn_items, false);
+    DnW A;
+    dn_issue_blk(a, d, A, true);
+    dn_copy_h(a, d, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the weights and the copies
+    __syncthreads();
+    dn_compute_blk(a, d, false, A, reinterpret_cast<const f32x4_t*>(lds));
+    return;
+  }
+  uint4* s_x = reinterpret_cast<uint4*>(lds);
+  const int T = min(a.T, kBlockT);
+  int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
+  int* s_rt = s_tab + 1 + 3 * a.max_slots;
+  stage_block_rows(a, s_x);
+  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
+  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
+  __syncthreads();
+  const int ns = min(max(s_tab[0], 0), a.max_slots);
+  gateup_block_items(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
 }
 
 // Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
@@ -1794,10 +1807,12 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
            lds_rt, s, a, n_sw);
     const int ng = L.max_slots * L.gu_items;
     const int gg = ng < kStreamBlocks ? ng : kStreamBlocks;
+    const int n_sd = shared ? L.dn_items : 0;
     const uint32_t lds_gu =
         (uint32_t)(d.T * kXRow * 16 + sizeof(int) * (1 + 3 * L.max_slots + d.R));
-    launch("gateup_block_kernel", gateup_block_kernel, dim3(gg), dim3(kThreads), lds_gu, s, a, gg);
-    const int nd = (L.max_slots + (shared ? 1 : 0)) * L.dn_items;
+    launch("gateup_block_kernel", gateup_block_kernel, dim3(gg + n_sd), dim3(kThreads), lds_gu, s, a,
+           gg);
+    const int nd = L.max_slots * L.dn_items;
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
     const uint32_t lds_dn = (uint32_t)(1024 * sizeof(int) + d.T * 8 * kDnU * 8 * 16);
     launch("down_block_kernel", down_block_kernel, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
