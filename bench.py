@@ -278,10 +278,15 @@ def kernel_work(name, w, U, shared=True):
             b += gu_expert + T * I * 4
         return "hbm", b
     rows = R + (T if shared else 0)
+    # grouped GEMMs: the flops, and the bytes they cannot avoid (each touched
+    # expert's weights once, the activations once, the outputs once); the
+    # bound is whichever takes longer at its peak
     if name == "gemm_gateup_kernel":
-        return "mfma", rows * 2.0 * 2 * H * I
+        return "gemm", (rows * 2.0 * 2 * H * I,
+                        (U + (1 if shared else 0)) * gu_expert + T * H * 2 + rows * I * 2)
     if name == "gemm_down_kernel":
-        return "mfma", rows * 2.0 * H * I
+        return "gemm", (rows * 2.0 * H * I,
+                        (U + (1 if shared else 0)) * dn_expert + rows * I * 2 + rows * H * 4)
     if name == "router_mfma_kernel":
         return "mfma", T * 2.0 * w.E * H
     return None, None
@@ -347,7 +352,17 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         log(f"[bench] dominant kernel {name}: no algorithmic work model, roofline omitted")
         return None
     # per-launch work averaged over the calls the timed loop made
-    work = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1] for i in range(K)]))
+    if bound == "gemm":
+        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1][0] for i in range(K)]))
+        by = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1][1] for i in range(K)]))
+        # the bound is the resource the work needs longer at its peak
+        bound = "mfma" if fl / (MFMA_16BIT_PEAK_TFLOPS * 1e12) >= by / (HBM_PEAK_GBS * 1e9) \
+            else "hbm"
+        work = fl if bound == "mfma" else by
+        log(f"[bench] {name}: {fl / 1e12:.3f} TFLOP, {by / 1e9:.2f} GB unavoidable -> "
+            f"bound by {bound.upper()}")
+    else:
+        work = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1] for i in range(K)]))
     if bound == "hbm":
         ach = work / (t_ms / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
