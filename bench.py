@@ -44,12 +44,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="decode",
-                    choices=["tiny", "decode", "spec5", "prefill2k_zipf", "prefill16k"])
+                    choices=["tiny", "decode", "spec5", "prefill2k_zipf", "prefill16k",
+                             "draft128"])
     ap.add_argument("--copies", type=int, default=None, help="bank copies to rotate over")
     ap.add_argument("--pool", type=int, default=None, help="distinct token batches")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-loop", action="store_true")
+    ap.add_argument("--verify-sweep", action="store_true",
+                    help="instead of one workload: verification blocks of 2..8 correlated "
+                         "tokens at the decode shape; per block size, time, the union of "
+                         "routed experts and the bytes it costs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 3 plain device copies of BYTES bytes (the reference "
                          "reading for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -83,6 +88,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return 0
+
+    if args.verify_sweep:
+        return verify_sweep(args, M, S, np, torch)
 
     w = S.get(args.config)
     small = w.T <= 16
@@ -217,6 +225,117 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     return 0
 
+
+
+def sweep_kernel_times(M, torch, np, call, n):
+    """Mean duration (us) of each kernel of `call` over n calls, from events the
+    library records at each launch's dispatch begin and end."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    call(0)
+    torch.cuda.synchronize()
+    nl = M.moe_last_call_launches()
+    names = [M.moe_launch_name(i) for i in range(nl)]
+    evs = []
+    for _ in range(n):
+        arr = (ctypes.c_void_p * (2 * nl))()
+        for j in range(2 * nl):
+            e = ctypes.c_void_p()
+            hip.hipEventCreate(ctypes.byref(e))
+            arr[j] = e.value
+        evs.append(arr)
+    try:
+        for i in range(n):
+            M.moe_set_kernel_events(evs[i], nl)
+            call(i)
+        M.moe_set_kernel_events(None, 0)
+        torch.cuda.synchronize()
+        f = ctypes.c_float()
+        dur = np.zeros((n, nl))
+        for i in range(n):
+            for j in range(nl):
+                hip.hipEventElapsedTime(ctypes.byref(f), evs[i][2 * j], evs[i][2 * j + 1])
+                dur[i, j] = f.value * 1e3
+    finally:
+        M.moe_set_kernel_events(None, 0)
+        for arr in evs:
+            for e in arr:
+                hip.hipEventDestroy(e)
+    return {nm: round(float(d), 2) for nm, d in zip(names, dur.mean(axis=0))}
+
+
+def verify_sweep(args, M, S, np, torch):
+    """A verification block of K+1 tokens pays for the union of its tokens'
+    experts (ai.rs article, "The draft head that works and does not pay").
+    For K+1 = 2..8 correlated tokens (block recipe of spec5) at the decode
+    shape: time per block, the mean union |U| of routed experts, and the
+    expert bytes (|U| + 1 shared) x 18.8 MB it reads."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = S.get("spec5")
+    K = args.steps if args.steps is not None else 200
+    W = args.warmup if args.warmup is not None else 20
+    C, P = 4, 16
+    routed_np = S.gen_bank(base, 0)
+    shared_np = S.gen_bank(base, 0, shared=True)
+    keys = ("gate_up_codes", "gate_up_scales", "down_codes", "down_scales")
+    banks = []
+    for c in range(C):
+        banks.append((M.BankTensors(*[torch.from_numpy(routed_np[k]).to(dev) for k in keys]),
+                      M.BankTensors(*[torch.from_numpy(shared_np[k]).to(dev) for k in keys])))
+    del routed_np, shared_np
+    wr = torch.from_numpy(S.gen_router(base, 0).view(np.int16)).to(dev).view(torch.bfloat16)
+    expert_bytes = 3 * base.I * base.H * 17 // 32
+    rows = []
+    for T in range(2, 9):
+        w = S.Workload(f"verify{T}", base.cfg_id, T=T, H=base.H, E=base.E, k=base.k, I=base.I,
+                       exp_lo=base.exp_lo, exp_hi=base.exp_hi, block=T, noise=base.noise)
+        xs = [torch.from_numpy(S.gen_tokens(w, 0, call=i).view(np.int16)).to(dev)
+              .view(torch.bfloat16) for i in range(P)]
+        out = torch.empty((T, w.H), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+        ws = M.workspace(T, w.H, w.I, w.E + 1, w.k + 1, dev)
+        U = []
+        for x in xs:
+            M.moe_router_topk(x, wr, None, w.k, ids, wts, None, ws)
+            U.append(int(torch.unique(ids).numel()))
+        for i in range(W):
+            rd, sd = banks[i % C]
+            M.moe_layer_forward(xs[i % P], wr, None, rd, sd, w.k, out, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            rd, sd = banks[i % C]
+            M.moe_layer_forward(xs[i % P], wr, None, rd, sd, w.k, out, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        per_kernel = sweep_kernel_times(M, torch, np, lambda i: M.moe_layer_forward(
+            xs[i % P], wr, None, banks[i % C][0], banks[i % C][1], w.k, out, ws=ws), 50)
+        u = float(np.mean(U))
+        union = (u + 1) * expert_bytes
+        path = [M.moe_launch_name(i) for i in range(M.moe_last_call_launches())]
+        row = dict(tokens=T, us_per_block=round(us, 2), tokens_per_s=round(T / us * 1e6, 1),
+                   union_routed_experts=round(u, 2), union_bytes=int(union),
+                   bytes_per_token=int(union / T), union_gbs=round(union / us / 1e3, 1),
+                   launches=path, kernel_us=per_kernel)
+        rows.append(row)
+        log(f"[sweep] T={T}: {us:8.2f} us/block, {T / us * 1e6:9,.0f} tokens/s, |U| = {u:5.2f}, "
+            f"{union / 1e6:7.1f} MB union ({union / T / 1e6:6.1f} MB/token) -> "
+            f"{union / us / 1e3:6.0f} GB/s; "
+            + ", ".join(f"{k} {v:.1f}" for k, v in per_kernel.items()))
+        del ws
+    print(json.dumps({"verify_sweep": rows, "decode_shape": {"H": base.H, "E": base.E, "k": base.k,
+                                                             "I": base.I, "shared_experts": 1},
+                      "block_recipe": "x_t = bf16(b + 0.5 n_t), b, n_t ~ N(0,1)^H",
+                      "steps": K, "warmup": W, "bank_copies": C, "token_batches": P}), flush=True)
+    return 0
 
 
 # Algorithmic work per launch of each kernel, from the call's shape and the

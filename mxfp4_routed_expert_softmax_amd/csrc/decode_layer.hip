@@ -1162,9 +1162,11 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
 // items the same way, and the workgroup that completes a column group
 // combines it for every token.
 // ---------------------------------------------------------------------------
-constexpr int kBlockT = 5;
+// The block kernels are instantiated for at most TB = 5 and TB = 8 tokens
+// (the smaller keeps the gate/up workgroups at three a CU).
+constexpr int kBlockT = 8;
 constexpr int kXRow = 4 * kGuLanes * kGuU;  // uint4 per staged token row (H <= 5120)
-constexpr int kBlockXLoads = 16;            // router: T * H / 8 <= 16 * kThreads
+constexpr int kBlockXLoads = 20;            // router: T * H / 8 <= 20 * kThreads
 
 // Gate/up item `it` of the block: items [0, n_sh) are the shared expert's
 // 8-row groups (all T tokens), then (routed slot, 8-row group) pairs,
@@ -1178,7 +1180,26 @@ struct BlkItem {
   bool shared;
 };
 
-__device__ __forceinline__ BlkItem blk_item(const DecodeArgs& a, const int* tab, int n_sh, int it,
+// A small table held across the lanes of a wave: entry i sits in lane
+// i % 64 of word i / 64, and is read with readlane (the index is uniform).
+// It keeps the slot table off LDS and off the path of memory latency.
+struct LaneTable {
+  static constexpr int kMax = 256;  // entries
+  int v[4];
+  __device__ __forceinline__ void load(const int* src, int n) {
+    const int l = lane_id();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = src[min(64 * q + l, n - 1)];
+  }
+  __device__ __forceinline__ int operator[](int i) const {
+    i = min(max(__builtin_amdgcn_readfirstlane(i), 0), kMax - 1);
+    const int w = i < 64 ? v[0] : i < 128 ? v[1] : i < 192 ? v[2] : v[3];
+    return __builtin_amdgcn_readlane(w, i & 63);
+  }
+};
+
+template <int TB, class Tab>
+__device__ __forceinline__ BlkItem blk_item(const DecodeArgs& a, const Tab& tab, int n_sh, int it,
                                             int per, bool gu) {
   const uint32_t crow = (uint32_t)(gu ? a.H : a.I) >> 1, srow = (uint32_t)(gu ? a.H : a.I) >> 5;
   const size_t mat = gu ? 2 * (size_t)a.I : (size_t)a.H;
@@ -1186,11 +1207,11 @@ __device__ __forceinline__ BlkItem blk_item(const DecodeArgs& a, const int* tab,
   const uint8_t* s0 = gu ? a.routed.gu_scales : a.routed.d_scales;
   if (it < n_sh)
     return BlkItem{gu ? a.shared.gu_codes : a.shared.d_codes,
-                   gu ? a.shared.gu_scales : a.shared.d_scales, it, a.R, min(a.T, kBlockT), true};
+                   gu ? a.shared.gu_scales : a.shared.d_scales, it, a.R, min(a.T, TB), true};
   const int q = it - n_sh, sl = q / per, rb = q - sl * per;
   const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + sl], 0), a.routed.E - 1));
   const int row0 = min(max(tab[1 + a.max_slots + sl], 0), a.R);
-  const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, kBlockT));
+  const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, TB));
   return BlkItem{c0 + (size_t)e * mat * crow, s0 + (size_t)e * mat * srow, rb, row0, m, false};
 }
 
@@ -1223,8 +1244,9 @@ __device__ __forceinline__ void gu_issue_blk(const DecodeArgs& a, const BlkItem&
 // comes from the staged block at s_x + t * kXRow. Unrolled over the block
 // (no loop-carried store, so the waits for this item's weights do not also
 // wait for the next item's).
+template <int TB, class Tab>
 __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkItem& d,
-                                               const int* s_rt, const GuRegs& r,
+                                               const Tab& s_rt, const GuRegs& r,
                                                const uint4* s_x) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & (kGuLanes - 1);
@@ -1232,10 +1254,10 @@ __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkIte
   const int kc = a.H >> 5;
   const uint32_t sh = 8u * (j & 3);
   constexpr int P = kGuLanes * kGuU;
-  const uint4* xt[kBlockT];
-  float ag[kBlockT], au[kBlockT];
+  const uint4* xt[TB];
+  float ag[TB], au[TB];
 #pragma unroll
-  for (int i = 0; i < kBlockT; ++i) {
+  for (int i = 0; i < TB; ++i) {
     const int t = i >= d.m ? 0 : d.shared ? i : min(max(s_rt[d.row0 + i], 0), a.T - 1);
     xt[i] = s_x + t * kXRow;
     ag[i] = au[i] = 0.0f;
@@ -1261,7 +1283,7 @@ __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkIte
         wu[4 * q + 3] = fp4x2_to_bf16<3>(uw[q]);
       }
 #pragma unroll
-      for (int i = 0; i < kBlockT; ++i) {
+      for (int i = 0; i < TB; ++i) {
         if (i < d.m) {
           const uint4* xv = xt[i] + c;
           float pg = 0.0f, pu = 0.0f;
@@ -1282,7 +1304,7 @@ __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkIte
     }
   }
 #pragma unroll
-  for (int i = 0; i < kBlockT; ++i) {
+  for (int i = 0; i < TB; ++i) {
     if (i < d.m) {
       const float g = group_sum<kGuLanes>(ag[i]), u = group_sum<kGuLanes>(au[i]);
       if (j == 0 && n < a.I) a.h[(size_t)(d.row0 + i) * a.I + n] = silu_mul(g, u);
@@ -1329,7 +1351,7 @@ __device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
 // The block's T token rows into LDS (row t at s_x + t * kXRow, chunk-
 // transposed like the one-token row).
 __device__ __forceinline__ void stage_block_rows(const DecodeArgs& a, uint4* s_x) {
-  const int T = min(a.T, kBlockT);
+  const int T = min(a.T, kBlockT);  // the host keeps T within the instantiation's TB
   const int nv = a.H >> 3;
   stage_rows<uint4>(
       T * nv, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
@@ -1341,25 +1363,27 @@ __device__ __forceinline__ void stage_block_rows(const DecodeArgs& a, uint4* s_x
 
 // Streams gate/up items b, b + G, ... < n (item numbering of blk_item with
 // n_sh shared items first) with two register buffers.
-__device__ __forceinline__ void gateup_block_items(const DecodeArgs& a, const int* s_tab,
-                                                   const int* s_rt, const uint4* s_x, int n_sh,
+template <int TB, class Tab>
+__device__ __forceinline__ void gateup_block_items(const DecodeArgs& a, const Tab& s_tab,
+                                                   const Tab& s_rt, const uint4* s_x, int n_sh,
                                                    int n, int b, int G) {
   // fixed trip over pairs of items; padding issues read nothing
   const int mine = b < n ? (n - b + G - 1) / G : 0;
   GuRegs A, B;
-  gu_issue_blk(a, blk_item(a, s_tab, n_sh, b < n ? b : 0, a.gu_items, true), A, b < n);
+  gu_issue_blk(a, blk_item<TB>(a, s_tab, n_sh, b < n ? b : 0, a.gu_items, true), A, b < n);
   for (int kk = 0; kk < mine; kk += 2) {
     const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
-    gu_issue_blk(a, blk_item(a, s_tab, n_sh, i1 < n ? i1 : i0, a.gu_items, true), B, i1 < n);
-    gu_compute_blk(a, blk_item(a, s_tab, n_sh, i0, a.gu_items, true), s_rt, A, s_x);
-    gu_issue_blk(a, blk_item(a, s_tab, n_sh, i2 < n ? i2 : i0, a.gu_items, true), A, i2 < n);
-    if (i1 < n) gu_compute_blk(a, blk_item(a, s_tab, n_sh, i1, a.gu_items, true), s_rt, B, s_x);
+    gu_issue_blk(a, blk_item<TB>(a, s_tab, n_sh, i1 < n ? i1 : i0, a.gu_items, true), B, i1 < n);
+    gu_compute_blk<TB>(a, blk_item<TB>(a, s_tab, n_sh, i0, a.gu_items, true), s_rt, A, s_x);
+    gu_issue_blk(a, blk_item<TB>(a, s_tab, n_sh, i2 < n ? i2 : i0, a.gu_items, true), A, i2 < n);
+    if (i1 < n) gu_compute_blk<TB>(a, blk_item<TB>(a, s_tab, n_sh, i1, a.gu_items, true), s_rt, B, s_x);
   }
 }
 
 // Block launch 1: [router rows | the routing workgroup | n_sw workgroups
 // streaming the shared expert's gate/up items, which need no routing and
 // use the bandwidth the router and the routing leave idle].
+template <int TB>
 __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int n_sw) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x;
@@ -1371,8 +1395,9 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int
     uint4* s_x = reinterpret_cast<uint4*>(lds);
     stage_block_rows(a, s_x);
     __syncthreads();
-    gateup_block_items(a, nullptr, nullptr, s_x, a.gu_items, a.gu_items, b - a.nb_router - 1,
-                       n_sw);
+    const int* none = nullptr;
+    gateup_block_items<TB>(a, none, none, s_x, a.gu_items, a.gu_items, b - a.nb_router - 1,
+                           n_sw);
   }
 }
 
@@ -1432,6 +1457,7 @@ __device__ __forceinline__ void dn_copy_h(const DecodeArgs& a, const BlkItem& d,
 // for the combine in this launch. `fresh`: the slot's h rows were just
 // copied (before the kDnIssueLoads loads of the next item's weights), so
 // wait for the copies and make them visible to every wave first.
+template <int TB>
 __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkItem& d, bool fresh,
                                                const DnW& r, const f32x4_t* s_h) {
   if (fresh) {
@@ -1444,9 +1470,9 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
   const int kc = a.I >> 5;
   const uint32_t sh = 8u * (j & 3);
   constexpr int P = 8 * kDnU;
-  float acc[kBlockT];
+  float acc[TB];
 #pragma unroll
-  for (int i = 0; i < kBlockT; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < TB; ++i) acc[i] = 0.0f;
   // each 16-byte chunk of weights converted to fp32 once, used by every row
 #pragma unroll
   for (int u = 0; u < kDnU; ++u) {
@@ -1463,7 +1489,7 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
         wf[4 * q + 3] = fp4x2_to_f32<3>(ww[q]);
       }
 #pragma unroll
-      for (int i = 0; i < kBlockT; ++i) {
+      for (int i = 0; i < TB; ++i) {
         if (i < d.m) {
           const f32x4_t* hv = s_h + i * kHRow + ch;
           float pd = 0.0f;
@@ -1485,7 +1511,7 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
     }
   }
 #pragma unroll
-  for (int i = 0; i < kBlockT; ++i) {
+  for (int i = 0; i < TB; ++i) {
     if (i < d.m) {
       const float v = group_sum<8>(acc[i]);
       if (j == 0 && n < a.H) cst(a.y + (size_t)(d.row0 + i) * a.H + n, v);
@@ -1498,12 +1524,13 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
 // [n b / G, n (b + 1) / G) with two register buffers for the weights. The
 // combine is a launch of its own: combining in the last workgroup to finish
 // a column group put the combine's coherent loads on the tail of this one.
+template <int TB>
 __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
-  int* tab = reinterpret_cast<int*>(lds);
-  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int));
-  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) tab[i] = a.tab[i];
-  __syncthreads();
+  // LDS holds only the staged h rows; the slot table rides across the lanes
+  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds);
+  LaneTable tab;
+  tab.load(a.tab, 1 + 3 * a.max_slots);
   const int ns = min(max(tab[0], 0), a.max_slots);
   const int nr = ns * a.dn_items;
   const int n = nr;  // the shared expert's rows were done in the gate/up launch
@@ -1512,16 +1539,15 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
   if (lo >= hi) return;
   // item it: routed items first, so the shared groups follow at offset nr
   auto item = [&](int it) {
-    return it < nr ? blk_item(a, tab, 0, it, a.dn_items, false)
-                   : blk_item(a, tab, a.dn_items, it - nr, a.dn_items, false);
+    return it < nr ? blk_item<TB>(a, tab, 0, it, a.dn_items, false)
+                   : blk_item<TB>(a, tab, a.dn_items, it - nr, a.dn_items, false);
   };
   auto slot_of = [&](int it) { return it < nr ? it / a.dn_items : ns; };
   // The slot's h rows are copied into LDS when an item's slot differs from
   // the one staged (once or twice per workgroup: its items are a contiguous
   // stretch), each copy issued between the item's weights and the next
   // item's, so waiting for it never waits for the next item's weights.
-  const uint32_t s_h_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds +
-                           1024 * sizeof(int);
+  const uint32_t s_h_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
   auto restage = [&](int it, int& staged) {
     __syncthreads();  // every wave is done reading the staged rows
     dn_copy_h(a, item(it), s_h_lds);
@@ -1535,7 +1561,7 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
   for (int i0 = lo; i0 < hi; i0 += 2) {
     const int i1 = i0 + 1, i2 = i0 + 2;
     dn_issue_blk(a, item(i1 < hi ? i1 : i0), B, i1 < hi);
-    dn_compute_blk(a, item(i0), fresh, A, s_h);
+    dn_compute_blk<TB>(a, item(i0), fresh, A, s_h);
     fresh = false;
     if (i1 < hi && slot_of(i1) != staged) {
       restage(i1, staged);
@@ -1543,7 +1569,7 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
     }
     dn_issue_blk(a, item(i2 < hi ? i2 : i0), A, i2 < hi);
     if (i1 < hi) {
-      dn_compute_blk(a, item(i1), fresh, B, s_h);
+      dn_compute_blk<TB>(a, item(i1), fresh, B, s_h);
       fresh = false;
       if (i2 < hi && slot_of(i2) != staged) {
         restage(i2, staged);
@@ -1558,28 +1584,43 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
 // last n_sd workgroups of the grid each take one 32-row group of the shared
 // expert's down rows (its h rows came from the previous launch); dispatched
 // last, they run in the tail of the routed stream.
+template <int TB>
 __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
   if ((int)blockIdx.x >= G) {
-    const BlkItem d = blk_item(a, nullptr, a.dn_items, (int)blockIdx.x - G, a.dn_items, false);
+    const int* none = nullptr;
+    const BlkItem d = blk_item<TB>(a, none, a.dn_items, (int)blockIdx.x - G, a.dn_items, false);
     DnW A;
     dn_issue_blk(a, d, A, true);
     dn_copy_h(a, d, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the weights and the copies
     __syncthreads();
-    dn_compute_blk(a, d, false, A, reinterpret_cast<const f32x4_t*>(lds));
+    dn_compute_blk<TB>(a, d, false, A, reinterpret_cast<const f32x4_t*>(lds));
     return;
   }
   uint4* s_x = reinterpret_cast<uint4*>(lds);
-  const int T = min(a.T, kBlockT);
-  int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
-  int* s_rt = s_tab + 1 + 3 * a.max_slots;
   stage_block_rows(a, s_x);
-  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
-  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
-  __syncthreads();
-  const int ns = min(max(s_tab[0], 0), a.max_slots);
-  gateup_block_items(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
+  if constexpr (TB <= 5) {
+    // the slot table and row map in LDS too: their reads sit on the path of
+    // every item's weight addresses
+    const int T = min(a.T, TB);
+    int* s_tab = reinterpret_cast<int*>(lds + (size_t)T * kXRow * 16);
+    int* s_rt = s_tab + 1 + 3 * a.max_slots;
+    for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) s_tab[i] = a.tab[i];
+    for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
+    __syncthreads();
+    const int ns = min(max(s_tab[0], 0), a.max_slots);
+    gateup_block_items<TB>(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
+  } else {
+    // LDS holds only the T token rows (at most 80 KB: two workgroups a CU);
+    // the slot table and row map ride in registers across each wave's lanes
+    LaneTable tab, rt;
+    tab.load(a.tab, 1 + 3 * a.max_slots);
+    rt.load(a.row_token, a.R);
+    __syncthreads();
+    const int ns = min(max(tab[0], 0), a.max_slots);
+    gateup_block_items<TB>(a, tab, rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
+  }
 }
 
 // Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
@@ -1720,6 +1761,35 @@ void launch_chain(const DecodeArgs& a, const DecodeLayout& L, bool ffn, bool sha
                      a, ffn ? 0 : 1);
 }
 
+// Persistent grids no larger than the workgroups the CUs hold at once:
+// three a CU by registers, fewer where the LDS a workgroup needs allows less.
+int resident_grid(uint32_t lds_bytes) {
+  const int by_lds = lds_bytes ? (int)(163840u / lds_bytes) : 3;
+  return 256 * (by_lds < 3 ? (by_lds < 1 ? 1 : by_lds) : 3);
+}
+
+template <int TB>
+void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch& d, bool shared,
+                  hipStream_t s) {
+  const uint32_t lds_x = (uint32_t)(d.T * kXRow * 16);
+  const uint32_t lds_rt = lds_x > (uint32_t)kLdsBytes ? lds_x : (uint32_t)kLdsBytes;
+  const int n_sw = shared ? (L.gu_items < 256 ? L.gu_items : 256) : 0;
+  launch("route_block_kernel", route_block_kernel<TB>, dim3(L.nb_router + 1 + n_sw),
+         dim3(kThreads), lds_rt, s, a, n_sw);
+  const uint32_t lds_gu =
+      lds_x + (TB <= 5 ? (uint32_t)(sizeof(int) * (1 + 3 * L.max_slots + d.R)) : 0u);
+  const int ng = L.max_slots * L.gu_items, rg = resident_grid(lds_gu);
+  const int gg = ng < rg ? ng : rg;
+  const int n_sd = shared ? L.dn_items : 0;
+  launch("gateup_block_kernel", gateup_block_kernel<TB>, dim3(gg + n_sd), dim3(kThreads), lds_gu,
+         s, a, gg);
+  const uint32_t lds_dn = (uint32_t)(d.T * 8 * kDnU * 8 * 16);
+  const int nd = L.max_slots * L.dn_items, rd = resident_grid(lds_dn);
+  const int gd = nd < rd ? nd : rd;
+  launch("down_block_kernel", down_block_kernel<TB>, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
+  launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
+}
+
 void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   const bool ffn = d.ffn_mode != 0;
   const bool shared = d.has_shared && !ffn;
@@ -1797,26 +1867,13 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   // gate/up and down launches over the union of the block's experts.
   const bool block = d.T >= 2 && d.T <= kBlockT && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
                      d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU &&
-                     d.E <= 16 * kWave && 1 + 3 * L.max_slots <= 1024 &&
-                     d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
+                     d.E <= 16 * kWave && 1 + 3 * L.max_slots <= LaneTable::kMax &&
+                     d.R <= LaneTable::kMax && d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
   if (block) {
-    const uint32_t lds_x = (uint32_t)(d.T * kXRow * 16);
-    const uint32_t lds_rt = lds_x > (uint32_t)kLdsBytes ? lds_x : (uint32_t)kLdsBytes;
-    const int n_sw = shared ? (L.gu_items < 256 ? L.gu_items : 256) : 0;
-    launch("route_block_kernel", route_block_kernel, dim3(L.nb_router + 1 + n_sw), dim3(kThreads),
-           lds_rt, s, a, n_sw);
-    const int ng = L.max_slots * L.gu_items;
-    const int gg = ng < kStreamBlocks ? ng : kStreamBlocks;
-    const int n_sd = shared ? L.dn_items : 0;
-    const uint32_t lds_gu =
-        (uint32_t)(d.T * kXRow * 16 + sizeof(int) * (1 + 3 * L.max_slots + d.R));
-    launch("gateup_block_kernel", gateup_block_kernel, dim3(gg + n_sd), dim3(kThreads), lds_gu, s, a,
-           gg);
-    const int nd = L.max_slots * L.dn_items;
-    const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
-    const uint32_t lds_dn = (uint32_t)(1024 * sizeof(int) + d.T * 8 * kDnU * 8 * 16);
-    launch("down_block_kernel", down_block_kernel, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
-    launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
+    if (d.T <= 5)
+      launch_block<5>(a, L, d, shared, s);
+    else
+      launch_block<8>(a, L, d, shared, s);
     return;
   }
   if (one)

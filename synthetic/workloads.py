@@ -74,6 +74,13 @@ WORKLOADS: dict[str, Workload] = {
         Workload("prefill16k", 4, T=16384, H=5120, E=384, k=6, I=2304,
                  exp_lo=-8, exp_hi=-4,
                  desc="16384-token prefill, uniform router"),
+        # The draft head's MoE: 128 routed experts, blocks of 5. Its hidden
+        # and intermediate sizes, top-k and shared expert are taken equal to
+        # the main layer's (the pages give only the expert count and call
+        # its layers full blocks of the main model).
+        Workload("draft128", 5, T=5, H=5120, E=128, k=6, I=2304, exp_lo=-8, exp_hi=-4,
+                 block=5,
+                 desc="draft-head MoE: 5-token block, 128 experts top-6 + 1 shared"),
     ]
 }
 

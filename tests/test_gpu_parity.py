@@ -301,14 +301,14 @@ def _selected_bank(w, x, wr, bias):
     return S.gen_bank(w, 0, experts=sel), sel
 
 
-@pytest.mark.parametrize("name", ["decode", "spec5"])
+@pytest.mark.parametrize("name", ["decode", "spec5", "draft128"])
 def test_layer_small_batch_real_shape(name):
     w = S.get(name)
     x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
     routed, sel = _selected_bank(w, x, wr, None)
     shared = S.gen_bank(w, 0, shared=True)
-    if name == "spec5":
-        print(f"spec5 union of routed experts: {len(sel)} of {w.T * w.k}")
+    if w.T > 1:
+        print(f"{name} union of routed experts: {len(sel)} of {w.T * w.k}")
     _layer_parity(w, x, wr, None, routed, shared)
 
 
@@ -365,6 +365,8 @@ BLOCKS = [
     S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
     S.Workload("blk_narrow", 97, T=4, H=256, E=16, k=2, I=256, exp_lo=-6, exp_hi=-3),
     S.Workload("blk_five_wide", 98, T=5, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_six", 100, T=6, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_eight_wide", 101, T=8, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
 ]
 
 # kernels of the block path
@@ -380,6 +382,21 @@ def test_layer_block_path(w, variant):
     if variant == "no_shared_with_bias":
         bias, shared = np.linspace(-0.5, 0.5, w.E).astype(np.float32), None
     err = _layer_parity(w, d["x"], d["w_router"], bias, d["routed"], shared)
+    assert _launches() == BLOCK_PATH
+    assert err < HP.FP32_TOL
+
+
+def test_layer_block_of_eight_real_shape():
+    # the largest block the streaming path takes, at the real layer shape,
+    # correlated tokens as in the verification sweep
+    base = S.get("spec5")
+    w = S.Workload("verify8", base.cfg_id, T=8, H=base.H, E=base.E, k=base.k, I=base.I,
+                   exp_lo=base.exp_lo, exp_hi=base.exp_hi, block=8, noise=base.noise)
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    routed, sel = _selected_bank(w, x, wr, None)
+    shared = S.gen_bank(w, 0, shared=True)
+    print(f"verify8 union of routed experts: {len(sel)} of {w.T * w.k}")
+    err = _layer_parity(w, x, wr, None, routed, shared)
     assert _launches() == BLOCK_PATH
     assert err < HP.FP32_TOL
 
