@@ -1863,9 +1863,13 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
            gd);
     return;
   }
-  // A block of 2..kBlockT tokens: router + routing, then the streaming
-  // gate/up and down launches over the union of the block's experts.
-  const bool block = d.T >= 2 && d.T <= kBlockT && !ffn && (d.H >> 5) <= kGuLanes * kGuU &&
+  // A block of 2..5 or 8 tokens: router + routing, then the streaming
+  // gate/up and down launches over the union of the block's experts. At 6
+  // and 7 tokens the instantiation for 8 measured no faster than the chain
+  // below at the real shape (164.5 and 184.0 us against 165.2 and 166.3 us),
+  // so those take the chain.
+  const bool block = d.T >= 2 && d.T <= kBlockT && d.T != 6 && d.T != 7 && !ffn &&
+                     (d.H >> 5) <= kGuLanes * kGuU &&
                      d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU &&
                      d.E <= 16 * kWave && 1 + 3 * L.max_slots <= LaneTable::kMax &&
                      d.R <= LaneTable::kMax && d.T * (d.H >> 3) <= kBlockXLoads * kThreads;

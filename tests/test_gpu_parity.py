@@ -365,7 +365,6 @@ BLOCKS = [
     S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
     S.Workload("blk_narrow", 97, T=4, H=256, E=16, k=2, I=256, exp_lo=-6, exp_hi=-3),
     S.Workload("blk_five_wide", 98, T=5, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
-    S.Workload("blk_six", 100, T=6, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
     S.Workload("blk_eight_wide", 101, T=8, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
 ]
 
