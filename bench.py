@@ -36,6 +36,10 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s; decode HBM GB/s vs peak; prefill MFMA util (1 MI355X)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_16BIT_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the rate of fp8 x fp4 scaled MFMA)
+# kernels whose MFMA peak is not the 16-bit one
+MFMA_PEAK_OF = {"gemm_mx_gateup_kernel": MFMA_FP8_PEAK_TFLOPS,
+                "gemm_mx_down_kernel": MFMA_FP8_PEAK_TFLOPS}
 
 
 def parse():
@@ -55,6 +59,10 @@ def parse():
                     help="instead of one workload: verification blocks of 2..8 correlated "
                          "tokens at the decode shape; per block size, time, the union of "
                          "routed experts and the bytes it costs")
+    ap.add_argument("--mxfp8-act", action="store_true",
+                    help="time moe_layer_forward_mxfp8_act, the opt-in mode with MXFP8 "
+                         "activations on the scaled fp8 x fp4 MFMA (an approximation of the "
+                         "layer; its error against the exact layer is reported)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 3 plain device copies of BYTES bytes (the reference "
                          "reading for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -133,7 +141,8 @@ def main() -> int:
         f"({C} bank copies, {P} token batches)")
 
     # Pre-marshalled arguments: the timed loop makes one C call per step.
-    fwd = lib.moe_layer_forward
+    fwd_name = "moe_layer_forward_mxfp8_act" if args.mxfp8_act else "moe_layer_forward"
+    fwd = getattr(lib, fwd_name)
     sh = stream.cuda_stream
     ws_n = ws.numel()
     import ctypes
@@ -150,7 +159,7 @@ def main() -> int:
     def step(i):
         st = fwd(*step_args[i % n_args])
         if st != 0:
-            raise M.MoeError("moe_layer_forward", st, M.status_str(st))
+            raise M.MoeError(fwd_name, st, M.status_str(st))
 
     for i in range(W):
         step(i)
@@ -180,8 +189,28 @@ def main() -> int:
                                ids, wts, ws, P, C, W, K, stream)
     # ---- CPU baseline: the fp64 oracle on the host -------------------------
     cpu = None
+    mx_err = None
+    if args.mxfp8_act:
+        # error of the mode against the exact layer on a few tokens of the
+        # last timed batch (the oracle's own rounding reproduces the mode)
+        from oracle import moe as O
+        from oracle import mxfp8_act as MXO
+        step(W + K - 1)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        xb = xs_np[(W + K - 1) % P]
+        tok = sorted(set([0, w.T // 3, w.T // 2, w.T - 1]))
+        ex = O.layer(xb, S.gen_router(w, 0), bias_np, routed_np, shared_np, w.k, tokens=tok)["out"]
+        mx = MXO.layer_mx(xb, S.gen_router(w, 0), bias_np, routed_np, shared_np, w.k,
+                          tokens=tok)["out"]
+        rel = lambda a, b: float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        mx_err = dict(tokens=tok, rel_l2_vs_exact_layer=round(rel(got[tok], ex), 5),
+                      rel_l2_vs_mode_oracle=round(rel(got[tok], mx), 6))
+        log(f"[bench] mxfp8-act error on tokens {tok}: {mx_err}")
     if not args.no_cpu_baseline:
         from oracle import moe as O
+        from oracle import mxfp8_act as MXO
+        layer_fn = MXO.layer_mx if args.mxfp8_act else O.layer
         try:
             from threadpoolctl import threadpool_info
             cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -193,7 +222,7 @@ def main() -> int:
         while t_cpu < args.cpu_seconds and calls < P:
             xb = xs_np[calls % P][:Tcpu] if w.T <= 16 else xs_np[0][calls:calls + 1]
             ta = time.perf_counter()
-            O.layer(xb, wr_np, bias_np, routed_np, shared_np, w.k)
+            layer_fn(xb, wr_np, bias_np, routed_np, shared_np, w.k)
             t_cpu += time.perf_counter() - ta
             n_tok += xb.shape[0]
             calls += 1
@@ -214,14 +243,17 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 x mxfp4 -> fp32",
+        "dtype": "mxfp8 x mxfp4 -> fp32" if args.mxfp8_act else "bf16 x mxfp4 -> fp32",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "intermediate": w.I, "shared_experts": 1,
-                   "bank_copies": C, "token_batches": P},
+                   "bank_copies": C, "token_batches": P,
+                   "expert_activations": "mxfp8" if args.mxfp8_act else "bf16/fp16/fp32"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if mx_err is not None:
+        line["mxfp8_act_error"] = mx_err
     print(json.dumps(line), flush=True)
     return 0
 
@@ -406,6 +438,17 @@ def kernel_work(name, w, U, shared=True):
     if name == "gemm_down_kernel":
         return "gemm", (rows * 2.0 * H * I,
                         (U + (1 if shared else 0)) * dn_expert + rows * I * 2 + rows * H * 4)
+    if name == "gemm_mx_gateup_kernel":
+        # activations and h at one byte plus one scale byte per 32
+        return "gemm", (rows * 2.0 * 2 * H * I,
+                        (U + (1 if shared else 0)) * gu_expert + T * H * 33 // 32
+                        + rows * I * 33 // 32)
+    if name == "gemm_mx_down_kernel":
+        return "gemm", (rows * 2.0 * H * I,
+                        (U + (1 if shared else 0)) * dn_expert + rows * I * 33 // 32
+                        + rows * H * 4)
+    if name == "quant_mxfp8_kernel":
+        return "hbm", T * H * 2 + T * H * 33 // 32
     if name == "router_mfma_kernel":
         return "mfma", T * 2.0 * w.E * H
     return None, None
@@ -475,8 +518,8 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         fl = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1][0] for i in range(K)]))
         by = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1][1] for i in range(K)]))
         # the bound is the resource the work needs longer at its peak
-        bound = "mfma" if fl / (MFMA_16BIT_PEAK_TFLOPS * 1e12) >= by / (HBM_PEAK_GBS * 1e9) \
-            else "hbm"
+        mpeak = MFMA_PEAK_OF.get(name, MFMA_16BIT_PEAK_TFLOPS)
+        bound = "mfma" if fl / (mpeak * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm"
         work = fl if bound == "mfma" else by
         log(f"[bench] {name}: {fl / 1e12:.3f} TFLOP, {by / 1e9:.2f} GB unavoidable -> "
             f"bound by {bound.upper()}")
@@ -490,7 +533,7 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
             f"{ach:,.0f} GB/s")
     else:
         ach = work / (t_ms / 1e3) / 1e12
-        peak, unit = MFMA_16BIT_PEAK_TFLOPS, "TFLOP/s"
+        peak, unit = MFMA_PEAK_OF.get(name, MFMA_16BIT_PEAK_TFLOPS), "TFLOP/s"
         log(f"[bench] {name}: {t_ms:.3f} ms/launch, {work / 1e12:.3f} TFLOP -> "
             f"{ach:,.1f} TFLOP/s")
     return dict(bound=bound, achieved=round(ach, 1), peak=peak, unit=unit,

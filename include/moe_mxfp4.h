@@ -206,6 +206,56 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16,
                       int32_t* topk_ids_out, float* topk_w_out,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Opt-in mode with MXFP8 activations on the scaled matrix cores.
+ *
+ * The reference model runs its linear layers in fp8 with block scales and
+ * activations rounded on the fly (llama.cpp discussion #28766, "Is it
+ * supported?": a dynamic activation scheme with ue8m0 scales); the pages
+ * also tabulate what that rounding costs against full precision, about
+ * 1.45 % relative error for one fp8 linear layer (ai.rs article on
+ * DeepSeek-V4.1-Flash, "What remains is the reference rounding itself").
+ * This mode takes the same kind of rounding for the expert FFNs so that the
+ * gfx950 scaled MFMA can multiply E4M3 activations by the bank's E2M1 codes
+ * as stored (no weight conversion). It is an approximation of the layer,
+ * not the layer: its results differ from moe_layer_forward by the
+ * activation rounding, a few percent relative, and it is selected only by
+ * calling the entry points below.
+ *
+ * The rounding (OCP Microscaling v1.0 conversion, the reading taken where
+ * the pages are silent): per block of 32 consecutive values, scale byte
+ * s = clamp(floor(log2(max |v|)) - 8, -127, 127) + 127 (an all-zero block
+ * takes s = 0); each value v becomes the E4M3 code nearest to
+ * v / 2^(s - 127), ties to even, magnitudes above 448 clamped to 448, the
+ * sign kept (a negative value that rounds to zero gives 0x80).
+ */
+
+/*
+ * MXFP8 rounding of bf16 rows: codes[t][h] (E4M3 byte) and
+ * scales[t][h / 32] (E8M0 byte) of x_bf16 [T][H]. H a multiple of 32;
+ * x_bf16 and codes 16-byte aligned. Bitwise a pure function of x.
+ */
+int moe_quantize_mxfp8(const void* x_bf16, int T, int H, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream);
+
+/*
+ * moe_layer_forward in the MXFP8-activation mode. Arguments, ownership,
+ * ordering, determinism and the routing (router, top-k, weights and
+ * bucketing on the exact bf16 x) are those of moe_layer_forward. The expert
+ * FFNs of the routed and the shared expert take x rounded to MXFP8 per row
+ * (blocks of 32 along H) and round h = silu(g) * u to MXFP8 per row (blocks
+ * of 32 along I) before the down product; every product sums in fp32. Every
+ * T runs the grouped GEMM (the mode is meant for prefill).
+ * Needs H and I multiples of 256 and 128, H, I <= 8192, T*H < 2^31 and
+ * (T*k + T)*I < 2^31, else MOE_ERR_UNSUPPORTED. moe_workspace_bytes covers
+ * its workspace.
+ */
+int moe_layer_forward_mxfp8_act(const void* x_bf16, const void* w_router_bf16,
+                                const float* logit_bias, const moe_mxfp4_bank* routed,
+                                const moe_mxfp4_bank* shared, int T, int k, float* out,
+                                int32_t* topk_ids_out, float* topk_w_out,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

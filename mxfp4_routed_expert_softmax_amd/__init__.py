@@ -21,7 +21,9 @@ from ._lib import (  # noqa: F401
     moe_last_call_launches,
     moe_launch_name,
     moe_layer_forward,
+    moe_layer_forward_mxfp8_act,
     moe_permute,
+    moe_quantize_mxfp8,
     moe_router_topk,
     moe_set_kernel_events,
     moe_workspace_bytes,

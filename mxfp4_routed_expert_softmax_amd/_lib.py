@@ -56,6 +56,9 @@ _SIGS = {
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_layer_forward": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank), _I, _I,
                                 _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_mxfp8_act": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank),
+                                          _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_quantize_mxfp8": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_set_kernel_events": (_I, [_P, _I]),
     "moe_last_call_launches": (_I, []),
     "moe_launch_name": (ctypes.c_char_p, [_I]),
@@ -241,8 +244,8 @@ def moe_combine(y_rows, inv_row, topk_w, y_shared, out, stream=None):
     _check("moe_combine", st)
 
 
-def moe_layer_forward(x, w_router, logit_bias, routed: BankTensors, shared: BankTensors | None,
-                      k, out, topk_ids_out=None, topk_w_out=None, ws=None, stream=None):
+def _layer(fn, x, w_router, logit_bias, routed, shared, k, out, topk_ids_out, topk_w_out, ws,
+           stream):
     import torch
     _need(x, "x", _bf16_types(), 2)
     _need(w_router, "w_router", _bf16_types(), 2)
@@ -250,12 +253,37 @@ def moe_layer_forward(x, w_router, logit_bias, routed: BankTensors, shared: Bank
     if logit_bias is not None:
         _need(logit_bias, "logit_bias", (torch.float32,))
     T = x.shape[0]
-    st = lib().moe_layer_forward(
+    st = getattr(lib(), fn)(
         _ptr(x), _ptr(w_router), _ptr(logit_bias), ctypes.byref(routed.struct),
         None if shared is None else ctypes.byref(shared.struct), T, k, _ptr(out),
         _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, x))
-    _check("moe_layer_forward", st)
+    _check(fn, st)
+
+
+def moe_layer_forward(x, w_router, logit_bias, routed: BankTensors, shared: BankTensors | None,
+                      k, out, topk_ids_out=None, topk_w_out=None, ws=None, stream=None):
+    _layer("moe_layer_forward", x, w_router, logit_bias, routed, shared, k, out, topk_ids_out,
+           topk_w_out, ws, stream)
+
+
+def moe_layer_forward_mxfp8_act(x, w_router, logit_bias, routed: BankTensors,
+                                shared: BankTensors | None, k, out, topk_ids_out=None,
+                                topk_w_out=None, ws=None, stream=None):
+    _layer("moe_layer_forward_mxfp8_act", x, w_router, logit_bias, routed, shared, k, out,
+           topk_ids_out, topk_w_out, ws, stream)
+
+
+def moe_quantize_mxfp8(x, codes, scales, stream=None):
+    import torch
+    _need(x, "x", _bf16_types(), 2)
+    _need(codes, "codes", (torch.uint8,))
+    _need(scales, "scales", (torch.uint8,))
+    T, H = x.shape
+    if codes.numel() != T * H or scales.numel() != T * (H // 32):
+        raise ValueError("codes must hold T*H bytes and scales T*H/32")
+    st = lib().moe_quantize_mxfp8(_ptr(x), T, H, _ptr(codes), _ptr(scales), _stream(stream, x))
+    _check("moe_quantize_mxfp8", st)
 
 
 def moe_set_kernel_events(events, n: int) -> None:

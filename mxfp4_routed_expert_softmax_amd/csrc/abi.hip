@@ -89,7 +89,9 @@ LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
   L.perm = c.take<char>(permute_ws_bytes(T, k, E));
   const size_t gemv = align_up(R * I * sizeof(float)) + align_up((size_t)T * I * sizeof(float));
   const size_t gemm = gemm_ws_bytes(T, H, I, E, (int)R, true);
-  char* ffn = c.take<char>(gemv > gemm ? gemv : gemm);
+  const size_t mx = gemm_mx_ws_bytes(T, H, I, E, (int)R, true);
+  const size_t big = gemm > mx ? gemm : mx;
+  char* ffn = c.take<char>(gemv > big ? gemv : big);
   L.ffn = ffn;
   L.h = reinterpret_cast<float*>(ffn);
   L.h_sh = reinterpret_cast<float*>(ffn ? ffn + align_up(R * I * sizeof(float)) : nullptr);
@@ -276,10 +278,29 @@ int moe_combine(const float* y_rows, const int32_t* inv_row, const float* topk_w
   return launch_status();
 }
 
-int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
-                      const moe_mxfp4_bank* routed, const moe_mxfp4_bank* shared, int T, int k,
-                      float* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                      size_t ws_bytes, hipStream_t stream) {
+int moe_quantize_mxfp8(const void* x_bf16, int T, int H, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream) {
+  begin_call();
+  if (T < 0 || H <= 0 || H % 32) return MOE_ERR_INVALID_ARG;
+  if ((long long)T * H >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !codes || !scales || !aligned16(x_bf16) || !aligned16(codes))
+    return MOE_ERR_INVALID_ARG;
+  launch_quant_mxfp8(static_cast<const uint16_t*>(x_bf16), (long)T * H / 32, codes, scales, stream);
+  return launch_status();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both layer entry points: the default mode (exact weights, bf16 / fp32
+// activations; few tokens take the persistent kernels) and the MXFP8-
+// activation mode (every T on the grouped scaled-MFMA GEMM).
+int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
+                  const moe_mxfp4_bank* routed, const moe_mxfp4_bank* shared, int T, int k,
+                  float* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                  size_t ws_bytes, hipStream_t stream, bool mx_act) {
   begin_call();
   int st = check_bank(routed);
   if (st != MOE_OK) return st;
@@ -291,11 +312,12 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float
     if (st != MOE_OK) return st;
     if (shared->E != 1 || shared->H != H || shared->I != I) return MOE_ERR_INVALID_ARG;
   }
+  if (mx_act && !gemm_mx_supported(T, H, I, T * k, shared != nullptr)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !w_router_bf16 || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
-  const bool few = T <= kDecodeMaxT;
+  const bool few = T <= kDecodeMaxT && !mx_act;
   const size_t need = few ? decode_ws_bytes(T, H, I, E, k, T * k, false, shared != nullptr)
                           : layer_ws(nullptr, T, H, I, E, k).bytes;
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
@@ -352,12 +374,35 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float
     p.h_sh = L.h_sh;
     p.y_sh = L.y_sh;
   }
-  if (gemm_supported(T, H, I, R, shared != nullptr))
+  if (mx_act)
+    launch_expert_gemm_mx(p, L.ffn, stream);
+  else if (gemm_supported(T, H, I, R, shared != nullptr))
     launch_expert_gemm(p, L.ffn, stream);
   else
     launch_expert_ffn(p, stream);
   launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
+                      const moe_mxfp4_bank* routed, const moe_mxfp4_bank* shared, int T, int k,
+                      float* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  return layer_forward(x_bf16, w_router_bf16, logit_bias, routed, shared, T, k, out, topk_ids_out,
+                       topk_w_out, ws, ws_bytes, stream, false);
+}
+
+int moe_layer_forward_mxfp8_act(const void* x_bf16, const void* w_router_bf16,
+                                const float* logit_bias, const moe_mxfp4_bank* routed,
+                                const moe_mxfp4_bank* shared, int T, int k, float* out,
+                                int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  return layer_forward(x_bf16, w_router_bf16, logit_bias, routed, shared, T, k, out, topk_ids_out,
+                       topk_w_out, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

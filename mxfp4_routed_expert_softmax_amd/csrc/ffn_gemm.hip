@@ -75,6 +75,11 @@ struct GemmArgs {
   _Float16* h;    // [R + T][I]: routed rows, then the shared expert's T rows
   float* y;       // [R][H]
   float* y_sh;    // [T][H]
+  // MXFP8-activation mode: x and h as E4M3 codes with one E8M0 scale per 32
+  const uint8_t* xq;  // [T][H]
+  const uint8_t* xs;  // [T][H / 32]
+  uint8_t* hq;        // [R + T][I]
+  uint8_t* hs;        // [R + T][I / 32]
 };
 
 struct Bucket {
@@ -404,6 +409,281 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8-activation mode: both operands microscaled, on the gfx950 scaled
+// MFMA (v_mfma_scale_f32_16x16x128_f8f6f4: A = E4M3 activations, B = the
+// bank's E2M1 codes as stored, each with one E8M0 scale per 32 K). The
+// weights need no conversion at all; the activations are rounded to MXFP8
+// once (x before the gate/up GEMM, h in its epilogue), which is the one
+// approximation of this mode.
+//
+// Operand layout of the 16x16x128 instruction (lane l, c = l % 16,
+// g = l / 16): A row c, bytes 0..15 = K 16 g .. 16 g + 15 and bytes 16..31
+// = K 64 + 16 g .. 64 + 16 g + 15; B column c, 16 bytes = K 32 g .. 32 g +
+// 31 in the bank's nibble order; the scale operand of lane l is that of row
+// (column) c over K block g; D as for the other MFMAs (element v -> row
+// 4 g + v, column c).
+//
+// Tile and pipeline as in gemm_kernel, with A at one byte per element:
+// stage = 128 rows x 128 B of E4M3 (piece p of row r at slot
+// p ^ ((r / 2) % 8), so 16 consecutive rows reading one piece hit 16
+// distinct 16-byte bank groups) + 256 weight rows x 64 B of codes. The E8M0
+// scales of both operands over all of K sit in LDS for the whole tile.
+// ---------------------------------------------------------------------------
+
+constexpr int kMxABytes = kBM * kBK;                   // 16 KB of E4M3 per stage
+constexpr int kMxStageBytes = kMxABytes + kBBytes;     // 32 KB
+constexpr int kMxALoads = kMxABytes / 16 / kThreads;   // 2 per thread per stage
+constexpr int kMxAScaleBytes = kBM * (8192 / 32);      // 32 KB (K <= 8192)
+constexpr int kMxLds = kStages * kMxStageBytes + kScaleBytes + kMxAScaleBytes;  // 160 KB
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+// E8M0 exponent of a block whose largest magnitude is `amax` (OCP MX: the
+// binade of amax minus 8, the largest E4M3 exponent, clamped to [-127, 127];
+// an all-zero block takes -127).
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int ef = (int)(b >> 23);
+  const uint32_t mant = b & 0x7fffffu;
+  const int fl = ef ? ef - 127 : (31 - __builtin_clz(mant | 1u)) - 149;
+  return amax == 0.0f ? -127 : min(max(fl - 8, -127), 127);
+}
+
+// |v| / 2^se (0 <= q < 512) -> E4M3 magnitude code: nearest, ties to even,
+// clamped to 448 (0x7E). Below 2^-6 the steps are 2^-9 and the step count is
+// the code (8 steps = 2^-6 = code 0x08).
+__device__ __forceinline__ uint32_t e4m3_mag_code(float q) {
+  if (q < 0x1p-6f) return (uint32_t)rintf(q * 512.0f);
+  uint32_t b = __float_as_uint(q);
+  b += 0x7ffffu + ((b >> 20) & 1u);
+  const uint32_t code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  return min(code, 0x7eu);
+}
+
+// x [n_blocks * 32] bf16 -> E4M3 codes + one E8M0 byte per 32 (one thread
+// per block of 32).
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x,
+                                                          long n_blocks, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ s) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= n_blocks) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  // magnitudes of bf16 values order like their bit patterns without the sign
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) am = max(am, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+  const int se = mx_block_exp(__uint_as_float(am << 16));
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t bits = (w[2 * i + (j >> 1)] >> (16 * (j & 1))) & 0xffffu;
+      const float mag = __uint_as_float((bits & 0x7fffu) << 16);
+      const uint32_t code = e4m3_mag_code(ldexpf(mag, -se)) | ((bits >> 8) & 0x80u);
+      word |= code << (8 * j);
+    }
+    out[i] = word;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q + b * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  s[b] = (uint8_t)(se + 127);
+}
+
+template <bool GU>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
+  __shared__ __align__(16) char lds[kMxLds];
+  constexpr int kBN = GU ? kWRows / 2 : kWRows;
+  const int N = GU ? g.I : g.H;
+  const int K = GU ? g.H : g.I;
+  const int ncol = N / kBN;
+  const int total = min(g.tile_count[GU ? 0 : 1], g.max_rb * ncol);
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return;
+  const int nb = g.E + (g.has_shared ? 1 : 0);
+  const Bucket bk = bucket_of(g, min(max(g.tile_b[GU ? 0 : 1][t], 0), nb - 1));
+  const int mn = g.tile_mn[GU ? 0 : 1][t];
+  const int m0 = (mn >> 8) * kBM;
+  const int n0 = min(mn & 255, ncol - 1) * kBN;
+  if (m0 < 0 || m0 >= bk.count) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3, c = lane & 15, grp = lane >> 4;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  const uint32_t srow = (uint32_t)K / 32;
+
+  // activation row of tile row m (clamped into the bucket)
+  auto act_row = [&](int m) -> int {
+    m = min(m0 + m, bk.count - 1);
+    if (GU) {
+      const int row = bk.shared ? m : (g.row_token ? g.row_token[bk.begin + m] : bk.begin + m);
+      return min(max(row, 0), g.T - 1);
+    }
+    return bk.begin + m;
+  };
+
+  // A: thread tid fills slot (row 64 u + tid / 8, slot tid % 8), which holds
+  // K piece (tid % 8) ^ ((row / 2) % 8) of that row.
+  const uint8_t* a_src = GU ? g.xq : g.hq;
+  const uint8_t* as_src = GU ? g.xs : g.hs;
+  uint32_t a_off[kMxALoads];
+#pragma unroll
+  for (int u = 0; u < kMxALoads; ++u) {
+    const int r = 64 * u + (tid >> 3);
+    const int piece = (tid & 7) ^ ((r >> 1) & 7);
+    a_off[u] = (uint32_t)act_row(r) * (uint32_t)K + (uint32_t)(piece * 16);
+  }
+
+  const BankView bv = bk.shared ? g.shared : g.routed;
+  const uint32_t crow = (uint32_t)K / 2;
+  const size_t mat_rows = GU ? 2 * (size_t)g.I : (size_t)g.H;
+  const uint8_t* cbase = (GU ? bv.gu_codes : bv.d_codes) + (size_t)bk.e * mat_rows * crow;
+  const uint8_t* sbase = (GU ? bv.gu_scales : bv.d_scales) + (size_t)bk.e * mat_rows * srow;
+  auto wrow = [&](int r) -> uint32_t {
+    return GU ? (uint32_t)(r < 128 ? n0 + r : g.I + n0 + r - 128) : (uint32_t)(n0 + r);
+  };
+  uint32_t b_off[kBLoads];
+#pragma unroll
+  for (int u = 0; u < kBLoads; ++u) {
+    const int r = 128 * u + (tid >> 2);
+    b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
+  }
+  const uint32_t bs_lds = lds_base + kStages * kMxStageBytes;
+  const uint32_t as_lds = bs_lds + kScaleBytes;
+
+  auto issue = [&](int st, int ks) {
+    const uint32_t base = lds_base + (uint32_t)(st * kMxStageBytes);
+    const uint32_t k0 = (uint32_t)(ks * kBK);
+#pragma unroll
+    for (int u = 0; u < kMxALoads; ++u)
+      lds_load16(a_src, a_off[u] + k0, base + (uint32_t)((u * kThreads + 64 * wave) * 16));
+#pragma unroll
+    for (int u = 0; u < kBLoads; ++u)
+      lds_load16(cbase, b_off[u] + k0 / 2,
+                 base + kMxABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
+  };
+  // Scales of the tile over all of K, [row][K / 32] in LDS: the 256 weight
+  // rows', then the 128 activation rows' (4-byte pieces; srow % 4 == 0).
+  auto load_scales = [&]() {
+    const int pieces = kWRows * (int)srow / 4;
+    for (int p0 = 64 * wave; p0 < pieces; p0 += kThreads) {
+      const int p = min(p0 + lane, pieces - 1);
+      const uint32_t b = 4u * (uint32_t)p;
+      const uint32_t r = b / srow;
+      lds_load4(sbase, wrow((int)r) * srow + (b - r * srow), bs_lds + 4u * (uint32_t)p0);
+    }
+    const int apieces = kBM * (int)srow / 4;
+    for (int p0 = 64 * wave; p0 < apieces; p0 += kThreads) {
+      const int p = min(p0 + lane, apieces - 1);
+      const uint32_t b = 4u * (uint32_t)p;
+      const uint32_t r = b / srow;
+      lds_load4(as_src, (uint32_t)act_row((int)r) * srow + (b - r * srow), as_lds + 4u * (uint32_t)p0);
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool active = m0 + 64 * wm < bk.count;
+
+  // One K step of 128: 16 scaled MFMAs per wave (4 row x 4 column fragments).
+  auto compute = [&](int st, int ks) {
+    const char* sb = lds + st * kMxStageBytes;
+    const uint4* sa = reinterpret_cast<const uint4*>(sb);
+    const uint4* sbk = reinterpret_cast<const uint4*>(sb + kMxABytes);
+    const uint8_t* bsc = reinterpret_cast<const uint8_t*>(lds + kStages * kMxStageBytes) + ks * 4 + grp;
+    const uint8_t* asc = reinterpret_cast<const uint8_t*>(lds + kStages * kMxStageBytes + kScaleBytes) +
+                         ks * 4 + grp;
+    v8i_t b[4];
+    int sbv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = frag_row<GU>(wn, j, c);
+      const uint4 q = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
+      b[j] = v8i_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+      sbv[j] = bsc[r * srow];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 64 * wm + 16 * i + c;
+      const int sw = (r >> 1) & 7;
+      const uint4 lo = sa[r * 8 + (grp ^ sw)];
+      const uint4 hi = sa[r * 8 + ((4 + grp) ^ sw)];
+      const v8i_t a = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const int sav = asc[r * srow];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acc[i][j], 0, 4, 0,
+                                                                      sav, 0, sbv[j]);
+    }
+  };
+
+  const int steps = K / kBK;
+  load_scales();
+  issue(0, 0);
+  for (int ks = 0; ks < steps; ++ks) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + 1 < steps) issue((ks + 1) % kStages, ks + 1);
+    if (active) compute(ks % kStages, ks);
+  }
+
+  if (!active) return;
+  if constexpr (GU) {
+    // h = silu(g) * u for 32 consecutive columns per row (two fragments of
+    // the 16 lanes of a lane group), rounded to one MXFP8 block.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * grp + v;
+        const float h0 = silu_mul(acc[i][0][v], acc[i][2][v]);
+        const float h1 = silu_mul(acc[i][1][v], acc[i][3][v]);
+        float am = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
+        const int se = mx_block_exp(am);
+        const uint32_t c0 = e4m3_mag_code(ldexpf(fabsf(h0), -se)) | ((__float_as_uint(h0) >> 24) & 0x80u);
+        const uint32_t c1 = e4m3_mag_code(ldexpf(fabsf(h1), -se)) | ((__float_as_uint(h1) >> 24) & 0x80u);
+        if (m < bk.count) {
+          uint8_t* hr = g.hq + (size_t)(bk.begin + m) * g.I + n0 + 32 * wn + c;
+          hr[0] = (uint8_t)c0;
+          hr[16] = (uint8_t)c1;
+          if (c == 0) g.hs[(size_t)(bk.begin + m) * (g.I / 32) + (n0 + 32 * wn) / 32] = (uint8_t)(se + 127);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * grp + v;
+        if (m >= bk.count) continue;
+        float* yr = (bk.shared ? g.y_sh + (size_t)m * g.H : g.y + (size_t)(bk.begin + m) * g.H) +
+                    n0 + 64 * wn + c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][v];
+      }
+    }
+  }
+}
+
 struct GemmLayout {
   _Float16* h;
   int32_t* tiles;
@@ -426,7 +706,92 @@ GemmLayout gemm_layout(void* ws, int T, int H, int I, int E, int R, bool shared)
   return L;
 }
 
+struct MxLayout {
+  uint8_t *xq, *xs, *hq, *hs;
+  int32_t* tiles;
+  int max_rb, ncol_gu, ncol_dn;
+  size_t bytes;
+};
+
+MxLayout mx_layout(void* ws, int T, int H, int I, int E, int R, bool shared) {
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  MxLayout L;
+  const size_t rows = (size_t)R + (shared ? T : 0);
+  L.max_rb = (R + kBM - 1) / kBM + E + (shared ? (T + kBM - 1) / kBM + 1 : 0);
+  L.ncol_gu = I / (kWRows / 2);
+  L.ncol_dn = H / kWRows;
+  const size_t nt = 2 * (size_t)L.max_rb * (L.ncol_gu + L.ncol_dn) + 2;
+  const size_t sz[5] = {al((size_t)T * H), al((size_t)T * H / 32), al(rows * I), al(rows * I / 32),
+                        al(nt * sizeof(int32_t))};
+  char* w = static_cast<char*>(ws);
+  size_t off = 0;
+  char* part[5];
+  for (int i = 0; i < 5; ++i) {
+    part[i] = w ? w + off : nullptr;
+    off += sz[i];
+  }
+  L.xq = reinterpret_cast<uint8_t*>(part[0]);
+  L.xs = reinterpret_cast<uint8_t*>(part[1]);
+  L.hq = reinterpret_cast<uint8_t*>(part[2]);
+  L.hs = reinterpret_cast<uint8_t*>(part[3]);
+  L.tiles = reinterpret_cast<int32_t*>(part[4]);
+  L.bytes = off;
+  return L;
+}
+
 }  // namespace
+
+bool gemm_mx_supported(int T, int H, int I, int R, bool shared) {
+  // 32-bit byte offsets of the activation rows; scales of a tile fit LDS
+  const size_t rows = (size_t)R + (shared ? T : 0);
+  return H % kBK == 0 && I % kBK == 0 && I % (kWRows / 2) == 0 && H % kWRows == 0 && H <= 8192 &&
+         I <= 8192 && (size_t)T * H < (1ull << 31) && rows * I < (1ull << 31);
+}
+
+size_t gemm_mx_ws_bytes(int T, int H, int I, int E, int R, bool shared) {
+  return mx_layout(nullptr, T, H, I, E, R, shared).bytes;
+}
+
+void launch_quant_mxfp8(const uint16_t* x, long n_blocks, uint8_t* q, uint8_t* s, hipStream_t st) {
+  const long grid = (n_blocks + 255) / 256;
+  launch("quant_mxfp8_kernel", quant_mxfp8_kernel, dim3((unsigned)grid), dim3(256), 0, st, x,
+         n_blocks, q, s);
+}
+
+void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s) {
+  const int E = p.offsets ? p.routed.E : 1;
+  const MxLayout L = mx_layout(ws, p.T, p.H, p.I, E, p.R, p.has_shared);
+  GemmArgs g{};
+  g.x = p.x;
+  g.T = p.T;
+  g.H = p.H;
+  g.I = p.I;
+  g.E = E;
+  g.R = p.R;
+  g.routed = p.routed;
+  g.shared = p.shared;
+  g.has_shared = p.has_shared;
+  g.offsets = p.offsets;
+  g.row_token = p.row_token;
+  const size_t n_gu = (size_t)L.max_rb * L.ncol_gu, n_dn = (size_t)L.max_rb * L.ncol_dn;
+  g.tile_b[0] = L.tiles;
+  g.tile_mn[0] = L.tiles + n_gu;
+  g.tile_b[1] = L.tiles + 2 * n_gu;
+  g.tile_mn[1] = L.tiles + 2 * n_gu + n_dn;
+  g.tile_count = L.tiles + 2 * (n_gu + n_dn);
+  g.max_rb = L.max_rb;
+  g.y = p.y;
+  g.y_sh = p.y_sh;
+  g.xq = L.xq;
+  g.xs = L.xs;
+  g.hq = L.hq;
+  g.hs = L.hs;
+  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  launch_quant_mxfp8(p.x, (long)p.T * p.H / 32, L.xq, L.xs, s);
+  const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
+  launch("gemm_mx_gateup_kernel", gemm_mx_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
+  launch("gemm_mx_down_kernel", gemm_mx_kernel<false>, dim3(grid_dn), dim3(kThreads), 0, s, g);
+}
 
 bool gemm_supported(int T, int H, int I, int R, bool shared) {
   // 32-bit byte offsets of the activation rows

@@ -79,6 +79,15 @@ bool gemm_supported(int T, int H, int I, int R, bool shared);
 size_t gemm_ws_bytes(int T, int H, int I, int E, int R, bool shared);
 void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s);
 
+// MXFP8-activation mode of the grouped GEMM: x and h rounded to E4M3 with
+// one E8M0 scale per 32, the bank's E2M1 codes fed to the scaled MFMA as
+// they are. Call only where gemm_mx_supported().
+bool gemm_mx_supported(int T, int H, int I, int R, bool shared);
+size_t gemm_mx_ws_bytes(int T, int H, int I, int E, int R, bool shared);
+void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s);
+// bf16 values in blocks of 32 -> E4M3 codes + E8M0 scales (n_blocks blocks).
+void launch_quant_mxfp8(const uint16_t* x, long n_blocks, uint8_t* q, uint8_t* s, hipStream_t st);
+
 // The persistent few-token kernel (layer mode: router..combine in one
 // launch; FFN mode: bucketed rows given by offsets, writes y_rows).
 constexpr int kDecodeMaxT = 16;

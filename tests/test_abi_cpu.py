@@ -18,7 +18,8 @@ def test_library_exports_every_header_function():
     assert set(names) == {"moe_router_topk", "moe_permute", "moe_expert_ffn_mxfp4",
                           "moe_combine", "moe_layer_forward", "moe_workspace_bytes",
                           "moe_status_str", "moe_set_kernel_events",
-                          "moe_last_call_launches", "moe_launch_name"}
+                          "moe_last_call_launches", "moe_launch_name",
+                          "moe_quantize_mxfp8", "moe_layer_forward_mxfp8_act"}
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -126,3 +127,24 @@ def test_oracle_is_not_imported_by_the_product_path():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(root, f)).read()
                 assert "oracle" not in text.replace("oracle is", ""), f
+
+
+def test_mxfp8_act_entry_points_validate_before_launching():
+    lib = M.lib()
+    b = _bank(E=16, H=256, I=128)
+    fwd = lambda bank, T=8, k=2, x=FAKE, ws_bytes=1 << 40: lib.moe_layer_forward_mxfp8_act(
+        x, FAKE, None, ctypes.byref(bank), None, T, k, FAKE, None, None, FAKE, ws_bytes, None)
+    assert fwd(b, x=None) == M.MOE_ERR_INVALID_ARG
+    assert fwd(_bank(E=16, H=160, I=128)) == M.MOE_ERR_UNSUPPORTED   # H not a multiple of 256
+    assert fwd(_bank(E=16, H=256, I=96)) == M.MOE_ERR_UNSUPPORTED    # I not a multiple of 128
+    assert fwd(b, ws_bytes=16) == M.MOE_ERR_WORKSPACE
+    assert fwd(b, T=0) == M.MOE_OK
+    q = lib.moe_quantize_mxfp8
+    assert q(FAKE, 4, 48, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG      # H % 32
+    assert q(FAKE, -1, 64, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert q(FAKE + 2, 4, 64, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG  # misaligned x
+    assert q(None, 4, 64, FAKE, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert q(None, 0, 64, None, None, None) == M.MOE_OK
+    # the workspace covers the mode at every size
+    for T in (1, 300, 16384):
+        assert M.moe_workspace_bytes(T, 5120, 2304, 384, 6) >= T * 5120 * 33 // 32
