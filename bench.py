@@ -219,7 +219,7 @@ def main() -> int:
         wr_np = S.gen_router(w, 0)
         n_tok, t_cpu, calls = 0, 0.0, 0
         Tcpu = w.T if w.T <= 16 else 1
-        while t_cpu < args.cpu_seconds and calls < P:
+        while t_cpu < args.cpu_seconds and calls < (P if w.T <= 16 else w.T):
             xb = xs_np[calls % P][:Tcpu] if w.T <= 16 else xs_np[0][calls:calls + 1]
             ta = time.perf_counter()
             layer_fn(xb, wr_np, bias_np, routed_np, shared_np, w.k)

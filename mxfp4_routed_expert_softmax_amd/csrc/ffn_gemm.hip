@@ -223,6 +223,31 @@ __device__ __forceinline__ int frag_row(int wn, int j, int c) {
   return GU ? 32 * wn + 16 * (j & 1) + c + 128 * (j >> 1) : 64 * wn + 16 * j + c;
 }
 
+// LDS slot swizzles of the fragment reads (16 consecutive rows per lane
+// group read one piece index each): code rows (64 B, 4 slots) at
+// p ^ ((r / 4) % 4), E4M3 activation rows (128 B, 8 slots) at
+// p ^ ((r / 2) % 8). Variants that make every 8 and every 16 consecutive
+// rows hit distinct 16-byte bank groups lowered the bank-conflict counter
+// but measured 5 % slower on the MX gate/up GEMM, so these stay.
+__device__ __forceinline__ int code_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int act8_swz(int r) { return (r >> 1) & 7; }
+// Scale rows in LDS: srow bytes (K / 32, a multiple of 4) padded to an odd
+// number of 4-byte words, so 16 consecutive rows hit distinct banks; at
+// K = 8192 the padded rows would not fit and stay unpadded.
+__device__ __forceinline__ uint32_t scale_stride(uint32_t srow) {
+  return (((srow >> 2) & 1u) == 0u && srow < 256u) ? srow + 4u : srow;
+}
+// Copies `nrows` rows of srow bytes (source byte offset src_row(r) of row r)
+// into LDS at lds + r * stride, one row per wave iteration, one 4-byte
+// piece per lane (srow <= 256).
+template <class F>
+__device__ __forceinline__ void load_scale_rows(const void* src, F src_row, int nrows,
+                                                uint32_t srow, uint32_t stride, uint32_t lds,
+                                                int wave, int lane, int nwaves) {
+  for (int r = wave; r < nrows; r += nwaves)
+    if (lane < (int)(srow >> 2)) lds_load4(src, src_row(r) + 4u * (uint32_t)lane, lds + (uint32_t)r * stride);
+}
+
 template <bool GU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) char lds[kStages * kStageBytes + kScaleBytes];  // 160 KB
@@ -271,8 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   }
 
   // B: thread tid fills code slot (r = 128 u + tid / 4, piece tid % 4),
-  // which holds piece (tid % 4) ^ ((r / 4) % 4) of weight row r; threads
-  // tid < 256 also load the 4 E8M0 bytes of weight row tid.
+  // which holds piece (tid % 4) ^ ((r / 4) % 4) of weight row r.
   const BankView bv = bk.shared ? g.shared : g.routed;
   const uint32_t crow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
   const size_t mat_rows = GU ? 2 * (size_t)g.I : (size_t)g.H;
@@ -304,7 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   };
   // The tile's scales: rows r of the tile (gate/up: two runs of 128 rows,
   // down: one run of 256), srow bytes each, contiguous in the bank and in
-  // LDS ([r][K / 32]); 4-byte pieces, srow is a multiple of 4.
+  // LDS ([r][K / 32]); 4-byte pieces, srow is a multiple of 4. (Rows padded
+  // to an odd word count, and the code swizzle of the MX kernel, measured
+  // 2 % slower here.)
   auto load_scales = [&]() {
     const int pieces = kWRows * (int)srow / 4;
     for (int p0 = 64 * wave; p0 < pieces; p0 += kThreads) {
@@ -426,16 +452,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 //
 // Tile and pipeline as in gemm_kernel, with A at one byte per element:
 // stage = 128 rows x 128 B of E4M3 (piece p of row r at slot
-// p ^ ((r / 2) % 8), so 16 consecutive rows reading one piece hit 16
-// distinct 16-byte bank groups) + 256 weight rows x 64 B of codes. The E8M0
-// scales of both operands over all of K sit in LDS for the whole tile.
+// p ^ act8_swz(r)) + 256 weight rows x 64 B of codes. The E8M0 scales of
+// both operands over all of K sit in LDS for the whole tile.
 // ---------------------------------------------------------------------------
 
 constexpr int kMxABytes = kBM * kBK;                   // 16 KB of E4M3 per stage
 constexpr int kMxStageBytes = kMxABytes + kBBytes;     // 32 KB
 constexpr int kMxALoads = kMxABytes / 16 / kThreads;   // 2 per thread per stage
-constexpr int kMxAScaleBytes = kBM * (8192 / 32);      // 32 KB (K <= 8192)
-constexpr int kMxLds = kStages * kMxStageBytes + kScaleBytes + kMxAScaleBytes;  // 160 KB
+constexpr int kMxLds = 160 * 1024;                     // stages + both operands' scales
+constexpr int kMxIssueLoads = kMxALoads + kBLoads;     // loads per thread per stage
+static_assert(kMxIssueLoads == 4, "the pipeline waits below count 4 loads per stage");
+
+// Pipeline depth of the MX GEMM at reduction length K: as many 32 KB stages
+// (up to 4) as fit beside the tile's scales (384 rows at the padded stride).
+inline int mx_stages(int K) {
+  const int sr = K / 32;
+  const int stride = ((sr / 4) % 2 == 0 && sr < 256) ? sr + 4 : sr;
+  const int free = kMxLds - (kWRows + kBM) * stride;
+  return free >= 4 * kMxStageBytes ? 4 : free >= 3 * kMxStageBytes ? 3 : 2;
+}
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
@@ -499,7 +534,7 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __rest
   s[b] = (uint8_t)(se + 127);
 }
 
-template <bool GU>
+template <bool GU, int S>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
   __shared__ __align__(16) char lds[kMxLds];
   constexpr int kBN = GU ? kWRows / 2 : kWRows;
@@ -542,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
 #pragma unroll
   for (int u = 0; u < kMxALoads; ++u) {
     const int r = 64 * u + (tid >> 3);
-    const int piece = (tid & 7) ^ ((r >> 1) & 7);
+    const int piece = (tid & 7) ^ act8_swz(r);
     a_off[u] = (uint32_t)act_row(r) * (uint32_t)K + (uint32_t)(piece * 16);
   }
 
@@ -558,10 +593,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
 #pragma unroll
   for (int u = 0; u < kBLoads; ++u) {
     const int r = 128 * u + (tid >> 2);
-    b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
+    b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ code_swz(r));
   }
-  const uint32_t bs_lds = lds_base + kStages * kMxStageBytes;
-  const uint32_t as_lds = bs_lds + kScaleBytes;
+  const uint32_t sstride = scale_stride(srow);
+  if (S * kMxStageBytes + (kWRows + kBM) * (int)sstride > kMxLds) return;  // launcher picks S to fit
+  const uint32_t bs_lds = lds_base + S * kMxStageBytes;
+  const uint32_t as_lds = bs_lds + kWRows * sstride;
 
   auto issue = [&](int st, int ks) {
     const uint32_t base = lds_base + (uint32_t)(st * kMxStageBytes);
@@ -574,23 +611,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
       lds_load16(cbase, b_off[u] + k0 / 2,
                  base + kMxABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
   };
-  // Scales of the tile over all of K, [row][K / 32] in LDS: the 256 weight
-  // rows', then the 128 activation rows' (4-byte pieces; srow % 4 == 0).
+  // Scales of the tile over all of K, [row][K / 32] at LDS row stride
+  // sstride: the 256 weight rows', then the 128 activation rows'.
   auto load_scales = [&]() {
-    const int pieces = kWRows * (int)srow / 4;
-    for (int p0 = 64 * wave; p0 < pieces; p0 += kThreads) {
-      const int p = min(p0 + lane, pieces - 1);
-      const uint32_t b = 4u * (uint32_t)p;
-      const uint32_t r = b / srow;
-      lds_load4(sbase, wrow((int)r) * srow + (b - r * srow), bs_lds + 4u * (uint32_t)p0);
-    }
-    const int apieces = kBM * (int)srow / 4;
-    for (int p0 = 64 * wave; p0 < apieces; p0 += kThreads) {
-      const int p = min(p0 + lane, apieces - 1);
-      const uint32_t b = 4u * (uint32_t)p;
-      const uint32_t r = b / srow;
-      lds_load4(as_src, (uint32_t)act_row((int)r) * srow + (b - r * srow), as_lds + 4u * (uint32_t)p0);
-    }
+    load_scale_rows(sbase, [&](int r) { return wrow(r) * srow; }, kWRows, srow, sstride, bs_lds,
+                    wave, lane, kThreads / 64);
+    load_scale_rows(as_src, [&](int r) { return (uint32_t)act_row(r) * srow; }, kBM, srow,
+                    sstride, as_lds, wave, lane, kThreads / 64);
   };
 
   f32x4_t acc[4][4];
@@ -605,27 +632,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
     const char* sb = lds + st * kMxStageBytes;
     const uint4* sa = reinterpret_cast<const uint4*>(sb);
     const uint4* sbk = reinterpret_cast<const uint4*>(sb + kMxABytes);
-    const uint8_t* bsc = reinterpret_cast<const uint8_t*>(lds + kStages * kMxStageBytes) + ks * 4 + grp;
-    const uint8_t* asc = reinterpret_cast<const uint8_t*>(lds + kStages * kMxStageBytes + kScaleBytes) +
-                         ks * 4 + grp;
+    const uint8_t* bsc = reinterpret_cast<const uint8_t*>(lds + S * kMxStageBytes) + ks * 4 + grp;
+    const uint8_t* asc = bsc + kWRows * sstride;
     v8i_t b[4];
     int sbv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = frag_row<GU>(wn, j, c);
-      const uint4 q = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
+      const uint4 q = sbk[r * 4 + (grp ^ code_swz(r))];
       b[j] = v8i_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-      sbv[j] = bsc[r * srow];
+      sbv[j] = bsc[r * sstride];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 64 * wm + 16 * i + c;
-      const int sw = (r >> 1) & 7;
+      const int sw = act8_swz(r);
       const uint4 lo = sa[r * 8 + (grp ^ sw)];
       const uint4 hi = sa[r * 8 + ((4 + grp) ^ sw)];
       const v8i_t a = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const int sav = asc[r * srow];
+      const int sav = asc[r * sstride];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acc[i][j], 0, 4, 0,
@@ -633,14 +659,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmArgs g) {
     }
   };
 
+  // S-stage pipeline: stages ks + 1 .. ks + S - 2 stay in flight while step
+  // ks computes. At the top of step ks the wait leaves only the loads of the
+  // later stages already issued outstanding (vector loads complete in
+  // order), so stage ks has landed; the barrier makes it visible to every
+  // wave and frees the buffer of step ks - 1 for stage ks + S - 1.
   const int steps = K / kBK;
   load_scales();
-  issue(0, 0);
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < steps) issue(st, st);
   for (int ks = 0; ks < steps; ++ks) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (steps - 1 - ks >= S - 2) {
+      if constexpr (S == 4)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (S == 3)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else if (S == 4 && steps - 1 - ks == 1) {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    if (ks + 1 < steps) issue((ks + 1) % kStages, ks + 1);
-    if (active) compute(ks % kStages, ks);
+    if (ks + S - 1 < steps) issue((ks + S - 1) % S, ks + S - 1);
+    if (active) compute(ks % S, ks);
   }
 
   if (!active) return;
@@ -789,8 +833,13 @@ void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s) {
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
   launch_quant_mxfp8(p.x, (long)p.T * p.H / 32, L.xq, L.xs, s);
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
-  launch("gemm_mx_gateup_kernel", gemm_mx_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
-  launch("gemm_mx_down_kernel", gemm_mx_kernel<false>, dim3(grid_dn), dim3(kThreads), 0, s, g);
+  const int s_gu = mx_stages(p.H), s_dn = mx_stages(p.I);
+  auto gu = s_gu == 4 ? gemm_mx_kernel<true, 4> : s_gu == 3 ? gemm_mx_kernel<true, 3>
+                                                             : gemm_mx_kernel<true, 2>;
+  auto dn = s_dn == 4 ? gemm_mx_kernel<false, 4> : s_dn == 3 ? gemm_mx_kernel<false, 3>
+                                                              : gemm_mx_kernel<false, 2>;
+  launch("gemm_mx_gateup_kernel", gu, dim3(grid_gu), dim3(kThreads), 0, s, g);
+  launch("gemm_mx_down_kernel", dn, dim3(grid_dn), dim3(kThreads), 0, s, g);
 }
 
 bool gemm_supported(int T, int H, int I, int R, bool shared) {
