@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     f64_to_bf16_bits,
     gen_bank,
     gen_expert,
+    gen_fp8_bank,
     gen_inputs,
     gen_router,
     gen_tokens,

@@ -18,6 +18,9 @@ experts of a 6.7 GiB bank without generating the rest):
     [seed, cfg_id, 2, b, 0]        correlated blocks: base vector of block b
     [seed, cfg_id, 2, b, j + 1]    correlated blocks: noise of token j
     [seed, cfg_id, 3]              popularity ranks for the Zipf logit offset
+    [seed, cfg_id, 4, copy, m]     FP8 shared expert (32 x 32 block scales),
+                                   matrix m: 0 gate, 1 up, 2 down. Element
+                                   bytes first, then scales.
 
 Floating-point samples are drawn in fp64, rounded to fp32 (round to nearest
 even) and then to bf16 (round to nearest even on the fp32 bit pattern). The
@@ -186,6 +189,40 @@ def gen_bank(w: Workload, seed: int, copy: int = 0, shared: bool = False,
             fill(s)
     arrs.update(E=E, H=w.H, I=w.I)
     return arrs
+
+
+def _fp8_matrix(key, n_rows: int, k_cols: int, exp_lo: int, exp_hi: int,
+                e_lo: int = 5, e_hi: int = 9, all_codes: bool = False):
+    """E4M3 element bytes [n][k] drawn field by field (sign uniform, exponent
+    field uniform in [e_lo, e_hi], mantissa uniform; 1 in 16 bytes zero), or
+    uniform over every finite byte (all_codes); E8M0 scale bytes 127 + exp
+    for each 32 x 32 block, exp uniform in [exp_lo, exp_hi]."""
+    rng = np.random.default_rng(key)
+    n = n_rows * k_cols
+    if all_codes:
+        b = rng.integers(0, 254, n, dtype=np.int64)
+        b = np.where(b >= 0x7F, b + 1, b).astype(np.uint8)     # skip the NaN 0x7F, 0xFF
+        b[b == 0xFF] = 0xFE
+    else:
+        sign = rng.integers(0, 2, n, dtype=np.uint8)
+        e = rng.integers(e_lo, e_hi + 1, n, dtype=np.uint8)
+        m = rng.integers(0, 8, n, dtype=np.uint8)
+        b = (sign << 7) | (e << 3) | m
+        b[rng.integers(0, 16, n) == 0] = 0
+    s = (127 + rng.integers(exp_lo, exp_hi + 1, (n_rows // 32) * (k_cols // 32))).astype(np.uint8)
+    return b.reshape(n_rows, k_cols), s.reshape(n_rows // 32, k_cols // 32)
+
+
+def gen_fp8_bank(w: Workload, seed: int, copy: int = 0, all_codes: bool = False) -> dict:
+    """One-expert FP8 bank (the shared expert in the checkpoint's dense
+    format): gate_up_w [1][2][I][H], gate_up_scales [1][2][I/32][H/32],
+    down_w [1][H][I], down_scales [1][H/32][I/32]."""
+    H, I = w.H, w.I
+    g = _fp8_matrix([seed, w.cfg_id, 4, copy, 0], I, H, w.exp_lo, w.exp_hi, all_codes=all_codes)
+    u = _fp8_matrix([seed, w.cfg_id, 4, copy, 1], I, H, w.exp_lo, w.exp_hi, all_codes=all_codes)
+    d = _fp8_matrix([seed, w.cfg_id, 4, copy, 2], H, I, w.exp_lo, w.exp_hi, all_codes=all_codes)
+    return dict(gate_up_w=np.stack([g[0], u[0]])[None], gate_up_scales=np.stack([g[1], u[1]])[None],
+                down_w=d[0][None], down_scales=d[1][None], E=1, H=H, I=I)
 
 
 # ---------------------------------------------------------------------------
