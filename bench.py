@@ -63,6 +63,9 @@ def parse():
                     help="time moe_layer_forward_mxfp8_act, the opt-in mode with MXFP8 "
                          "activations on the scaled fp8 x fp4 MFMA (an approximation of the "
                          "layer; its error against the exact layer is reported)")
+    ap.add_argument("--fp8-shared", action="store_true",
+                    help="time moe_layer_forward_fp8_shared: the shared expert in the "
+                         "checkpoint's FP8 format (E4M3, 32 x 32 ue8m0 block scales)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 3 plain device copies of BYTES bytes (the reference "
                          "reading for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -126,6 +129,14 @@ def main() -> int:
             routed=M.BankTensors(*[c[k][: w.E] for k in keys]),
             shared=M.BankTensors(*[c[k][w.E:] for k in keys]),
             both=M.BankTensors(*[c[k] for k in keys])))
+    if args.fp8_shared:
+        if args.mxfp8_act:
+            log("--fp8-shared and --mxfp8-act are separate modes")
+            return 2
+        shared8_np = S.gen_fp8_bank(w, 0)
+        s8 = M.Fp8BankTensors.from_numpy(shared8_np, dev)
+        for i, b in enumerate(banks):
+            b["shared"] = s8 if i == 0 else M.Fp8BankTensors(*[t.clone() for t in s8.tensors])
     wr0 = torch.from_numpy(S.gen_router(w, 0).view(np.int16)).to(dev).view(torch.bfloat16)
     wrs = [wr0] + [wr0.clone() for _ in range(C - 1)]
     bias_np = S.gen_zipf_bias(w, 0)
@@ -141,7 +152,8 @@ def main() -> int:
         f"({C} bank copies, {P} token batches)")
 
     # Pre-marshalled arguments: the timed loop makes one C call per step.
-    fwd_name = "moe_layer_forward_mxfp8_act" if args.mxfp8_act else "moe_layer_forward"
+    fwd_name = ("moe_layer_forward_mxfp8_act" if args.mxfp8_act else
+                "moe_layer_forward_fp8_shared" if args.fp8_shared else "moe_layer_forward")
     fwd = getattr(lib, fwd_name)
     sh = stream.cuda_stream
     ws_n = ws.numel()
@@ -186,7 +198,7 @@ def main() -> int:
     roof = None
     if not args.no_roofline_loop:
         roof = kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bias,
-                               ids, wts, ws, P, C, W, K, stream)
+                               ids, wts, ws, P, C, W, K, stream, shared8=args.fp8_shared)
     # ---- CPU baseline: the fp64 oracle on the host -------------------------
     cpu = None
     mx_err = None
@@ -211,6 +223,10 @@ def main() -> int:
         from oracle import moe as O
         from oracle import mxfp8_act as MXO
         layer_fn = MXO.layer_mx if args.mxfp8_act else O.layer
+        if args.fp8_shared:
+            from oracle import fp8_dense as F8O
+            layer_fn = F8O.layer_fp8_shared
+            shared_np = shared8_np
         try:
             from threadpoolctl import threadpool_info
             cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -243,12 +259,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 x mxfp4 -> fp32" if args.mxfp8_act else "bf16 x mxfp4 -> fp32",
+        "dtype": ("mxfp8 x mxfp4 -> fp32" if args.mxfp8_act else
+                  "bf16 x mxfp4 (shared: bf16 x fp8) -> fp32" if args.fp8_shared else
+                  "bf16 x mxfp4 -> fp32"),
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "intermediate": w.I, "shared_experts": 1,
                    "bank_copies": C, "token_batches": P,
-                   "expert_activations": "mxfp8" if args.mxfp8_act else "bf16/fp16/fp32"},
+                   "expert_activations": "mxfp8" if args.mxfp8_act else "bf16/fp16/fp32",
+                   "shared_expert_format": "fp8 e4m3, 32x32 ue8m0 blocks" if args.fp8_shared
+                   else "mxfp4"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -376,6 +396,15 @@ def verify_sweep(args, M, S, np, torch):
 # one E8M0 byte per 32); flops count 2 per multiply-add of the expert FFN.
 def kernel_work(name, w, U, shared=True):
     H, I, T, R = w.H, w.I, w.T, w.T * w.k
+    if name == "fp8_gateup_gemv_kernel":
+        # the FP8 shared expert's gate/up: 1 byte per weight, 1 per 32 x 32 block
+        return "hbm", 2 * I * H + 2 * (I // 32) * (H // 32) + T * H * 2 + T * I * 4
+    if name == "fp8_down_gemv_kernel":
+        return "hbm", H * I + (H // 32) * (I // 32) + T * I * 4 + T * H * 4
+    if name == "gemm_fp8w_gateup_kernel":
+        return "gemm", (T * 2.0 * 2 * H * I, 2 * I * H + T * H * 2 + T * I * 2)
+    if name == "gemm_fp8w_down_kernel":
+        return "gemm", (T * 2.0 * H * I, H * I + T * I * 2 + T * H * 4)
     gu_expert = 2 * I * H * 17 // 32       # gate + up of one expert
     dn_expert = I * H * 17 // 32           # down of one expert
     if name == "gateup_fused_kernel":
@@ -455,7 +484,7 @@ def kernel_work(name, w, U, shared=True):
 
 
 def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bias, ids, wts,
-                    ws, P, C, W, K, stream):
+                    ws, P, C, W, K, stream, shared8=False):
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch already loaded
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -509,14 +538,15 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
     log(f"[bench] kernels (event-timed, mean of {K}): {per}")
     j = int(np.argmax(mean_ms))
     name, t_ms = names[j], float(mean_ms[j])
-    bound, _ = kernel_work(name, w, 1)
+    sh = not shared8
+    bound, _ = kernel_work(name, w, 1, sh)
     if bound is None:
         log(f"[bench] dominant kernel {name}: no algorithmic work model, roofline omitted")
         return None
     # per-launch work averaged over the calls the timed loop made
     if bound == "gemm":
-        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1][0] for i in range(K)]))
-        by = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1][1] for i in range(K)]))
+        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh)[1][0] for i in range(K)]))
+        by = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh)[1][1] for i in range(K)]))
         # the bound is the resource the work needs longer at its peak
         mpeak = MFMA_PEAK_OF.get(name, MFMA_16BIT_PEAK_TFLOPS)
         bound = "mfma" if fl / (mpeak * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm"
@@ -524,7 +554,7 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         log(f"[bench] {name}: {fl / 1e12:.3f} TFLOP, {by / 1e9:.2f} GB unavoidable -> "
             f"bound by {bound.upper()}")
     else:
-        work = float(np.mean([kernel_work(name, w, U[(W + i) % P])[1] for i in range(K)]))
+        work = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh)[1] for i in range(K)]))
     if bound == "hbm":
         ach = work / (t_ms / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"

@@ -85,6 +85,32 @@ typedef struct moe_mxfp4_bank {
   int32_t E, H, I;
 } moe_mxfp4_bank;
 
+/*
+ * An FP8 expert bank: the reference checkpoint's dense format, fp8 weights
+ * in 32 x 32 blocks with ue8m0 scales (llama.cpp discussion #28766, "Is it
+ * supported?"; the same page and the comment pointing at the port's list of
+ * V4 -> V4.1 differences warn that 128 x 128 blocks here mis-scale every
+ * weight without any error). Used for the shared expert, so E must be 1.
+ *
+ *   gate_up_w      [E][2][I][H]       E4M3 bytes, matrix 0 = gate, 1 = up
+ *   gate_up_scales [E][2][I/32][H/32] E8M0: block (i, j) covers rows
+ *                                     32i..32i+31, columns 32j..32j+31
+ *   down_w         [E][H][I]          E4M3 bytes
+ *   down_scales    [E][H/32][I/32]
+ *
+ * E4M3 is the OCP fp8 format (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; S.1111.111 is NaN); scale byte s multiplies its block by
+ * 2^(s - 127), s == 255 is NaN. Rows run along the reduction dimension, as
+ * in the MXFP4 banks. Weight arrays must be 16-byte aligned.
+ */
+typedef struct moe_fp8_bank {
+  const uint8_t* gate_up_w;
+  const uint8_t* gate_up_scales;
+  const uint8_t* down_w;
+  const uint8_t* down_scales;
+  int32_t E, H, I;
+} moe_fp8_bank;
+
 /* Workspace bytes that suffice for any call below at these sizes. */
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k);
 
@@ -205,6 +231,30 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16,
                       const moe_mxfp4_bank* shared, int T, int k, float* out,
                       int32_t* topk_ids_out, float* topk_w_out,
                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One FP8 expert over T rows (the shared expert or a dense SwiGLU FFN in the
+ * checkpoint's fp8 format): y[t] = W_down (silu(W_gate x_t) * (W_up x_t)),
+ * weights dequantised exactly (E4M3 times a power of two), products summed
+ * in fp32. x_bf16 [T][H] bf16, y [T][H] fp32, both 16-byte aligned; bank->E
+ * must be 1. moe_workspace_bytes(T, H, I, 1, 1) suffices.
+ */
+int moe_expert_ffn_fp8(const void* x_bf16, const moe_fp8_bank* bank, int T, float* y,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_layer_forward with the shared expert in the FP8 format above (the
+ * reference checkpoint's layout: FP4 routed experts, FP8 dense weights;
+ * llama.cpp discussion #28766, "Is it supported?"). Routing, routed experts,
+ * ordering and determinism are those of moe_layer_forward; the shared row
+ * is added first in the combine, with weight 1. `shared` is required.
+ * moe_workspace_bytes covers its workspace.
+ */
+int moe_layer_forward_fp8_shared(const void* x_bf16, const void* w_router_bf16,
+                                 const float* logit_bias, const moe_mxfp4_bank* routed,
+                                 const moe_fp8_bank* shared, int T, int k, float* out,
+                                 int32_t* topk_ids_out, float* topk_w_out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Opt-in mode with MXFP8 activations on the scaled matrix cores.

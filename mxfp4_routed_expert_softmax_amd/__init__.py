@@ -8,6 +8,8 @@ script (build.py) and a ctypes binding (_lib.py) with the same call names.
 from ._lib import (  # noqa: F401
     Bank,
     BankTensors,
+    Fp8Bank,
+    Fp8BankTensors,
     MoeError,
     MOE_ERR_HIP,
     MOE_ERR_INVALID_ARG,
@@ -17,10 +19,12 @@ from ._lib import (  # noqa: F401
     header_functions,
     lib,
     moe_combine,
+    moe_expert_ffn_fp8,
     moe_expert_ffn_mxfp4,
     moe_last_call_launches,
     moe_launch_name,
     moe_layer_forward,
+    moe_layer_forward_fp8_shared,
     moe_layer_forward_mxfp8_act,
     moe_permute,
     moe_quantize_mxfp8,

@@ -44,6 +44,20 @@ class Bank(ctypes.Structure):
     ]
 
 
+class Fp8Bank(ctypes.Structure):
+    """moe_fp8_bank: device pointers of one FP8 (32 x 32 block-scaled) bank."""
+
+    _fields_ = [
+        ("gate_up_w", ctypes.c_void_p),
+        ("gate_up_scales", ctypes.c_void_p),
+        ("down_w", ctypes.c_void_p),
+        ("down_scales", ctypes.c_void_p),
+        ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("I", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -59,6 +73,9 @@ _SIGS = {
     "moe_layer_forward_mxfp8_act": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank),
                                           _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_mxfp8": (_I, [_P, _I, _I, _P, _P, _P]),
+    "moe_expert_ffn_fp8": (_I, [_P, ctypes.POINTER(Fp8Bank), _I, _P, _P, _SZ, _P]),
+    "moe_layer_forward_fp8_shared": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Fp8Bank),
+                                           _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_set_kernel_events": (_I, [_P, _I]),
     "moe_last_call_launches": (_I, []),
     "moe_launch_name": (ctypes.c_char_p, [_I]),
@@ -159,6 +176,32 @@ class BankTensors:
         t = {k: torch.from_numpy(arrs[k]).to(device) for k in
              ("gate_up_codes", "gate_up_scales", "down_codes", "down_scales")}
         return cls(t["gate_up_codes"], t["gate_up_scales"], t["down_codes"], t["down_scales"])
+
+
+class Fp8BankTensors:
+    """Keeps the four FP8 bank tensors alive next to their ctypes struct."""
+
+    def __init__(self, gate_up_w, gate_up_scales, down_w, down_scales):
+        import torch
+        for n, t in [("gate_up_w", gate_up_w), ("gate_up_scales", gate_up_scales),
+                     ("down_w", down_w), ("down_scales", down_scales)]:
+            _need(t, n, (torch.uint8,))
+        E, two, I, H = gate_up_w.shape
+        if two != 2 or tuple(gate_up_scales.shape) != (E, 2, I // 32, H // 32) \
+                or tuple(down_w.shape) != (E, H, I) \
+                or tuple(down_scales.shape) != (E, H // 32, I // 32):
+            raise ValueError("FP8 bank tensors do not have the [E][2][I][H] ... layout")
+        self.tensors = (gate_up_w, gate_up_scales, down_w, down_scales)
+        self.E, self.H, self.I = E, H, I
+        self.struct = Fp8Bank(gate_up_w.data_ptr(), gate_up_scales.data_ptr(),
+                              down_w.data_ptr(), down_scales.data_ptr(), E, H, I)
+
+    @classmethod
+    def from_numpy(cls, arrs: dict, device="cuda"):
+        import torch
+        t = {k: torch.from_numpy(arrs[k]).to(device) for k in
+             ("gate_up_w", "gate_up_scales", "down_w", "down_scales")}
+        return cls(t["gate_up_w"], t["gate_up_scales"], t["down_w"], t["down_scales"])
 
 
 # ---------------------------------------------------------------------------
@@ -271,6 +314,24 @@ def moe_layer_forward_mxfp8_act(x, w_router, logit_bias, routed: BankTensors,
                                 shared: BankTensors | None, k, out, topk_ids_out=None,
                                 topk_w_out=None, ws=None, stream=None):
     _layer("moe_layer_forward_mxfp8_act", x, w_router, logit_bias, routed, shared, k, out,
+           topk_ids_out, topk_w_out, ws, stream)
+
+
+def moe_expert_ffn_fp8(x, bank: Fp8BankTensors, y, ws, stream=None):
+    import torch
+    _need(x, "x", _bf16_types(), 2)
+    _need(y, "y", (torch.float32,), 2)
+    T = x.shape[0]
+    st = lib().moe_expert_ffn_fp8(_ptr(x), ctypes.byref(bank.struct), T, _ptr(y), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream, x))
+    _check("moe_expert_ffn_fp8", st)
+
+
+def moe_layer_forward_fp8_shared(x, w_router, logit_bias, routed: BankTensors,
+                                 shared: Fp8BankTensors, k, out, topk_ids_out=None,
+                                 topk_w_out=None, ws=None, stream=None):
+    _layer("moe_layer_forward_fp8_shared", x, w_router, logit_bias, routed, shared, k, out,
            topk_ids_out, topk_w_out, ws, stream)
 
 

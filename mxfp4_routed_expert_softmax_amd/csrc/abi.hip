@@ -44,6 +44,57 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int check_fp8_bank(const moe_fp8_bank* b) {
+  if (!b || !b->gate_up_w || !b->gate_up_scales || !b->down_w || !b->down_scales)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(b->gate_up_w) || !aligned16(b->down_w)) return MOE_ERR_INVALID_ARG;
+  if (b->E != 1 || b->H <= 0 || b->I <= 0 || b->H % 32 || b->I % 32) return MOE_ERR_INVALID_ARG;
+  if (b->H > kMaxH || b->I > kMaxI) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Scratch of the FP8 expert over T rows: the grouped GEMM's where it tiles
+// the shape and T exceeds the few-token kernels, else fp32 h for at most
+// kDecodeMaxT rows at a time.
+bool fp8_uses_gemm(int T, int H, int I) { return T > kDecodeMaxT && gemm_supported(T, H, I, 0, true); }
+size_t fp8_ffn_ws(int T, int H, int I) {
+  return fp8_uses_gemm(T, H, I) ? fp8_gemm_ws_bytes(T, H, I)
+                                : fp8_gemv_ws_bytes(T < kDecodeMaxT ? T : kDecodeMaxT, I);
+}
+
+// Workspace of the few-token layer with an FP8 shared expert: the decode
+// path's (no MXFP4 shared expert), then y_sh [T][H], then the FP8 scratch.
+size_t few_fp8_ws(int T, int H, int I, int E, int k) {
+  return align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false)) +
+         align_up((size_t)T * H * sizeof(float)) + fp8_ffn_ws(T, H, I);
+}
+
+// The FP8 expert over rows x[0..T) into y[0..T); `scratch` holds fp8_ffn_ws.
+void launch_fp8_ffn(const uint16_t* x, const moe_fp8_bank* b, int T, float* y, void* scratch,
+                    hipStream_t stream) {
+  Fp8Ffn p{};
+  p.H = b->H;
+  p.I = b->I;
+  p.gu_w = b->gate_up_w;
+  p.gu_s = b->gate_up_scales;
+  p.d_w = b->down_w;
+  p.d_s = b->down_scales;
+  if (fp8_uses_gemm(T, b->H, b->I)) {
+    p.x = x;
+    p.T = T;
+    p.y = y;
+    launch_fp8_gemm(p, scratch, stream);
+    return;
+  }
+  p.h = static_cast<float*>(scratch);
+  for (int t0 = 0; t0 < T; t0 += kDecodeMaxT) {
+    p.x = x + (size_t)t0 * b->H;
+    p.y = y + (size_t)t0 * b->H;
+    p.T = T - t0 < kDecodeMaxT ? T - t0 : kDecodeMaxT;
+    launch_fp8_ffn_gemv(p, stream);
+  }
+}
+
 // Bump allocator over the caller's workspace.
 struct Carve {
   char* base;
@@ -90,7 +141,9 @@ LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
   const size_t gemv = align_up(R * I * sizeof(float)) + align_up((size_t)T * I * sizeof(float));
   const size_t gemm = gemm_ws_bytes(T, H, I, E, (int)R, true);
   const size_t mx = gemm_mx_ws_bytes(T, H, I, E, (int)R, true);
-  const size_t big = gemm > mx ? gemm : mx;
+  size_t big = gemm > mx ? gemm : mx;
+  const size_t f8 = fp8_ffn_ws(T, H, I);
+  big = big > f8 ? big : f8;
   char* ffn = c.take<char>(gemv > big ? gemv : big);
   L.ffn = ffn;
   L.h = reinterpret_cast<float*>(ffn);
@@ -149,7 +202,13 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int k) {
   const size_t d = decode_ws_bytes(T, H, I, E, k, R, false, true);
   const size_t f = decode_ws_bytes(T, H, I, E, k, R, true, false);
   b = b > d ? b : d;
-  return b > f ? b : f;
+  b = b > f ? b : f;
+  if (T <= kDecodeMaxT) {
+    const size_t g = few_fp8_ws(T, H, I, E, k);
+    b = b > g ? b : g;
+  }
+  const size_t e8 = fp8_ffn_ws(T, H, I);
+  return b > e8 ? b : e8;
 }
 
 const char* moe_status_str(int status) {
@@ -300,7 +359,8 @@ namespace {
 int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* logit_bias,
                   const moe_mxfp4_bank* routed, const moe_mxfp4_bank* shared, int T, int k,
                   float* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                  size_t ws_bytes, hipStream_t stream, bool mx_act) {
+                  size_t ws_bytes, hipStream_t stream, bool mx_act,
+                  const moe_fp8_bank* shared8 = nullptr) {
   begin_call();
   int st = check_bank(routed);
   if (st != MOE_OK) return st;
@@ -312,18 +372,35 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
     if (st != MOE_OK) return st;
     if (shared->E != 1 || shared->H != H || shared->I != I) return MOE_ERR_INVALID_ARG;
   }
+  if (shared8) {
+    st = check_fp8_bank(shared8);
+    if (st != MOE_OK) return st;
+    if (shared8->H != H || shared8->I != I) return MOE_ERR_INVALID_ARG;
+  }
   if (mx_act && !gemm_mx_supported(T, H, I, T * k, shared != nullptr)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x_bf16 || !w_router_bf16 || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
   const bool few = T <= kDecodeMaxT && !mx_act;
-  const size_t need = few ? decode_ws_bytes(T, H, I, E, k, T * k, false, shared != nullptr)
+  const size_t need = few ? (shared8 ? few_fp8_ws(T, H, I, E, k)
+                                     : decode_ws_bytes(T, H, I, E, k, T * k, false, shared != nullptr))
                           : layer_ws(nullptr, T, H, I, E, k).bytes;
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (few) {
+    const float* y_ext = nullptr;
+    if (shared8) {
+      // the FP8 shared expert first (it needs no routing); the routed
+      // launches' combine adds its rows first, in the fixed order
+      char* w8 = static_cast<char*>(ws) + align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false));
+      float* y_sh = reinterpret_cast<float*>(w8);
+      launch_fp8_ffn(static_cast<const uint16_t*>(x_bf16), shared8, T, y_sh,
+                     w8 + align_up((size_t)T * H * sizeof(float)), stream);
+      y_ext = y_sh;
+    }
     DecodeLaunch d{};
+    d.y_shared_ext = y_ext;
     d.ffn_mode = 0;
     d.x = static_cast<const uint16_t*>(x_bf16);
     d.wr = static_cast<const uint16_t*>(w_router_bf16);
@@ -380,7 +457,11 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
     launch_expert_gemm(p, L.ffn, stream);
   else
     launch_expert_ffn(p, stream);
-  launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
+  // an FP8 shared expert runs after the routed FFN, in the same scratch
+  if (shared8)
+    launch_fp8_ffn(static_cast<const uint16_t*>(x_bf16), shared8, T, L.y_sh, L.ffn, stream);
+  launch_combine(L.y, L.inv_row, w, (shared || shared8) ? L.y_sh : nullptr, T, k, H, R, out,
+                 stream);
   return launch_status();
 }
 
@@ -394,6 +475,31 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16, const float
                       size_t ws_bytes, hipStream_t stream) {
   return layer_forward(x_bf16, w_router_bf16, logit_bias, routed, shared, T, k, out, topk_ids_out,
                        topk_w_out, ws, ws_bytes, stream, false);
+}
+
+int moe_expert_ffn_fp8(const void* x_bf16, const moe_fp8_bank* bank, int T, float* y,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  begin_call();
+  int st = check_fp8_bank(bank);
+  if (st != MOE_OK) return st;
+  st = check_dims(T, bank->H, 1, 1, bank->I);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !y || !aligned16(x_bf16) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < fp8_ffn_ws(T, bank->H, bank->I)) return MOE_ERR_WORKSPACE;
+  launch_fp8_ffn(static_cast<const uint16_t*>(x_bf16), bank, T, y, ws, stream);
+  return launch_status();
+}
+
+int moe_layer_forward_fp8_shared(const void* x_bf16, const void* w_router_bf16,
+                                 const float* logit_bias, const moe_mxfp4_bank* routed,
+                                 const moe_fp8_bank* shared, int T, int k, float* out,
+                                 int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (!shared) return MOE_ERR_INVALID_ARG;
+  return layer_forward(x_bf16, w_router_bf16, logit_bias, routed, nullptr, T, k, out,
+                       topk_ids_out, topk_w_out, ws, ws_bytes, stream, false, shared);
 }
 
 int moe_layer_forward_mxfp8_act(const void* x_bf16, const void* w_router_bf16,

@@ -140,6 +140,7 @@ struct DecodeArgs {
   const float* bias;
   BankView routed, shared;
   int has_shared;
+  const float* y_shared_ext;  // [T][H] shared rows from earlier launches, or null
   int T, H, I, E, k, R;
   const int32_t* offsets_in;    // FFN mode: caller's bucket offsets
   const int32_t* row_token_in;  // FFN mode (null = identity)
@@ -650,7 +651,8 @@ __device__ void combine_column(const DecodeArgs& a, int c) {
   const int n = c * kDnRows + (threadIdx.x & 31);
   if (n >= a.H) return;
   for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
-    float v = a.has_shared ? cld(a.y + (size_t)(a.R + t) * a.H + n) : 0.0f;
+    float v = a.y_shared_ext ? a.y_shared_ext[(size_t)t * a.H + n]
+              : a.has_shared ? cld(a.y + (size_t)(a.R + t) * a.H + n) : 0.0f;
     for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
       float yv[8];
 #pragma unroll
@@ -1003,7 +1005,8 @@ __device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
                                    const float* s_w) {
   const int n = c * kDnRows + (int)threadIdx.x;
   if (threadIdx.x >= kDnRows || n >= a.H) return;
-  float v = a.has_shared ? cld(a.y + (size_t)a.R * a.H + n) : 0.0f;
+  float v = a.y_shared_ext ? a.y_shared_ext[n]
+            : a.has_shared ? cld(a.y + (size_t)a.R * a.H + n) : 0.0f;
   for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
     float y[8];
 #pragma unroll
@@ -1802,6 +1805,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.routed = d.routed;
   a.shared = d.shared;
   a.has_shared = shared;
+  a.y_shared_ext = ffn ? nullptr : d.y_shared_ext;
   a.T = d.T;
   a.H = d.H;
   a.I = d.I;

@@ -436,6 +436,206 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// FP8 weights (E4M3, one E8M0 scale per 32 x 32 block; the checkpoint's
+// dense format, used for an FP8 shared expert): gemm_kernel with a B
+// operand of 128 bytes per weight row and K step. A weight row's K range
+// [32 g, 32 g + 32) is pieces 2 g and 2 g + 1 of its row (piece p at slot
+// p ^ act8_swz(r)); MFMA sub-step s takes bytes 8 s .. 8 s + 7 of those 32
+// and converts them with the gfx950 scaled FP8 conversion (exact: E4M3
+// times a power of two is representable in bf16, and in fp16 for scale
+// exponents in [-15, 7]). The scales of the tile's 8 blocks of 32 weight
+// rows over all of K take 8 x K / 32 bytes of LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kF8BBytes = kWRows * kBK;               // 32 KB of E4M3 per stage
+constexpr int kF8StageBytes = kABytes + kF8BBytes;    // 64 KB
+constexpr int kF8BLoads = kF8BBytes / 16 / kThreads;  // 4 per thread per stage
+constexpr int kF8ScaleBytes = 8 * (8192 / 32);        // 2 KB
+
+template <bool GU>
+__device__ __forceinline__ Op<GU> cvt8_fp8(uint32_t w0, uint32_t w1, float sc) {
+  if constexpr (GU) {
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+    return bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  } else {
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, sc, false);
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, sc, true);
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, sc, false);
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, sc, true);
+    return f16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  }
+}
+
+template <bool GU>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8w_kernel(GemmArgs g) {
+  __shared__ __align__(16) char lds[kStages * kF8StageBytes + kF8ScaleBytes];  // 130 KB
+  constexpr int kBN = GU ? kWRows / 2 : kWRows;
+  const int N = GU ? g.I : g.H;
+  const int K = GU ? g.H : g.I;
+  const int ncol = N / kBN;
+  const int total = min(g.tile_count[GU ? 0 : 1], g.max_rb * ncol);
+  const int per = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  const int t = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= total) return;
+  const int nb = g.E + (g.has_shared ? 1 : 0);
+  const Bucket bk = bucket_of(g, min(max(g.tile_b[GU ? 0 : 1][t], 0), nb - 1));
+  const int mn = g.tile_mn[GU ? 0 : 1][t];
+  const int m0 = (mn >> 8) * kBM;
+  const int n0 = min(mn & 255, ncol - 1) * kBN;
+  if (m0 < 0 || m0 >= bk.count) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3, c = lane & 15, grp = lane >> 4;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+
+  // A exactly as in gemm_kernel
+  const void* a_src = GU ? static_cast<const void*>(g.x) : static_cast<const void*>(g.h);
+  uint32_t a_off[kALoads];
+  {
+    const int piece = (tid & 15) ^ ((tid >> 4) & 15);
+#pragma unroll
+    for (int u = 0; u < kALoads; ++u) {
+      const int m = min(m0 + 32 * u + (tid >> 4), bk.count - 1);
+      int row;
+      if (GU) {
+        row = bk.shared ? m : (g.row_token ? g.row_token[bk.begin + m] : bk.begin + m);
+        row = min(max(row, 0), g.T - 1);
+      } else {
+        row = bk.begin + m;
+      }
+      a_off[u] = ((uint32_t)row * (uint32_t)K + (uint32_t)(piece * 8)) * 2u;
+    }
+  }
+
+  // B: thread tid fills slot (r = 64 u + tid / 8, slot tid % 8) with piece
+  // (tid % 8) ^ act8_swz(r) of weight row r.
+  const BankView bv = bk.shared ? g.shared : g.routed;
+  const uint32_t srow = (uint32_t)K / 32;
+  const size_t mat_rows = GU ? 2 * (size_t)g.I : (size_t)g.H;
+  const uint8_t* wbase = (GU ? bv.gu_codes : bv.d_codes) + (size_t)bk.e * mat_rows * K;
+  const uint8_t* sbase = (GU ? bv.gu_scales : bv.d_scales) + (size_t)bk.e * (mat_rows / 32) * srow;
+  auto wrow = [&](int r) -> uint32_t {
+    return GU ? (uint32_t)(r < 128 ? n0 + r : g.I + n0 + r - 128) : (uint32_t)(n0 + r);
+  };
+  uint32_t b_off[kF8BLoads];
+#pragma unroll
+  for (int u = 0; u < kF8BLoads; ++u) {
+    const int r = 64 * u + (tid >> 3);
+    b_off[u] = wrow(r) * (uint32_t)K + 16u * (uint32_t)((tid & 7) ^ act8_swz(r));
+  }
+  const uint32_t s_lds = lds_base + kStages * kF8StageBytes;
+
+  auto issue = [&](int st, int ks) {
+    const uint32_t base = lds_base + (uint32_t)(st * kF8StageBytes);
+    const uint32_t k0 = (uint32_t)(ks * kBK);
+#pragma unroll
+    for (int u = 0; u < kALoads; ++u)
+      lds_load16(a_src, a_off[u] + 2u * k0, base + (uint32_t)((u * kThreads + 64 * wave) * 16));
+#pragma unroll
+    for (int u = 0; u < kF8BLoads; ++u)
+      lds_load16(wbase, b_off[u] + k0, base + kABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
+  };
+  // scales of the tile's 8 blocks of 32 weight rows, [block][K / 32]
+  auto load_scales = [&]() {
+    load_scale_rows(sbase, [&](int rb) { return (wrow(32 * rb) >> 5) * srow; }, 8, srow, srow,
+                    s_lds, wave, lane, kThreads / 64);
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool active = m0 + 64 * wm < bk.count;
+
+  auto compute = [&](int st, int st_k) {
+    const char* sb = lds + st * kF8StageBytes;
+    const uint4* sa = reinterpret_cast<const uint4*>(sb);
+    const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABytes);
+    const uint8_t* ss = reinterpret_cast<const uint8_t*>(lds + kStages * kF8StageBytes) +
+                        (size_t)st_k * 4 + grp;
+    uint4 lo[4], hi[4];
+    float sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = frag_row<GU>(wn, j, c);
+      const int sw = act8_swz(r);
+      lo[j] = sbk[r * 8 + ((2 * grp) ^ sw)];
+      hi[j] = sbk[r * 8 + ((2 * grp + 1) ^ sw)];
+      sc[j] = e8m0_to_f32(ss[(r >> 5) * srow]);
+    }
+    auto a_frag = [&](int i, int s) {
+      return sa[(64 * wm + 16 * i + c) * 16 + ((4 * grp + s) ^ c)];
+    };
+    auto b_sub = [&](int j, int s) -> Op<GU> {
+      const uint4 v = s < 2 ? lo[j] : hi[j];
+      return (s & 1) ? cvt8_fp8<GU>(v.z, v.w, sc[j]) : cvt8_fp8<GU>(v.x, v.y, sc[j]);
+    };
+    Op<GU> bcur[4], bnext[4];
+    uint4 acur[4], anext[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acur[i] = a_frag(i, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bcur[j] = b_sub(j, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) anext[i] = a_frag(i, s + 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bnext[j] = b_sub(j, s + 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mma<GU>(acur[i], bcur[j], acc[i][j]);
+      if (s < 3) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acur[q] = anext[q];
+          bcur[q] = bnext[q];
+        }
+      }
+    }
+  };
+
+  const int steps = K / kBK;
+  load_scales();
+  issue(0, 0);
+  for (int ks = 0; ks < steps; ++ks) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + 1 < steps) issue((ks + 1) % kStages, ks + 1);
+    if (active) compute(ks % kStages, ks);
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * grp + v;
+      if (m >= bk.count) continue;
+      if constexpr (GU) {
+        _Float16* hr = g.h + (size_t)(bk.begin + m) * g.I + n0 + 32 * wn + c;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) hr[16 * j] = (_Float16)silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+      } else {
+        float* yr = (bk.shared ? g.y_sh + (size_t)m * g.H : g.y + (size_t)(bk.begin + m) * g.H) +
+                    n0 + 64 * wn + c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // MXFP8-activation mode: both operands microscaled, on the gfx950 scaled
 // MFMA (v_mfma_scale_f32_16x16x128_f8f6f4: A = E4M3 activations, B = the
 // bank's E2M1 codes as stored, each with one E8M0 scale per 32 K). The
@@ -840,6 +1040,39 @@ void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s) {
                                                               : gemm_mx_kernel<false, 2>;
   launch("gemm_mx_gateup_kernel", gu, dim3(grid_gu), dim3(kThreads), 0, s, g);
   launch("gemm_mx_down_kernel", dn, dim3(grid_dn), dim3(kThreads), 0, s, g);
+}
+
+size_t fp8_gemm_ws_bytes(int T, int H, int I) {
+  return gemm_layout(nullptr, T, H, I, 0, 0, true).bytes;
+}
+
+// The FP8 expert over all T rows (row t = token t) as the one bucket of the
+// grouped GEMM: no routed experts, the shared slot holds the FP8 bank.
+void launch_fp8_gemm(const Fp8Ffn& p, void* ws, hipStream_t s) {
+  const GemmLayout L = gemm_layout(ws, p.T, p.H, p.I, 0, 0, true);
+  GemmArgs g{};
+  g.x = p.x;
+  g.T = p.T;
+  g.H = p.H;
+  g.I = p.I;
+  g.E = 0;
+  g.R = 0;
+  g.shared = BankView{p.gu_w, p.gu_s, p.d_w, p.d_s, 1};
+  g.routed = g.shared;
+  g.has_shared = 1;
+  const size_t n_gu = (size_t)L.max_rb * L.ncol_gu, n_dn = (size_t)L.max_rb * L.ncol_dn;
+  g.tile_b[0] = L.tiles;
+  g.tile_mn[0] = L.tiles + n_gu;
+  g.tile_b[1] = L.tiles + 2 * n_gu;
+  g.tile_mn[1] = L.tiles + 2 * n_gu + n_dn;
+  g.tile_count = L.tiles + 2 * (n_gu + n_dn);
+  g.max_rb = L.max_rb;
+  g.h = L.h;
+  g.y_sh = p.y;
+  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
+  launch("gemm_fp8w_gateup_kernel", gemm_fp8w_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
+  launch("gemm_fp8w_down_kernel", gemm_fp8w_kernel<false>, dim3(grid_dn), dim3(kThreads), 0, s, g);
 }
 
 bool gemm_supported(int T, int H, int I, int R, bool shared) {

@@ -88,6 +88,24 @@ void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s);
 // bf16 values in blocks of 32 -> E4M3 codes + E8M0 scales (n_blocks blocks).
 void launch_quant_mxfp8(const uint16_t* x, long n_blocks, uint8_t* q, uint8_t* s, hipStream_t st);
 
+// One FP8 expert (E4M3, one E8M0 scale per 32 x 32 block) over T rows,
+// row t = token t: few-token GEMVs (h fp32 [T][I] in `h`) or the grouped
+// GEMM (h fp16 in its own workspace).
+struct Fp8Ffn {
+  const uint16_t* x;     // [T][H] bf16
+  int T, H, I;
+  const uint8_t* gu_w;   // [2][I][H]
+  const uint8_t* gu_s;   // [2][I/32][H/32]
+  const uint8_t* d_w;    // [H][I]
+  const uint8_t* d_s;    // [H/32][I/32]
+  float* h;              // GEMV path: [T][I] fp32 scratch
+  float* y;              // [T][H] fp32 out
+};
+size_t fp8_gemv_ws_bytes(int T, int I);
+void launch_fp8_ffn_gemv(const Fp8Ffn& p, hipStream_t s);  // T <= kDecodeMaxT
+size_t fp8_gemm_ws_bytes(int T, int H, int I);
+void launch_fp8_gemm(const Fp8Ffn& p, void* ws, hipStream_t s);  // where gemm_supported()
+
 // The persistent few-token kernel (layer mode: router..combine in one
 // launch; FFN mode: bucketed rows given by offsets, writes y_rows).
 constexpr int kDecodeMaxT = 16;
@@ -107,6 +125,9 @@ struct DecodeLaunch {
   int32_t* ids_out;
   float* w_out;
   float* y_rows;             // FFN mode output
+  const float* y_shared_ext; // layer mode: [T][H] shared-expert rows computed
+                             // by earlier launches (the combine adds them
+                             // first), or null
 };
 
 size_t decode_ws_bytes(int T, int H, int I, int E, int k, int R, bool ffn, bool shared);

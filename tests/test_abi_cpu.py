@@ -19,7 +19,8 @@ def test_library_exports_every_header_function():
                           "moe_combine", "moe_layer_forward", "moe_workspace_bytes",
                           "moe_status_str", "moe_set_kernel_events",
                           "moe_last_call_launches", "moe_launch_name",
-                          "moe_quantize_mxfp8", "moe_layer_forward_mxfp8_act"}
+                          "moe_quantize_mxfp8", "moe_layer_forward_mxfp8_act",
+                          "moe_expert_ffn_fp8", "moe_layer_forward_fp8_shared"}
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -148,3 +149,26 @@ def test_mxfp8_act_entry_points_validate_before_launching():
     # the workspace covers the mode at every size
     for T in (1, 300, 16384):
         assert M.moe_workspace_bytes(T, 5120, 2304, 384, 6) >= T * 5120 * 33 // 32
+
+
+def test_fp8_entry_points_validate_before_launching():
+    lib = M.lib()
+    good = L.Fp8Bank(FAKE, FAKE, FAKE, FAKE, 1, 256, 128)
+    ffn = lambda b, T=4, ws_bytes=1 << 40, x=FAKE: lib.moe_expert_ffn_fp8(
+        x, ctypes.byref(b), T, FAKE, FAKE, ws_bytes, None)
+    assert ffn(good, x=None) == M.MOE_ERR_INVALID_ARG
+    assert ffn(L.Fp8Bank(FAKE, FAKE, FAKE, FAKE, 2, 256, 128)) == M.MOE_ERR_INVALID_ARG   # E != 1
+    assert ffn(L.Fp8Bank(FAKE + 4, FAKE, FAKE, FAKE, 1, 256, 128)) == M.MOE_ERR_INVALID_ARG
+    assert ffn(L.Fp8Bank(FAKE, FAKE, FAKE, FAKE, 1, 250, 128)) == M.MOE_ERR_INVALID_ARG   # H % 32
+    assert ffn(good, ws_bytes=16) == M.MOE_ERR_WORKSPACE
+    assert ffn(good, T=0) == M.MOE_OK
+    routed = _bank(E=16, H=256, I=128)
+    fwd = lambda sh, T=8: lib.moe_layer_forward_fp8_shared(
+        FAKE, FAKE, None, ctypes.byref(routed), None if sh is None else ctypes.byref(sh), T, 2,
+        FAKE, None, None, FAKE, 1 << 40, None)
+    assert fwd(None) == M.MOE_ERR_INVALID_ARG
+    assert fwd(L.Fp8Bank(FAKE, FAKE, FAKE, FAKE, 1, 256, 96)) == M.MOE_ERR_INVALID_ARG   # I mismatch
+    assert fwd(good, T=0) == M.MOE_OK
+    # the workspace size covers the FP8 paths at every size
+    for T in (1, 5, 16, 17, 2048):
+        assert M.moe_workspace_bytes(T, 5120, 2304, 384, 6) >= T * 5120 * 4
