@@ -14,6 +14,7 @@ from .workloads import (  # noqa: F401
     gen_bank,
     gen_expert,
     gen_fp8_bank,
+    gen_nvfp4_bank,
     gen_inputs,
     gen_router,
     gen_tokens,

@@ -18,6 +18,9 @@ experts of a 6.7 GiB bank without generating the rest):
     [seed, cfg_id, 2, b, 0]        correlated blocks: base vector of block b
     [seed, cfg_id, 2, b, j + 1]    correlated blocks: noise of token j
     [seed, cfg_id, 3]              popularity ranks for the Zipf logit offset
+    [seed, cfg_id, 5, copy, e, m]  NVFP4 expert e (e == E: shared): codes,
+                                   then E4M3 scales per 16, then the fp32
+                                   matrix scale
     [seed, cfg_id, 4, copy, m]     FP8 shared expert (32 x 32 block scales),
                                    matrix m: 0 gate, 1 up, 2 down. Element
                                    bytes first, then scales.
@@ -223,6 +226,47 @@ def gen_fp8_bank(w: Workload, seed: int, copy: int = 0, all_codes: bool = False)
     d = _fp8_matrix([seed, w.cfg_id, 4, copy, 2], H, I, w.exp_lo, w.exp_hi, all_codes=all_codes)
     return dict(gate_up_w=np.stack([g[0], u[0]])[None], gate_up_scales=np.stack([g[1], u[1]])[None],
                 down_w=d[0][None], down_scales=d[1][None], E=1, H=H, I=I)
+
+
+def _nvfp4_matrix(key, n_rows: int, k_cols: int):
+    """Codes [n][k/2] (uniform bytes), E4M3 scale bytes [n][k/16] drawn field
+    by field (sign 0, exponent field uniform in [4, 8], mantissa uniform),
+    and one fp32 matrix scale 2^-5 * (1 + u), u uniform in [0, 1)."""
+    rng = np.random.default_rng(key)
+    codes = rng.integers(0, 256, n_rows * k_cols // 2, dtype=np.uint8).reshape(n_rows, k_cols // 2)
+    n_s = n_rows * k_cols // 16
+    e = rng.integers(4, 9, n_s, dtype=np.uint8)
+    m = rng.integers(0, 8, n_s, dtype=np.uint8)
+    scales = ((e << 3) | m).astype(np.uint8).reshape(n_rows, k_cols // 16)
+    g = np.float32(2.0 ** -5 * (1.0 + rng.random()))
+    return codes, scales, g
+
+
+def gen_nvfp4_bank(w: Workload, seed: int, copy: int = 0, shared: bool = False,
+                   experts=None) -> dict:
+    """NVFP4 bank: gate_up_codes [E][2][I][H/2], gate_up_scales [E][2][I][H/16]
+    (E4M3), down_codes [E][H][I/2], down_scales [E][H][I/16], global_scales
+    [E][3] fp32 (gate, up, down). Unlisted experts stay zero."""
+    E = 1 if shared else w.E
+    H, I = w.H, w.I
+    a = dict(gate_up_codes=np.zeros((E, 2, I, H // 2), np.uint8),
+             gate_up_scales=np.zeros((E, 2, I, H // 16), np.uint8),
+             down_codes=np.zeros((E, H, I // 2), np.uint8),
+             down_scales=np.zeros((E, H, I // 16), np.uint8),
+             global_scales=np.zeros((E, 3), np.float32))
+    ids = [0] if shared else (range(w.E) if experts is None else experts)
+    for slot in ids:
+        e = w.E if shared else slot
+        for m in range(3):
+            n, kk = (I, H) if m < 2 else (H, I)
+            c, s, g = _nvfp4_matrix([seed, w.cfg_id, 5, copy, e, m], n, kk)
+            if m < 2:
+                a["gate_up_codes"][slot, m], a["gate_up_scales"][slot, m] = c, s
+            else:
+                a["down_codes"][slot], a["down_scales"][slot] = c, s
+            a["global_scales"][slot, m] = g
+    a.update(E=E, H=H, I=I)
+    return a
 
 
 # ---------------------------------------------------------------------------
