@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--fp8-shared", action="store_true",
                     help="time moe_layer_forward_fp8_shared: the shared expert in the "
                          "checkpoint's FP8 format (E4M3, 32 x 32 ue8m0 block scales)")
+    ap.add_argument("--nvfp4", action="store_true",
+                    help="time moe_layer_forward_nvfp4: routed and shared experts in NVFP4 "
+                         "(E2M1 codes, E4M3 scale per 16, fp32 matrix scale)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 3 plain device copies of BYTES bytes (the reference "
                          "reading for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -117,18 +120,23 @@ def main() -> int:
 
     # ---- inputs, resident in HBM before timing ----------------------------
     t0 = time.time()
-    routed_np = S.gen_bank(w, 0)
-    shared_np = S.gen_bank(w, 0, shared=True)
-    keys = ("gate_up_codes", "gate_up_scales", "down_codes", "down_scales")
+    if sum([args.nvfp4, args.fp8_shared, args.mxfp8_act]) > 1:
+        log("--nvfp4, --fp8-shared and --mxfp8-act are separate modes")
+        return 2
+    gen = S.gen_nvfp4_bank if args.nvfp4 else S.gen_bank
+    routed_np = gen(w, 0)
+    shared_np = gen(w, 0, shared=True)
+    keys = ("gate_up_codes", "gate_up_scales", "down_codes", "down_scales") + \
+        (("global_scales",) if args.nvfp4 else ())
     ext = {k: torch.from_numpy(np.concatenate([routed_np[k], shared_np[k]], axis=0)).to(dev)
            for k in keys}
     copies = [ext] + [{k: v.clone() for k, v in ext.items()} for _ in range(C - 1)]
     banks = []
+    BT = M.NvBankTensors if args.nvfp4 else M.BankTensors
     for c in copies:
         banks.append(dict(
-            routed=M.BankTensors(*[c[k][: w.E] for k in keys]),
-            shared=M.BankTensors(*[c[k][w.E:] for k in keys]),
-            both=M.BankTensors(*[c[k] for k in keys])))
+            routed=BT(*[c[k][: w.E] for k in keys]),
+            shared=BT(*[c[k][w.E:] for k in keys])))
     if args.fp8_shared:
         if args.mxfp8_act:
             log("--fp8-shared and --mxfp8-act are separate modes")
@@ -153,7 +161,8 @@ def main() -> int:
 
     # Pre-marshalled arguments: the timed loop makes one C call per step.
     fwd_name = ("moe_layer_forward_mxfp8_act" if args.mxfp8_act else
-                "moe_layer_forward_fp8_shared" if args.fp8_shared else "moe_layer_forward")
+                "moe_layer_forward_fp8_shared" if args.fp8_shared else
+                "moe_layer_forward_nvfp4" if args.nvfp4 else "moe_layer_forward")
     fwd = getattr(lib, fwd_name)
     sh = stream.cuda_stream
     ws_n = ws.numel()
@@ -227,6 +236,9 @@ def main() -> int:
             from oracle import fp8_dense as F8O
             layer_fn = F8O.layer_fp8_shared
             shared_np = shared8_np
+        if args.nvfp4:
+            from oracle import nvfp4 as NVO
+            layer_fn = NVO.layer_nvfp4
         try:
             from threadpoolctl import threadpool_info
             cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -260,6 +272,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("mxfp8 x mxfp4 -> fp32" if args.mxfp8_act else
+                  "bf16 x nvfp4 -> fp32" if args.nvfp4 else
                   "bf16 x mxfp4 (shared: bf16 x fp8) -> fp32" if args.fp8_shared else
                   "bf16 x mxfp4 -> fp32"),
         "data": "synthetic",
@@ -267,8 +280,9 @@ def main() -> int:
                    "top_k": w.k, "intermediate": w.I, "shared_experts": 1,
                    "bank_copies": C, "token_batches": P,
                    "expert_activations": "mxfp8" if args.mxfp8_act else "bf16/fp16/fp32",
+                   "expert_format": "nvfp4" if args.nvfp4 else "mxfp4",
                    "shared_expert_format": "fp8 e4m3, 32x32 ue8m0 blocks" if args.fp8_shared
-                   else "mxfp4"},
+                   else "nvfp4" if args.nvfp4 else "mxfp4"},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -394,7 +408,7 @@ def verify_sweep(args, M, S, np, torch):
 # number U of distinct routed experts it touched. Bytes count every array a
 # kernel must read or write once (weights at 17/32 byte per weight: codes plus
 # one E8M0 byte per 32); flops count 2 per multiply-add of the expert FFN.
-def kernel_work(name, w, U, shared=True):
+def kernel_work(name, w, U, shared=True, nvfp4=False):
     H, I, T, R = w.H, w.I, w.T, w.T * w.k
     if name == "fp8_gateup_gemv_kernel":
         # the FP8 shared expert's gate/up: 1 byte per weight, 1 per 32 x 32 block
@@ -405,8 +419,15 @@ def kernel_work(name, w, U, shared=True):
         return "gemm", (T * 2.0 * 2 * H * I, 2 * I * H + T * H * 2 + T * I * 2)
     if name == "gemm_fp8w_down_kernel":
         return "gemm", (T * 2.0 * H * I, H * I + T * I * 2 + T * H * 4)
-    gu_expert = 2 * I * H * 17 // 32       # gate + up of one expert
-    dn_expert = I * H * 17 // 32           # down of one expert
+    # gate + up and down of one expert: MXFP4 17/32 byte per weight, NVFP4
+    # 9/16 (a scale byte per 16) plus its fp32 matrix scales
+    gu_expert = 2 * I * H * 9 // 16 + 8 if nvfp4 else 2 * I * H * 17 // 32
+    dn_expert = I * H * 9 // 16 + 4 if nvfp4 else I * H * 17 // 32
+    if name == "gateup_gemv_kernel":
+        # bucketed rows: the U experts' (+ shared) gate/up read once per 4 rows
+        return "hbm", (U + (1 if shared else 0)) * gu_expert + (R + (T if shared else 0)) * (H * 2 + I * 4)
+    if name == "down_gemv_kernel":
+        return "hbm", (U + (1 if shared else 0)) * dn_expert + (R + (T if shared else 0)) * (I * 4 + H * 4)
     if name == "gateup_fused_kernel":
         # one token: router rows, routing, shared + routed gate/up, and the
         # shared expert's down rows (its h read back, its y row written)
@@ -539,14 +560,15 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
     j = int(np.argmax(mean_ms))
     name, t_ms = names[j], float(mean_ms[j])
     sh = not shared8
-    bound, _ = kernel_work(name, w, 1, sh)
+    nv = bool(getattr(args, "nvfp4", False))
+    bound, _ = kernel_work(name, w, 1, sh, nv)
     if bound is None:
         log(f"[bench] dominant kernel {name}: no algorithmic work model, roofline omitted")
         return None
     # per-launch work averaged over the calls the timed loop made
     if bound == "gemm":
-        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh)[1][0] for i in range(K)]))
-        by = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh)[1][1] for i in range(K)]))
+        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv)[1][0] for i in range(K)]))
+        by = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv)[1][1] for i in range(K)]))
         # the bound is the resource the work needs longer at its peak
         mpeak = MFMA_PEAK_OF.get(name, MFMA_16BIT_PEAK_TFLOPS)
         bound = "mfma" if fl / (mpeak * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm"
@@ -554,7 +576,7 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         log(f"[bench] {name}: {fl / 1e12:.3f} TFLOP, {by / 1e9:.2f} GB unavoidable -> "
             f"bound by {bound.upper()}")
     else:
-        work = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh)[1] for i in range(K)]))
+        work = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv)[1] for i in range(K)]))
     if bound == "hbm":
         ach = work / (t_ms / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"

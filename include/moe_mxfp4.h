@@ -111,6 +111,32 @@ typedef struct moe_fp8_bank {
   int32_t E, H, I;
 } moe_fp8_bank;
 
+/*
+ * An NVFP4 expert bank, the expert format other engines load V4.1 in
+ * (FreeToken issue #444, the comment on the other pull request: "NVFP4
+ * experts"; llama.cpp discussion #28766, "Is it supported?"): E2M1 codes with
+ * one E4M3 scale per 16 (the layout the same issue gives for the model's fp4
+ * KV cache, in the architecture list under janit's comment), plus one fp32
+ * scale per expert and matrix.
+ *
+ *   gate_up_codes  [E][2][I][H/2]   packed as in moe_mxfp4_bank
+ *   gate_up_scales [E][2][I][H/16]  E4M3 (OCP fp8) bytes, one per 16 codes
+ *   down_codes     [E][H][I/2]
+ *   down_scales    [E][H][I/16]
+ *   global_scales  [E][3] fp32 (gate, up, down) multiplying the whole
+ *                  matrix, or NULL for 1
+ *
+ * Code arrays 16-byte aligned, scale arrays 4-byte aligned.
+ */
+typedef struct moe_nvfp4_bank {
+  const uint8_t* gate_up_codes;
+  const uint8_t* gate_up_scales;
+  const uint8_t* down_codes;
+  const uint8_t* down_scales;
+  const float* global_scales;
+  int32_t E, H, I;
+} moe_nvfp4_bank;
+
 /* Workspace bytes that suffice for any call below at these sizes. */
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k);
 
@@ -255,6 +281,29 @@ int moe_layer_forward_fp8_shared(const void* x_bf16, const void* w_router_bf16,
                                  const moe_fp8_bank* shared, int T, int k, float* out,
                                  int32_t* topk_ids_out, float* topk_w_out,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_mxfp4 for an NVFP4 bank: same arguments, buckets, limits and
+ * errors. Weights are dequantised exactly (E2M1 x E4M3 is exact in bf16 and
+ * fp16); the matrix scale multiplies the fp32 sums.
+ */
+int moe_expert_ffn_nvfp4(const void* x_bf16, const moe_nvfp4_bank* bank,
+                         const int32_t* expert_offsets, const int32_t* row_token,
+                         int T, int R, float* y_rows,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_layer_forward with NVFP4 routed experts and, optionally, an NVFP4
+ * shared expert (E = 1). Routing, bucketing, ordering and determinism are
+ * those of moe_layer_forward. Every T runs the separate router, top-k,
+ * bucketing, expert and combine launches (the fused few-token launches take
+ * MXFP4 banks only). moe_workspace_bytes covers its workspace.
+ */
+int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
+                            const float* logit_bias, const moe_nvfp4_bank* routed,
+                            const moe_nvfp4_bank* shared, int T, int k, float* out,
+                            int32_t* topk_ids_out, float* topk_w_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Opt-in mode with MXFP8 activations on the scaled matrix cores.

@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     Fp8Bank,
     Fp8BankTensors,
     MoeError,
+    NvBank,
+    NvBankTensors,
     MOE_ERR_HIP,
     MOE_ERR_INVALID_ARG,
     MOE_ERR_UNSUPPORTED,
@@ -21,11 +23,13 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_expert_ffn_fp8,
     moe_expert_ffn_mxfp4,
+    moe_expert_ffn_nvfp4,
     moe_last_call_launches,
     moe_launch_name,
     moe_layer_forward,
     moe_layer_forward_fp8_shared,
     moe_layer_forward_mxfp8_act,
+    moe_layer_forward_nvfp4,
     moe_permute,
     moe_quantize_mxfp8,
     moe_router_topk,

@@ -12,6 +12,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 # MOE_MXFP4_LIB points the binding at another build of the same library
 LIB_PATH = os.environ.get("MOE_MXFP4_LIB") or os.path.join(PKG, "libmoe_mxfp4.so")
@@ -58,6 +60,21 @@ class Fp8Bank(ctypes.Structure):
     ]
 
 
+class NvBank(ctypes.Structure):
+    """moe_nvfp4_bank: device pointers of one NVFP4 bank plus its sizes."""
+
+    _fields_ = [
+        ("gate_up_codes", ctypes.c_void_p),
+        ("gate_up_scales", ctypes.c_void_p),
+        ("down_codes", ctypes.c_void_p),
+        ("down_scales", ctypes.c_void_p),
+        ("global_scales", ctypes.c_void_p),
+        ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("I", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -74,6 +91,9 @@ _SIGS = {
                                           _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_mxfp8": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_expert_ffn_fp8": (_I, [_P, ctypes.POINTER(Fp8Bank), _I, _P, _P, _SZ, _P]),
+    "moe_expert_ffn_nvfp4": (_I, [_P, ctypes.POINTER(NvBank), _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "moe_layer_forward_nvfp4": (_I, [_P, _P, _P, ctypes.POINTER(NvBank), ctypes.POINTER(NvBank),
+                                      _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward_fp8_shared": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Fp8Bank),
                                            _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_set_kernel_events": (_I, [_P, _I]),
@@ -204,6 +224,41 @@ class Fp8BankTensors:
         return cls(t["gate_up_w"], t["gate_up_scales"], t["down_w"], t["down_scales"])
 
 
+class NvBankTensors:
+    """Keeps the NVFP4 bank tensors alive next to their ctypes struct."""
+
+    def __init__(self, gate_up_codes, gate_up_scales, down_codes, down_scales,
+                 global_scales=None):
+        import torch
+        for n, t in [("gate_up_codes", gate_up_codes), ("gate_up_scales", gate_up_scales),
+                     ("down_codes", down_codes), ("down_scales", down_scales)]:
+            _need(t, n, (torch.uint8,))
+        E, two, I, h2 = gate_up_codes.shape
+        H = 2 * h2
+        if two != 2 or tuple(gate_up_scales.shape) != (E, 2, I, H // 16) \
+                or tuple(down_codes.shape) != (E, H, I // 2) \
+                or tuple(down_scales.shape) != (E, H, I // 16):
+            raise ValueError("NVFP4 bank tensors do not have the [E][2][I][H/2] ... layout")
+        if global_scales is not None:
+            _need(global_scales, "global_scales", (torch.float32,))
+            if tuple(global_scales.shape) != (E, 3):
+                raise ValueError("global_scales must be [E][3]")
+        self.tensors = (gate_up_codes, gate_up_scales, down_codes, down_scales, global_scales)
+        self.E, self.H, self.I = E, H, I
+        self.struct = NvBank(gate_up_codes.data_ptr(), gate_up_scales.data_ptr(),
+                             down_codes.data_ptr(), down_scales.data_ptr(),
+                             None if global_scales is None else global_scales.data_ptr(), E, H, I)
+
+    @classmethod
+    def from_numpy(cls, arrs: dict, device="cuda"):
+        import torch
+        t = {k: torch.from_numpy(arrs[k]).to(device) for k in
+             ("gate_up_codes", "gate_up_scales", "down_codes", "down_scales")}
+        g = arrs.get("global_scales")
+        g = None if g is None else torch.from_numpy(np.asarray(g, np.float32)).to(device)
+        return cls(t["gate_up_codes"], t["gate_up_scales"], t["down_codes"], t["down_scales"], g)
+
+
 # ---------------------------------------------------------------------------
 # The C ABI, one Python function per entry point
 # ---------------------------------------------------------------------------
@@ -332,6 +387,26 @@ def moe_layer_forward_fp8_shared(x, w_router, logit_bias, routed: BankTensors,
                                  shared: Fp8BankTensors, k, out, topk_ids_out=None,
                                  topk_w_out=None, ws=None, stream=None):
     _layer("moe_layer_forward_fp8_shared", x, w_router, logit_bias, routed, shared, k, out,
+           topk_ids_out, topk_w_out, ws, stream)
+
+
+def moe_expert_ffn_nvfp4(x, bank: NvBankTensors, expert_offsets, row_token, R, y_rows, ws,
+                         stream=None):
+    import torch
+    _need(x, "x", _bf16_types(), 2)
+    _need(y_rows, "y_rows", (torch.float32,))
+    T = x.shape[0]
+    st = lib().moe_expert_ffn_nvfp4(_ptr(x), ctypes.byref(bank.struct), _ptr(expert_offsets),
+                                    _ptr(row_token), T, R, _ptr(y_rows), _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream, x))
+    _check("moe_expert_ffn_nvfp4", st)
+
+
+def moe_layer_forward_nvfp4(x, w_router, logit_bias, routed: NvBankTensors,
+                            shared: NvBankTensors | None, k, out, topk_ids_out=None,
+                            topk_w_out=None, ws=None, stream=None):
+    _layer("moe_layer_forward_nvfp4", x, w_router, logit_bias, routed, shared, k, out,
            topk_ids_out, topk_w_out, ws, stream)
 
 

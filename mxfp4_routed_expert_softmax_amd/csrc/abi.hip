@@ -44,6 +44,22 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int check_nv_bank(const moe_nvfp4_bank* b) {
+  if (!b || !b->gate_up_codes || !b->gate_up_scales || !b->down_codes || !b->down_scales)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(b->gate_up_codes) || !aligned16(b->down_codes)) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(b->gate_up_scales) | reinterpret_cast<uintptr_t>(b->down_scales)) & 3u)
+    return MOE_ERR_INVALID_ARG;
+  if (b->E <= 0 || b->H <= 0 || b->I <= 0 || b->H % 32 || b->I % 32) return MOE_ERR_INVALID_ARG;
+  if (b->E > kMaxE || b->H > kMaxH || b->I > kMaxI) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+BankView view_nv(const moe_nvfp4_bank* b) {
+  return BankView{b->gate_up_codes, b->gate_up_scales, b->down_codes, b->down_scales, b->E,
+                  kCodecNvfp4, b->global_scales};
+}
+
 int check_fp8_bank(const moe_fp8_bank* b) {
   if (!b || !b->gate_up_w || !b->gate_up_scales || !b->down_w || !b->down_scales)
     return MOE_ERR_INVALID_ARG;
@@ -500,6 +516,103 @@ int moe_layer_forward_fp8_shared(const void* x_bf16, const void* w_router_bf16,
   if (!shared) return MOE_ERR_INVALID_ARG;
   return layer_forward(x_bf16, w_router_bf16, logit_bias, routed, nullptr, T, k, out,
                        topk_ids_out, topk_w_out, ws, ws_bytes, stream, false, shared);
+}
+
+int moe_expert_ffn_nvfp4(const void* x_bf16, const moe_nvfp4_bank* bank,
+                         const int32_t* expert_offsets, const int32_t* row_token, int T, int R,
+                         float* y_rows, void* ws, size_t ws_bytes, hipStream_t stream) {
+  begin_call();
+  int st = check_nv_bank(bank);
+  if (st != MOE_OK) return st;
+  st = check_dims(T, bank->H, bank->E, 1, bank->I);
+  if (st != MOE_OK) return st;
+  if (R < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0 || R == 0) return MOE_OK;
+  if (!x_bf16 || !y_rows || !aligned16(x_bf16) || !aligned16(y_rows))
+    return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets && bank->E != 1) return MOE_ERR_INVALID_ARG;
+  if (!row_token && R > T) return MOE_ERR_INVALID_ARG;
+  const int E = expert_offsets ? bank->E : 1;
+  const bool mfma = R > kDecodeFfnMaxR && gemm_supported(T, bank->H, bank->I, R, false);
+  const size_t need = mfma ? gemm_ws_bytes(T, bank->H, bank->I, E, R, false)
+                           : ffn_ws_bytes(T, bank->H, bank->I, R, false);
+  if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  FfnProblem p{};
+  p.x = static_cast<const uint16_t*>(x_bf16);
+  p.T = T;
+  p.H = bank->H;
+  p.I = bank->I;
+  p.routed = view_nv(bank);
+  p.offsets = expert_offsets;
+  p.row_token = row_token;
+  p.R = R;
+  p.routed_slots = expert_offsets ? (bank->E < R ? bank->E : R) : 1;
+  p.h = static_cast<float*>(ws);
+  p.y = y_rows;
+  if (mfma)
+    launch_expert_gemm(p, ws, stream);
+  else
+    launch_expert_ffn(p, stream);
+  return launch_status();
+}
+
+int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
+                            const float* logit_bias, const moe_nvfp4_bank* routed,
+                            const moe_nvfp4_bank* shared, int T, int k, float* out,
+                            int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  begin_call();
+  int st = check_nv_bank(routed);
+  if (st != MOE_OK) return st;
+  const int E = routed->E, H = routed->H, I = routed->I;
+  st = check_dims(T, H, E, k, I);
+  if (st != MOE_OK) return st;
+  if (shared) {
+    st = check_nv_bank(shared);
+    if (st != MOE_OK) return st;
+    if (shared->E != 1 || shared->H != H || shared->I != I) return MOE_ERR_INVALID_ARG;
+  }
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !w_router_bf16 || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < layer_ws(nullptr, T, H, I, E, k).bytes) return MOE_ERR_WORKSPACE;
+  const LayerWs L = layer_ws(ws, T, H, I, E, k);
+  int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
+  float* w = topk_w_out ? topk_w_out : L.w;
+  const int R = T * k;
+  launch_router_logits(static_cast<const uint16_t*>(x_bf16),
+                       static_cast<const uint16_t*>(w_router_bf16), logit_bias, T, H, E, L.logits,
+                       stream);
+  launch_topk(L.logits, T, E, k, ids, w, stream);
+  launch_permute(ids, T, k, E, L.offsets, L.row_token, L.inv_row, L.active, L.perm, stream);
+  FfnProblem p{};
+  p.x = static_cast<const uint16_t*>(x_bf16);
+  p.T = T;
+  p.H = H;
+  p.I = I;
+  p.routed = view_nv(routed);
+  p.offsets = L.offsets;
+  p.active = L.active;
+  p.row_token = L.row_token;
+  p.R = R;
+  p.routed_slots = E < R ? E : R;
+  p.h = L.h;
+  p.y = L.y;
+  p.has_shared = shared != nullptr;
+  if (shared) {
+    p.shared = view_nv(shared);
+    p.h_sh = L.h_sh;
+    p.y_sh = L.y_sh;
+  }
+  if (T > kDecodeMaxT && gemm_supported(T, H, I, R, shared != nullptr))
+    launch_expert_gemm(p, L.ffn, stream);
+  else
+    launch_expert_ffn(p, stream);
+  launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
+  return launch_status();
 }
 
 int moe_layer_forward_mxfp8_act(const void* x_bf16, const void* w_router_bf16,

@@ -58,6 +58,7 @@ constexpr int kStageBytes = kABytes + kBBytes;  // 48 KB
 // E8M0 bytes of the tile's 256 weight rows over all of K (K <= 8192: 64 KB),
 // loaded once per tile
 constexpr int kScaleBytes = kWRows * (8192 / 32);
+constexpr int kNvSBytes = kWRows * 8;        // NVFP4: 8 scale bytes per weight row and K step
 constexpr int kALoads = kAPieces / kThreads;  // 4 per thread per stage
 constexpr int kBLoads = kBPieces / kThreads;  // 2 per thread per stage
 
@@ -189,6 +190,37 @@ __device__ __forceinline__ f32x4_t mma(uint4 a, Op<GU> b, f32x4_t c) {
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), b, c, 0, 0, 0);
 }
+// NVFP4: 8 E2M1 codes times an E4M3 scale that is generally not a power of
+// two. The scaled conversions above are only ever given powers of two (an
+// NVFP4 GEMM that passed the E4M3 value there came out 0.71 rel-L2 off, while
+// the GEMV that multiplies after converting matched): convert at scale 1
+// and multiply exactly (E2M1 x E4M3 has at most 6 significant bits), in fp32
+// then packed to bf16 for gate/up, in fp16 for down.
+template <bool GU>
+__device__ __forceinline__ Op<GU> cvt8_nv(uint32_t w, float sc) {
+  if constexpr (GU) {
+    bf16x8_t r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2_t f = q == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)
+                        : q == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1)
+                        : q == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2)
+                                 : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+      r[2 * q] = (__bf16)(f.x * sc);
+      r[2 * q + 1] = (__bf16)(f.y * sc);
+    }
+    return r;
+  } else {
+    const _Float16 h = (_Float16)sc;
+    const f16x2_t s2 = f16x2_t{h, h};
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return f16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  }
+}
+
 __device__ __forceinline__ uint32_t word_of(uint4 v, int s) {
   return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
@@ -248,9 +280,16 @@ __device__ __forceinline__ void load_scale_rows(const void* src, F src_row, int 
     if (lane < (int)(srow >> 2)) lds_load4(src, src_row(r) + 4u * (uint32_t)lane, lds + (uint32_t)r * stride);
 }
 
-template <bool GU>
+// NV: NVFP4 bank (E4M3 scale per 16 codes, fp32 matrix scale). Its scales,
+// 8 bytes per weight row and K step, travel with each stage (the tile's
+// scales over all of K would take 80 KB at K = 5120); a lane's 32 codes
+// span two scales, one for MFMA sub-steps 0-1 and one for 2-3. The
+// products E2M1 x E4M3 are exact in bf16 and fp16; the matrix scale
+// multiplies the fp32 sums in the epilogue.
+template <bool GU, bool NV>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __align__(16) char lds[kStages * kStageBytes + kScaleBytes];  // 160 KB
+  constexpr int kSt = NV ? kStageBytes + kNvSBytes : kStageBytes;   // bytes per stage
+  __shared__ __align__(16) char lds[NV ? kStages * kSt : kStages * kSt + kScaleBytes];
   constexpr int kBN = GU ? kWRows / 2 : kWRows;  // output columns per tile
   const int N = GU ? g.I : g.H;
   const int K = GU ? g.H : g.I;
@@ -298,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // B: thread tid fills code slot (r = 128 u + tid / 4, piece tid % 4),
   // which holds piece (tid % 4) ^ ((r / 4) % 4) of weight row r.
   const BankView bv = bk.shared ? g.shared : g.routed;
-  const uint32_t crow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
+  const uint32_t crow = (uint32_t)K / 2, srow = (uint32_t)K / (NV ? 16 : 32);
   const size_t mat_rows = GU ? 2 * (size_t)g.I : (size_t)g.H;
   const uint8_t* cbase = (GU ? bv.gu_codes : bv.d_codes) + (size_t)bk.e * mat_rows * crow;
   const uint8_t* sbase = (GU ? bv.gu_scales : bv.d_scales) + (size_t)bk.e * mat_rows * srow;
@@ -311,11 +350,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     const int r = 128 * u + (tid >> 2);
     b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
   }
-  const uint32_t s_lds = lds_base + kStages * kStageBytes;
+  const uint32_t s_lds = lds_base + kStages * kSt;
+  // NV: thread tid copies dword tid % 2 of weight row tid / 2's 8 scale
+  // bytes of each K step into the stage
+  const uint32_t nv_off = NV ? wrow(tid >> 1) * srow + 4u * (uint32_t)(tid & 1) : 0u;
 
   // Stage `st` <- K step `ks`.
   auto issue = [&](int st, int ks) {
-    const uint32_t base = lds_base + (uint32_t)(st * kStageBytes);
+    const uint32_t base = lds_base + (uint32_t)(st * kSt);
     const uint32_t k0 = (uint32_t)(ks * kBK);
 #pragma unroll
     for (int u = 0; u < kALoads; ++u)
@@ -324,7 +366,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     for (int u = 0; u < kBLoads; ++u)
       lds_load16(cbase, b_off[u] + k0 / 2,
                  base + kABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
-
+    if constexpr (NV)
+      lds_load4(sbase, nv_off + k0 / 16, base + kABytes + kBBytes + (uint32_t)(64 * wave * 4));
   };
   // The tile's scales: rows r of the tile (gate/up: two runs of 128 rows,
   // down: one run of 256), srow bytes each, contiguous in the bank and in
@@ -354,18 +397,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // MFMAs of sub-step s run, the A fragments of s + 1 are read from LDS and
   // its B fragments converted, into a second set of registers.
   auto compute = [&](int st, int st_k) {
-    const char* sb = lds + st * kStageBytes;
+    const char* sb = lds + st * kSt;
     const uint4* sa = reinterpret_cast<const uint4*>(sb);
     const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABytes);
-    const uint8_t* ss = reinterpret_cast<const uint8_t*>(lds + kStages * kStageBytes) +
+    const uint8_t* ss = reinterpret_cast<const uint8_t*>(lds + kStages * kSt) +
                         (size_t)st_k * 4;  // this K step's 4 scale bytes of each row
+    const uint16_t* ssn = reinterpret_cast<const uint16_t*>(sb + kABytes + kBBytes);
     uint4 bc[4];
-    float sc[4];
+    float sc[4], sc2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = frag_row<GU>(wn, j, c);
       bc[j] = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
-      sc[j] = e8m0_to_f32(ss[r * srow + grp]);
+      if constexpr (NV) {
+        const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ssn[r * 4 + grp], 1.0f, false);
+        sc[j] = f.x;
+        sc2[j] = f.y;
+      } else {
+        sc[j] = sc2[j] = e8m0_to_f32(ss[r * srow + grp]);
+      }
     }
     // A row 64 wm + 16 i + c, K values 32 grp + 8 s: piece 4 grp + s
     auto a_frag = [&](int i, int s) {
@@ -376,14 +426,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acur[i] = a_frag(i, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bcur[j] = cvt8<GU>(word_of(bc[j], 0), sc[j]);
+    for (int j = 0; j < 4; ++j) {  // sub-step 0
+      if constexpr (NV)
+        bcur[j] = cvt8_nv<GU>(word_of(bc[j], 0), sc[j]);
+      else
+        bcur[j] = cvt8<GU>(word_of(bc[j], 0), sc[j]);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) anext[i] = a_frag(i, s + 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bnext[j] = cvt8<GU>(word_of(bc[j], s + 1), sc[j]);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (NV)
+            bnext[j] = cvt8_nv<GU>(word_of(bc[j], s + 1), s + 1 < 2 ? sc[j] : sc2[j]);
+          else
+            bnext[j] = cvt8<GU>(word_of(bc[j], s + 1), sc[j]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -404,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // stage ks visible to every wave and frees the other buffer (read at
   // step ks - 1) for ks + 1.
   const int steps = K / kBK;
-  load_scales();
+  if constexpr (!NV) load_scales();
   issue(0, 0);
   for (int ks = 0; ks < steps; ++ks) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -415,6 +475,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
   // D layout: lane (c, grp), element v -> row 4 grp + v, column c
   if (!active) return;
+  float mg = 1.0f, mu = 1.0f;
+  if constexpr (NV) {
+    if (bv.gscale) {
+      mg = bv.gscale[bk.e * 3 + (GU ? 0 : 2)];
+      mu = bv.gscale[bk.e * 3 + 1];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -424,12 +491,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
       if constexpr (GU) {
         _Float16* hr = g.h + (size_t)(bk.begin + m) * g.I + n0 + 32 * wn + c;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) hr[16 * j] = (_Float16)silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+        for (int j = 0; j < 2; ++j) {
+          if constexpr (NV)
+            hr[16 * j] = (_Float16)silu_mul(acc[i][j][v] * mg, acc[i][j + 2][v] * mu);
+          else
+            hr[16 * j] = (_Float16)silu_mul(acc[i][j][v], acc[i][j + 2][v]);
+        }
       } else {
         float* yr = (bk.shared ? g.y_sh + (size_t)m * g.H : g.y + (size_t)(bk.begin + m) * g.H) +
                     n0 + 64 * wn + c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][v];
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (NV)
+            yr[16 * j] = acc[i][j][v] * mg;
+          else
+            yr[16 * j] = acc[i][j][v];
+        }
       }
     }
   }
@@ -1114,8 +1191,11 @@ void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
   // grids: every tile the lists can hold, rounded up to the 8 XCDs
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
-  launch("gemm_gateup_kernel", gemm_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
-  launch("gemm_down_kernel", gemm_kernel<false>, dim3(grid_dn), dim3(kThreads), 0, s, g);
+  const bool nv = p.routed.codec == kCodecNvfp4;
+  launch("gemm_gateup_kernel", nv ? gemm_kernel<true, true> : gemm_kernel<true, false>,
+         dim3(grid_gu), dim3(kThreads), 0, s, g);
+  launch("gemm_down_kernel", nv ? gemm_kernel<false, true> : gemm_kernel<false, false>,
+         dim3(grid_dn), dim3(kThreads), 0, s, g);
 }
 
 }  // namespace moe

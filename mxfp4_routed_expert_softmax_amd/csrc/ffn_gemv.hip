@@ -78,8 +78,18 @@ __device__ __forceinline__ SlotInfo resolve_slot(const FfnProblem& p, int s) {
   return si;
 }
 
+// Matrix scale of an NVFP4 bank (1 when absent or MXFP4).
+__device__ __forceinline__ float matrix_scale(const BankView& b, int e, int m) {
+  return (b.codec == kCodecNvfp4 && b.gscale) ? b.gscale[e * 3 + m] : 1.0f;
+}
+// The two E4M3 scales of a 32-code chunk (NVFP4), from their two bytes.
+__device__ __forceinline__ f32x2_t e4m3x2_to_f32(uint32_t two_bytes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two_bytes, 1.0f, false);
+}
+
 // gate/up + SwiGLU: h[row][n] = silu(W_g[n] . x) * (W_u[n] . x), K = H.
-template <int U>
+// NV: NVFP4 bank (two E4M3 scales per 32-code chunk, one per 16 codes).
+template <int U, bool NV>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(FfnProblem p) {
   extern __shared__ __align__(16) uint4 s_x[];  // [kGemvMT][H/8] bf16
   const SlotInfo si = resolve_slot(p, blockIdx.y);
@@ -92,7 +102,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(FfnProblem p)
   const bool row_ok = n < I;
   const int nr = row_ok ? n : I - 1;
   const int kc = H >> 5;
-  const size_t crow = (size_t)H >> 1, srow = (size_t)H >> 5;
+  const size_t crow = (size_t)H >> 1, srow = (size_t)H >> (NV ? 4 : 5);
   const uint8_t* gc = bk.gu_codes + ((size_t)si.e * 2 * I + nr) * crow;
   const uint8_t* uc = gc + (size_t)I * crow;
   const uint8_t* gs = bk.gu_scales + ((size_t)si.e * 2 * I + nr) * srow;
@@ -123,15 +133,27 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(FfnProblem p)
         if (c < kc) {
           wg[u] = *reinterpret_cast<const uint4*>(gc + (size_t)c * 16);
           wu[u] = *reinterpret_cast<const uint4*>(uc + (size_t)c * 16);
-          sg[u] = gs[c];
-          su[u] = us[c];
+          if constexpr (NV) {
+            sg[u] = *reinterpret_cast<const uint16_t*>(gs + 2 * (size_t)c);
+            su[u] = *reinterpret_cast<const uint16_t*>(us + 2 * (size_t)c);
+          } else {
+            sg[u] = gs[c];
+            su[u] = us[c];
+          }
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + 8 * u + j;
         if (c < kc) {
-          const float fg = e8m0_to_f32(sg[u]), fu = e8m0_to_f32(su[u]);
+          f32x2_t fg, fu;
+          if constexpr (NV) {
+            fg = e4m3x2_to_f32(sg[u]);
+            fu = e4m3x2_to_f32(su[u]);
+          } else {
+            fg.x = fg.y = e8m0_to_f32(sg[u]);
+            fu.x = fu.y = e8m0_to_f32(su[u]);
+          }
 #pragma unroll
           for (int t = 0; t < kGemvMT; ++t) {
             if (t < nt) {
@@ -139,30 +161,38 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(FfnProblem p)
               const uint4 x0 = xv[0], x1 = xv[1], x2 = xv[2], x3 = xv[3];
               float pg = dot8_fp4_bf16(wg[u].x, x0, 0.0f);
               pg = dot8_fp4_bf16(wg[u].y, x1, pg);
-              pg = dot8_fp4_bf16(wg[u].z, x2, pg);
-              pg = dot8_fp4_bf16(wg[u].w, x3, pg);
+              float pg1 = NV ? 0.0f : pg;
+              pg1 = dot8_fp4_bf16(wg[u].z, x2, pg1);
+              pg1 = dot8_fp4_bf16(wg[u].w, x3, pg1);
               float pu = dot8_fp4_bf16(wu[u].x, x0, 0.0f);
               pu = dot8_fp4_bf16(wu[u].y, x1, pu);
-              pu = dot8_fp4_bf16(wu[u].z, x2, pu);
-              pu = dot8_fp4_bf16(wu[u].w, x3, pu);
-              ag[t] = fmaf(pg, fg, ag[t]);
-              au[t] = fmaf(pu, fu, au[t]);
+              float pu1 = NV ? 0.0f : pu;
+              pu1 = dot8_fp4_bf16(wu[u].z, x2, pu1);
+              pu1 = dot8_fp4_bf16(wu[u].w, x3, pu1);
+              if constexpr (NV) {
+                ag[t] = fmaf(pg1, fg.y, fmaf(pg, fg.x, ag[t]));
+                au[t] = fmaf(pu1, fu.y, fmaf(pu, fu.x, au[t]));
+              } else {
+                ag[t] = fmaf(pg1, fg.x, ag[t]);
+                au[t] = fmaf(pu1, fu.x, au[t]);
+              }
             }
           }
         }
       }
     }
+    const float mg = matrix_scale(bk, si.e, 0), mu = matrix_scale(bk, si.e, 1);
 #pragma unroll
     for (int t = 0; t < kGemvMT; ++t) {
-      const float g = group_sum<8>(ag[t]);
-      const float u = group_sum<8>(au[t]);
+      const float g = group_sum<8>(ag[t]) * mg;
+      const float u = group_sum<8>(au[t]) * mu;
       if (row_ok && j == 0 && t < nt) hout[(size_t)(si.row0 + t0 + t) * I + n] = silu_mul(g, u);
     }
   }
 }
 
 // down: y[row][n] = W_d[n] . h[row], K = I, h in fp32.
-template <int U>
+template <int U, bool NV>
 __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(FfnProblem p) {
   extern __shared__ __align__(16) f32x4_t s_h[];  // [kGemvMT][I/4] fp32
   const SlotInfo si = resolve_slot(p, blockIdx.y);
@@ -175,7 +205,7 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(FfnProblem p) {
   const bool row_ok = n < H;
   const int nr = row_ok ? n : H - 1;
   const int kc = I >> 5;
-  const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 5;
+  const size_t crow = (size_t)I >> 1, srow = (size_t)I >> (NV ? 4 : 5);
   const uint8_t* dc = bk.d_codes + ((size_t)si.e * H + nr) * crow;
   const uint8_t* ds = bk.d_scales + ((size_t)si.e * H + nr) * srow;
   const int vpr = I >> 2;
@@ -201,31 +231,43 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(FfnProblem p) {
         const int c = c0 + 8 * u + j;
         if (c < kc) {
           wd[u] = *reinterpret_cast<const uint4*>(dc + (size_t)c * 16);
-          sd[u] = ds[c];
+          if constexpr (NV)
+            sd[u] = *reinterpret_cast<const uint16_t*>(ds + 2 * (size_t)c);
+          else
+            sd[u] = ds[c];
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + 8 * u + j;
         if (c < kc) {
-          const float fd = e8m0_to_f32(sd[u]);
+          f32x2_t fd;
+          if constexpr (NV)
+            fd = e4m3x2_to_f32(sd[u]);
+          else
+            fd.x = fd.y = e8m0_to_f32(sd[u]);
 #pragma unroll
           for (int t = 0; t < kGemvMT; ++t) {
             if (t < nt) {
               const f32x4_t* hv = s_h + t * vpr + c * 8;
               float pd = dot8_fp4_f32(wd[u].x, hv[0], hv[1], 0.0f);
               pd = dot8_fp4_f32(wd[u].y, hv[2], hv[3], pd);
-              pd = dot8_fp4_f32(wd[u].z, hv[4], hv[5], pd);
-              pd = dot8_fp4_f32(wd[u].w, hv[6], hv[7], pd);
-              acc[t] = fmaf(pd, fd, acc[t]);
+              float pd1 = NV ? 0.0f : pd;
+              pd1 = dot8_fp4_f32(wd[u].z, hv[4], hv[5], pd1);
+              pd1 = dot8_fp4_f32(wd[u].w, hv[6], hv[7], pd1);
+              if constexpr (NV)
+                acc[t] = fmaf(pd1, fd.y, fmaf(pd, fd.x, acc[t]));
+              else
+                acc[t] = fmaf(pd1, fd.x, acc[t]);
             }
           }
         }
       }
     }
+    const float md = matrix_scale(bk, si.e, 2);
 #pragma unroll
     for (int t = 0; t < kGemvMT; ++t) {
-      const float v = group_sum<8>(acc[t]);
+      const float v = group_sum<8>(acc[t]) * md;
       if (row_ok && j == 0 && t < nt) yout[(size_t)(si.row0 + t0 + t) * H + n] = v;
     }
   }
@@ -243,10 +285,11 @@ void launch_expert_ffn(const FfnProblem& p, hipStream_t s) {
   if (slots == 0) return;
   const size_t lds_gu = (size_t)kGemvMT * p.H * sizeof(uint16_t);
   const size_t lds_d = (size_t)kGemvMT * p.I * sizeof(float);
-  launch("gateup_gemv_kernel", gateup_gemv_kernel<5>,
+  const bool nv = p.routed.codec == kCodecNvfp4;
+  launch("gateup_gemv_kernel", nv ? gateup_gemv_kernel<5, true> : gateup_gemv_kernel<5, false>,
                      dim3((p.I + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock, slots),
                      dim3(kGemvThreads), lds_gu, s, p);
-  launch("down_gemv_kernel", down_gemv_kernel<9>,
+  launch("down_gemv_kernel", nv ? down_gemv_kernel<9, true> : down_gemv_kernel<9, false>,
                      dim3((p.H + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock, slots),
                      dim3(kGemvThreads), lds_d, s, p);
 }

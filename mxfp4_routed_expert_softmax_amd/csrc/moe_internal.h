@@ -42,14 +42,21 @@ void launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                     int32_t* row_token, int32_t* inv_row, int32_t* active,
                     void* ws, hipStream_t s);
 
-// One MXFP4 bank as the kernels see it.
+// One expert bank as the kernels see it. codec 0: MXFP4 (E8M0 scale per
+// 32 codes); codec 1: NVFP4 (E4M3 scale per 16 codes, scale rows K / 16
+// bytes, plus an optional fp32 scale per expert and matrix, gscale [E][3]:
+// gate, up, down). The few-token persistent kernels take MXFP4 only.
 struct BankView {
   const uint8_t* gu_codes;
   const uint8_t* gu_scales;
   const uint8_t* d_codes;
   const uint8_t* d_scales;
   int E;
+  int codec;
+  const float* gscale;
 };
+constexpr int kCodecMxfp4 = 0;
+constexpr int kCodecNvfp4 = 1;
 
 // Expert FFN over bucketed rows: routed bank rows (offsets/active/row_token)
 // plus, optionally, the shared expert over all T tokens.

@@ -255,7 +255,8 @@ def gen_nvfp4_bank(w: Workload, seed: int, copy: int = 0, shared: bool = False,
              down_scales=np.zeros((E, H, I // 16), np.uint8),
              global_scales=np.zeros((E, 3), np.float32))
     ids = [0] if shared else (range(w.E) if experts is None else experts)
-    for slot in ids:
+
+    def fill(slot: int) -> None:
         e = w.E if shared else slot
         for m in range(3):
             n, kk = (I, H) if m < 2 else (H, I)
@@ -265,6 +266,14 @@ def gen_nvfp4_bank(w: Workload, seed: int, copy: int = 0, shared: bool = False,
             else:
                 a["down_codes"][slot], a["down_scales"][slot] = c, s
             a["global_scales"][slot, m] = g
+
+    n = _threads()
+    if n > 1 and len(ids) > 1:
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(fill, ids))
+    else:
+        for slot in ids:
+            fill(slot)
     a.update(E=E, H=H, I=I)
     return a
 

@@ -20,7 +20,8 @@ def test_library_exports_every_header_function():
                           "moe_status_str", "moe_set_kernel_events",
                           "moe_last_call_launches", "moe_launch_name",
                           "moe_quantize_mxfp8", "moe_layer_forward_mxfp8_act",
-                          "moe_expert_ffn_fp8", "moe_layer_forward_fp8_shared"}
+                          "moe_expert_ffn_fp8", "moe_layer_forward_fp8_shared",
+                          "moe_expert_ffn_nvfp4", "moe_layer_forward_nvfp4"}
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -172,3 +173,22 @@ def test_fp8_entry_points_validate_before_launching():
     # the workspace size covers the FP8 paths at every size
     for T in (1, 5, 16, 17, 2048):
         assert M.moe_workspace_bytes(T, 5120, 2304, 384, 6) >= T * 5120 * 4
+
+
+def test_nvfp4_entry_points_validate_before_launching():
+    lib = M.lib()
+    good = L.NvBank(FAKE, FAKE, FAKE, FAKE, None, 16, 256, 128)
+    fwd = lambda b, sh=None, T=8, k=2, ws_bytes=1 << 40: lib.moe_layer_forward_nvfp4(
+        FAKE, FAKE, None, ctypes.byref(b), None if sh is None else ctypes.byref(sh), T, k, FAKE,
+        None, None, FAKE, ws_bytes, None)
+    assert fwd(L.NvBank(FAKE, FAKE + 2, FAKE, FAKE, None, 16, 256, 128)) == M.MOE_ERR_INVALID_ARG
+    assert fwd(L.NvBank(FAKE + 4, FAKE, FAKE, FAKE, None, 16, 256, 128)) == M.MOE_ERR_INVALID_ARG
+    assert fwd(good, sh=L.NvBank(FAKE, FAKE, FAKE, FAKE, None, 2, 256, 128)) == M.MOE_ERR_INVALID_ARG
+    assert fwd(good, k=17) == M.MOE_ERR_INVALID_ARG
+    assert fwd(good, ws_bytes=16) == M.MOE_ERR_WORKSPACE
+    assert fwd(good, T=0) == M.MOE_OK
+    ffn = lambda b, R=8, off=FAKE: lib.moe_expert_ffn_nvfp4(FAKE, ctypes.byref(b), off, FAKE, 8, R,
+                                                           FAKE, FAKE, 1 << 40, None)
+    assert ffn(good, off=None) == M.MOE_ERR_INVALID_ARG   # E > 1 needs offsets
+    assert ffn(good, R=-1) == M.MOE_ERR_INVALID_ARG
+    assert ffn(good, R=0) == M.MOE_OK

@@ -1,0 +1,161 @@
+"""Parity of the NVFP4 expert path (moe_expert_ffn_nvfp4,
+moe_layer_forward_nvfp4) with the fp64 oracle, oracle.nvfp4.
+
+Bars: the weights are dequantised exactly on both sides (E2M1 x E4M3 is
+exact in bf16 and fp16), the matrix scale costs one fp32 rounding of each
+sum. So the GEMVs (fp32 h) differ from the oracle by fp32 summation only
+(FP32_TOL), the grouped GEMM carries h in fp16 (GEMM_TOL), and the layer
+takes the routing rules and output bar of the default mode.
+"""
+
+import numpy as np
+import pytest
+import scipy.special
+
+import synthetic as S
+from oracle import moe as O
+from oracle import nvfp4 as N
+from tests import _helpers as HP
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+M = pytest.importorskip("mxfp4_routed_expert_softmax_amd")
+
+MID = S.Workload("nv_mid", 97, T=300, H=512, E=6, k=2, I=256, exp_lo=-6, exp_hi=-3, zipf_s=1.5)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    M.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _names():
+    return [M.moe_launch_name(i) for i in range(M.moe_last_call_launches())]
+
+
+def run_ffn(x_bits, bank_np, offsets, row_token, R):
+    T, H = x_bits.shape
+    bank = M.NvBankTensors.from_numpy(bank_np, HP.dev())
+    y = torch.empty((R, H), dtype=torch.float32, device=HP.dev())
+    ws = M.workspace(T, H, bank.I, bank.E, max(1, -(-R // T)), HP.dev())
+    off = None if offsets is None else HP.to_dev(np.asarray(offsets, np.int32))
+    rt = None if row_token is None else HP.to_dev(np.asarray(row_token, np.int32))
+    M.moe_expert_ffn_nvfp4(HP.to_dev(x_bits), bank, off, rt, R, y, ws)
+    return _np(y), _names()
+
+
+@pytest.mark.parametrize("w,tol,kernel", [(S.get("tiny"), HP.FP32_TOL, "gateup_gemv_kernel"),
+                                          (MID, HP.GEMM_TOL, "gemm_gateup_kernel")],
+                         ids=["gemv", "gemm"])
+def test_ffn_bucketed_rows(w, tol, kernel):
+    x, wr, bias = S.gen_tokens(w, 1), S.gen_router(w, 1), S.gen_zipf_bias(w, 1)
+    bank = S.gen_nvfp4_bank(w, 1)
+    r = O.route(x, wr, bias, w.k)
+    y, names = run_ffn(x, bank, r["offsets"], r["row_token"], w.R)
+    ref = N.expert_rows_nvfp4(r["x"], bank, r["offsets"], r["row_token"])
+    err = HP.rel_l2(y, ref)
+    print(w.name, names, err)
+    assert kernel in names
+    assert err < tol
+
+
+@pytest.mark.parametrize("T", [4, 300])
+def test_ffn_identity_probe(T):
+    n = 256
+    codes = np.zeros((n, n // 2), np.uint8)
+    for i in range(n):
+        codes[i, i // 2] = 0x2 if i % 2 == 0 else 0x20
+    sc = np.full((n, n // 16), 0x38, np.uint8)
+    bank = dict(gate_up_codes=np.stack([codes, codes])[None], gate_up_scales=np.stack([sc, sc])[None],
+                down_codes=codes[None], down_scales=sc[None],
+                global_scales=np.array([[2.0, 0.5, 0.25]], np.float32))
+    x = S.gen_tokens(S.Workload("eye", 98, T=T, H=n, E=1, k=1, I=n, exp_lo=0, exp_hi=0), 0)
+    y, names = run_ffn(x, bank, None, None, T)
+    xf = O.bf16_to_f64(x)
+    ref = 0.25 * (2 * xf) * scipy.special.expit(2 * xf) * (0.5 * xf)
+    assert HP.rel_l2(y, ref) < (HP.FP32_TOL if T <= 128 else HP.GEMM_TOL)
+
+
+def run_layer(x_bits, wr_bits, bias, routed_np, shared_np, k):
+    T = x_bits.shape[0]
+    rd = M.NvBankTensors.from_numpy(routed_np, HP.dev())
+    sd = None if shared_np is None else M.NvBankTensors.from_numpy(shared_np, HP.dev())
+    out = torch.empty((T, rd.H), dtype=torch.float32, device=HP.dev())
+    ids = torch.empty((T, k), dtype=torch.int32, device=HP.dev())
+    wt = torch.empty((T, k), dtype=torch.float32, device=HP.dev())
+    ws = M.workspace(T, rd.H, rd.I, rd.E, k, HP.dev())
+    b = None if bias is None else HP.to_dev(bias)
+    M.moe_layer_forward_nvfp4(HP.to_dev(x_bits), HP.to_dev(wr_bits), b, rd, sd, k, out, ids, wt, ws)
+    return _np(out), _np(ids), _np(wt), _names()
+
+
+def _parity(w, x, wr, bias, routed, shared, tokens=None, tol=HP.OUT_TOL):
+    ref = N.layer_nvfp4(x, wr, bias, routed, shared, w.k, tokens=tokens)
+    out, ids, wt, names = run_layer(x, wr, bias, routed, shared, w.k)
+    tok = ref["tokens"]
+    alt = HP.check_routing(ref, ids, wt, w.k)
+    rows = [N.token_out_with_nvfp4(ref["x"], ref["logits"], t, alt[t], routed,
+                                   None if ref["y_shared"] is None else ref["y_shared"][i])
+            if t in alt else ref["out"][i] for i, t in enumerate(tok)]
+    err = HP.rel_l2(out[tok], np.stack(rows))
+    print(f"{w.name}: rel-L2 {err:.3e} over {len(tok)} tokens; {names}")
+    assert err <= tol
+    return err
+
+
+def test_layer_tiny_with_and_without_shared():
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    routed = S.gen_nvfp4_bank(w, 0)
+    assert _parity(w, d["x"], d["w_router"], None, routed, S.gen_nvfp4_bank(w, 0, shared=True)) \
+        < HP.FP32_TOL
+    _parity(w, d["x"], d["w_router"], np.linspace(-1, 1, w.E).astype(np.float32), routed, None)
+
+
+def _selected(w, x, wr):
+    r = O.route(x, wr, None, w.k)
+    sel = set(r["ids"].reshape(-1).tolist())
+    for t in range(x.shape[0]):
+        if r["margin"][t] <= HP.MARGIN:
+            for c in O.near_tie_candidates(r["logits"][t], w.k):
+                sel |= set(c)
+    return sorted(sel)
+
+
+@pytest.mark.parametrize("name", ["decode", "spec5"])
+def test_layer_real_shape_few_tokens(name):
+    w = S.get(name)
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    routed = S.gen_nvfp4_bank(w, 0, experts=_selected(w, x, wr))
+    assert _parity(w, x, wr, None, routed, S.gen_nvfp4_bank(w, 0, shared=True)) < 1e-4
+
+
+def test_layer_gemm_ragged_and_prefill_sampled():
+    w = MID
+    x, wr, bias = S.gen_tokens(w, 3), S.gen_router(w, 3), S.gen_zipf_bias(w, 3)
+    _parity(w, x, wr, bias, S.gen_nvfp4_bank(w, 3), S.gen_nvfp4_bank(w, 3, shared=True),
+            tol=HP.GEMM_TOL)
+    w = S.get("prefill2k_zipf")
+    x, wr, bias = S.gen_tokens(w, 0), S.gen_router(w, 0), S.gen_zipf_bias(w, 0)
+    _parity(w, x, wr, bias, S.gen_nvfp4_bank(w, 0), S.gen_nvfp4_bank(w, 0, shared=True),
+            tokens=[0, 1, 1024, 2047], tol=HP.GEMM_TOL)
+
+
+def test_layer_is_bitwise_deterministic():
+    w = MID
+    x, wr = S.gen_tokens(w, 5), S.gen_router(w, 5)
+    routed, shared = S.gen_nvfp4_bank(w, 5), S.gen_nvfp4_bank(w, 5, shared=True)
+    a = run_layer(x, wr, None, routed, shared, w.k)
+    b = run_layer(x, wr, None, routed, shared, w.k)
+    for u, v in zip(a[:3], b[:3]):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
