@@ -408,8 +408,14 @@ def verify_sweep(args, M, S, np, torch):
 # number U of distinct routed experts it touched. Bytes count every array a
 # kernel must read or write once (weights at 17/32 byte per weight: codes plus
 # one E8M0 byte per 32); flops count 2 per multiply-add of the expert FFN.
-def kernel_work(name, w, U, shared=True, nvfp4=False):
+def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
     H, I, T, R = w.H, w.I, w.T, w.T * w.k
+    if name == "gateup_fused_kernel" and shared8:
+        # one token with the FP8 shared expert streamed in the same launch:
+        # the MXFP4 routed work plus the FP8 expert (1 byte per weight, 1 per
+        # 32 x 32 block), its h row written and read back and its y row
+        _, b = kernel_work(name, w, U, False)
+        return "hbm", b + 3 * H * I + 3 * (H // 32) * (I // 32) + T * I * 8 + T * H * 4
     if name == "fp8_gateup_gemv_kernel":
         # the FP8 shared expert's gate/up: 1 byte per weight, 1 per 32 x 32 block
         return "hbm", 2 * I * H + 2 * (I // 32) * (H // 32) + T * H * 2 + T * I * 4
@@ -561,14 +567,14 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
     name, t_ms = names[j], float(mean_ms[j])
     sh = not shared8
     nv = bool(getattr(args, "nvfp4", False))
-    bound, _ = kernel_work(name, w, 1, sh, nv)
+    bound, _ = kernel_work(name, w, 1, sh, nv, shared8)
     if bound is None:
         log(f"[bench] dominant kernel {name}: no algorithmic work model, roofline omitted")
         return None
     # per-launch work averaged over the calls the timed loop made
     if bound == "gemm":
-        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv)[1][0] for i in range(K)]))
-        by = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv)[1][1] for i in range(K)]))
+        fl = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv, shared8)[1][0] for i in range(K)]))
+        by = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv, shared8)[1][1] for i in range(K)]))
         # the bound is the resource the work needs longer at its peak
         mpeak = MFMA_PEAK_OF.get(name, MFMA_16BIT_PEAK_TFLOPS)
         bound = "mfma" if fl / (mpeak * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm"
@@ -576,7 +582,7 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         log(f"[bench] {name}: {fl / 1e12:.3f} TFLOP, {by / 1e9:.2f} GB unavoidable -> "
             f"bound by {bound.upper()}")
     else:
-        work = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv)[1] for i in range(K)]))
+        work = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv, shared8)[1] for i in range(K)]))
     if bound == "hbm":
         ach = work / (t_ms / 1e3) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"

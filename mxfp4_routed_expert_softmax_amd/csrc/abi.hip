@@ -80,9 +80,13 @@ size_t fp8_ffn_ws(int T, int H, int I) {
 
 // Workspace of the few-token layer with an FP8 shared expert: the decode
 // path's (no MXFP4 shared expert), then y_sh [T][H], then the FP8 scratch.
+// (One token may instead stream the FP8 expert inside the fused launches,
+// which needs the decode layout with a shared expert.)
 size_t few_fp8_ws(int T, int H, int I, int E, int k) {
-  return align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false)) +
-         align_up((size_t)T * H * sizeof(float)) + fp8_ffn_ws(T, H, I);
+  const size_t sep = align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false)) +
+                     align_up((size_t)T * H * sizeof(float)) + fp8_ffn_ws(T, H, I);
+  const size_t fused = decode_ws_bytes(T, H, I, E, k, T * k, false, true);
+  return sep > fused ? sep : fused;
 }
 
 // The FP8 expert over rows x[0..T) into y[0..T); `scratch` holds fp8_ffn_ws.
@@ -405,18 +409,7 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (few) {
-    const float* y_ext = nullptr;
-    if (shared8) {
-      // the FP8 shared expert first (it needs no routing); the routed
-      // launches' combine adds its rows first, in the fixed order
-      char* w8 = static_cast<char*>(ws) + align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false));
-      float* y_sh = reinterpret_cast<float*>(w8);
-      launch_fp8_ffn(static_cast<const uint16_t*>(x_bf16), shared8, T, y_sh,
-                     w8 + align_up((size_t)T * H * sizeof(float)), stream);
-      y_ext = y_sh;
-    }
     DecodeLaunch d{};
-    d.y_shared_ext = y_ext;
     d.ffn_mode = 0;
     d.x = static_cast<const uint16_t*>(x_bf16);
     d.wr = static_cast<const uint16_t*>(w_router_bf16);
@@ -433,6 +426,28 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
     d.out = out;
     d.ids_out = topk_ids_out;
     d.w_out = topk_w_out;
+    if (shared8) {
+      // one token: the FP8 expert streams inside the fused launches, like
+      // the MXFP4 shared expert
+      DecodeLaunch f = d;
+      f.has_shared = true;
+      f.shared_fp8 = true;
+      f.sh8_gu_w = shared8->gate_up_w;
+      f.sh8_gu_s = shared8->gate_up_scales;
+      f.sh8_d_w = shared8->down_w;
+      f.sh8_d_s = shared8->down_scales;
+      if (decode_fuses_fp8_shared(f)) {
+        launch_decode(f, ws, stream);
+        return launch_status();
+      }
+      // otherwise the FP8 expert runs first (it needs no routing); the
+      // routed launches' combine adds its rows first, in the fixed order
+      char* w8 = static_cast<char*>(ws) + align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false));
+      float* y_sh = reinterpret_cast<float*>(w8);
+      launch_fp8_ffn(static_cast<const uint16_t*>(x_bf16), shared8, T, y_sh,
+                     w8 + align_up((size_t)T * H * sizeof(float)), stream);
+      d.y_shared_ext = y_sh;
+    }
     launch_decode(d, ws, stream);
     return launch_status();
   }

@@ -141,6 +141,8 @@ struct DecodeArgs {
   BankView routed, shared;
   int has_shared;
   const float* y_shared_ext;  // [T][H] shared rows from earlier launches, or null
+  const uint8_t *sh8_gu_w, *sh8_gu_s, *sh8_d_w, *sh8_d_s;  // FP8 shared expert
+  int shared_fp8;
   int T, H, I, E, k, R;
   const int32_t* offsets_in;    // FFN mode: caller's bucket offsets
   const int32_t* row_token_in;  // FFN mode (null = identity)
@@ -1051,6 +1053,127 @@ __device__ void shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds
   dn_compute(a, nullptr, 0, c, A, reinterpret_cast<f32x4_t*>(lds));
 }
 
+// ---------------------------------------------------------------------------
+// The shared expert in FP8 (E4M3 bytes, one E8M0 scale per 32 x 32 block),
+// one token, inside the fused launch: the same item split, flags and
+// dispatch slots as the MXFP4 shared expert, with twice the weight bytes per
+// item. The gfx950 scaled FP8 conversions apply each block's power of two
+// exactly (E4M3 x 2^s is representable in bf16 and fp32).
+// ---------------------------------------------------------------------------
+constexpr int kF8GuU = 10;  // gate/up: 32 lanes per column x 10 chunks of 16 B (K <= 5120)
+constexpr int kF8DnU = 18;  // down: 8 lanes per row x 18 chunks of 16 B (K <= 2304)
+
+__device__ __forceinline__ float dot16_fp8s_bf16(uint4 w, float sc, uint4 x0, uint4 x1, float acc) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[i], sc, false),
+                                          as_bf16x2(xx[2 * i]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[i], sc, true),
+                                          as_bf16x2(xx[2 * i + 1]), acc, false);
+  }
+  return acc;
+}
+
+// Gate/up item: columns 8 item .. 8 item + 7 of the shared h row (2 per
+// wave, 32 lanes per column); h stored write-through for the down items of
+// this launch.
+__device__ void fp8_shared_gu_item(const DecodeArgs& a, int item, uint4* s_x) {
+  const int H = a.H, I = a.I;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, j = lane & 31;
+  const int n = item * kGuRows + wave * 2 + (lane >> 5);
+  const bool ok = n < I;
+  const int nr = ok ? n : I - 1;
+  const int nch = H >> 4, sb = H >> 5;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(a.sh8_gu_w, (uint32_t)I * H);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(a.sh8_gu_w + (size_t)I * H, (uint32_t)I * H);
+  const __amdgpu_buffer_rsrc_t rs = matrix_rsrc(a.sh8_gu_s, (uint32_t)(2 * (I >> 5) * sb));
+  uint4 wg[kF8GuU], wu[kF8GuU];
+  uint32_t sg[kF8GuU], su[kF8GuU];
+#pragma unroll
+  for (int u = 0; u < kF8GuU; ++u) {
+    const int c = j + 32 * u;
+    wg[u] = bload16(rg, nr * H + c * 16);
+    wu[u] = bload16(ru, nr * H + c * 16);
+    sg[u] = bload8(rs, (nr >> 5) * sb + (c >> 1));
+    su[u] = bload8(rs, ((I + nr) >> 5) * sb + (c >> 1));
+  }
+  stage_rows<uint4>(
+      H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+      [&](int idx, uint4 v) { s_x[idx] = v; });
+  __syncthreads();
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kF8GuU; ++u) {
+    const int c = j + 32 * u;
+    if (c < nch) {
+      const uint4 x0 = s_x[2 * c], x1 = s_x[2 * c + 1];
+      ag = dot16_fp8s_bf16(wg[u], e8m0_to_f32(sg[u]), x0, x1, ag);
+      au = dot16_fp8s_bf16(wu[u], e8m0_to_f32(su[u]), x0, x1, au);
+    }
+  }
+  ag = group_sum<32>(ag);
+  au = group_sum<32>(au);
+  if (ok && j == 0) cst(a.h + (size_t)a.R * I + n, silu_mul(ag, au));
+}
+
+// Down item c: 32 output rows of the shared y row, 8 lanes per row. The
+// weights are requested before the wait for the gate/up flags; h is read
+// coherently once they are all up.
+__device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
+  const int H = a.H, I = a.I;
+  const int q = threadIdx.x & 7;
+  const int n = c * kDnRows + (threadIdx.x >> 3);
+  const bool ok = n < H;
+  const int nr = ok ? n : H - 1;
+  const int nch = I >> 4, sb = I >> 5;
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(a.sh8_d_w, (uint32_t)H * I);
+  const __amdgpu_buffer_rsrc_t rs = matrix_rsrc(a.sh8_d_s, (uint32_t)((H >> 5) * sb));
+  uint4 wd[kF8DnU];
+  uint32_t sd[kF8DnU];
+#pragma unroll
+  for (int u = 0; u < kF8DnU; ++u) {
+    const int cc = q + 8 * u;
+    wd[u] = bload16(rd, nr * I + cc * 16);
+    sd[u] = bload8(rs, (nr >> 5) * sb + (cc >> 1));
+  }
+  if (threadIdx.x < kWave) {
+    uint32_t v[6];
+    poll_tagged<6>(a, shared_flags(a), n_sh, v);
+  }
+  __syncthreads();
+  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds);
+  const uint64_t* hrow = reinterpret_cast<const uint64_t*>(a.h + (size_t)a.R * I);
+  for (int f = threadIdx.x; f < (I >> 2); f += kThreads) {
+    const uint64_t lo = cld(hrow + 2 * f), hi = cld(hrow + 2 * f + 1);
+    s_h[f] = f32x4_t{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+  }
+  __syncthreads();
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kF8DnU; ++u) {
+    const int cc = q + 8 * u;
+    if (cc < nch) {
+      const float f = e8m0_to_f32(sd[u]);
+      const uint32_t ww[4] = {wd[u].x, wd[u].y, wd[u].z, wd[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_t h4 = s_h[4 * cc + i];
+        const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ww[i], f, false);
+        const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ww[i], f, true);
+        acc = fmaf(p0.x, h4.x, acc);
+        acc = fmaf(p0.y, h4.y, acc);
+        acc = fmaf(p1.x, h4.z, acc);
+        acc = fmaf(p1.y, h4.w, acc);
+      }
+    }
+  }
+  acc = group_sum<8>(acc);
+  if (ok && q == 0) cst(a.y + (size_t)a.R * H + n, acc);
+}
+
 __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
                                                                 int n_sd, int G) {
   extern __shared__ __align__(16) char lds[];
@@ -1071,14 +1194,20 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
   if (b0 <= a.nb_router + n_shared) {
     // a shared gate/up item, then its flag once its h stores have landed
     const int item = b0 - a.nb_router - 1;
-    gateup_item<1, true>(a, shared_slot(a), item, reinterpret_cast<uint4*>(lds), nullptr);
+    if (a.shared_fp8)
+      fp8_shared_gu_item(a, item, reinterpret_cast<uint4*>(lds));
+    else
+      gateup_item<1, true>(a, shared_slot(a), item, reinterpret_cast<uint4*>(lds), nullptr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) cst(shared_flags(a) + item, ((uint64_t)a.tag << 32) | 1u);
     return;
   }
   if (b0 >= a.nb_router + 1 + n_shared + G) {
-    shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
+    if (a.shared_fp8)
+      fp8_shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
+    else
+      shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
     return;
   }
   const int b = b0 - a.nb_router - 1 - n_shared;
@@ -1793,6 +1922,23 @@ void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch
   launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
 }
 
+// The one-token fused launches take this call.
+static bool stream_path(const DecodeLaunch& d, const DecodeLayout& L) {
+  const bool ffn = d.ffn_mode != 0;
+  return d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU && d.H % 128 == 0 &&
+         d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU && d.I <= 3 * 4 * kThreads &&
+         d.H * 2 + 4 * (1 + 3 * L.max_slots) <= kLdsBytes &&
+         1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave && d.E <= 16 * kWave &&
+         (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
+}
+
+bool decode_fuses_fp8_shared(const DecodeLaunch& d) {
+  if (d.ffn_mode != 0 || d.T != 1) return false;
+  const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, false, true);
+  // the FP8 items hold K = H in 32 x kF8GuU chunks and K = I in 8 x kF8DnU
+  return stream_path(d, L) && (d.H >> 4) <= 32 * kF8GuU && (d.I >> 4) <= 8 * kF8DnU;
+}
+
 void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   const bool ffn = d.ffn_mode != 0;
   const bool shared = d.has_shared && !ffn;
@@ -1806,6 +1952,11 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.shared = d.shared;
   a.has_shared = shared;
   a.y_shared_ext = ffn ? nullptr : d.y_shared_ext;
+  a.shared_fp8 = shared && d.shared_fp8;
+  a.sh8_gu_w = d.sh8_gu_w;
+  a.sh8_gu_s = d.sh8_gu_s;
+  a.sh8_d_w = d.sh8_d_w;
+  a.sh8_d_s = d.sh8_d_s;
   a.T = d.T;
   a.H = d.H;
   a.I = d.I;
@@ -1847,13 +1998,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   // One token (or one row per expert): every slot holds a single row, and a
   // kernel built for one staged row needs far fewer registers.
   const bool one = d.T == 1 || (ffn && d.R <= 1);
-  const bool stream = d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU && d.H % 128 == 0 &&
-                      d.I % 128 == 0 &&
-                      (d.I >> 5) <= 8 * kDnU && d.I <= 3 * 4 * kThreads &&
-                      d.H * 2 + 4 * (1 + 3 * L.max_slots) <= kLdsBytes &&
-                      1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave &&
-                      d.E <= 16 * kWave &&
-                      (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
+  const bool stream = stream_path(d, L);
   if (stream) {
     const int n_sh = shared ? L.gu_items : 0;
     const int n_sd = shared ? L.dn_items : 0;

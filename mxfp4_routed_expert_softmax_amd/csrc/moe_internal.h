@@ -132,12 +132,21 @@ struct DecodeLaunch {
   int32_t* ids_out;
   float* w_out;
   float* y_rows;             // FFN mode output
+  // layer mode, one token: the shared expert in FP8 (E4M3, 32 x 32 E8M0
+  // blocks: gate_up [2][I][H] + scales [2][I/32][H/32], down [H][I] +
+  // scales [H/32][I/32]) streamed inside the fused launches; with has_shared
+  const uint8_t *sh8_gu_w, *sh8_gu_s, *sh8_d_w, *sh8_d_s;
+  bool shared_fp8;
   const float* y_shared_ext; // layer mode: [T][H] shared-expert rows computed
                              // by earlier launches (the combine adds them
                              // first), or null
 };
 
 size_t decode_ws_bytes(int T, int H, int I, int E, int k, int R, bool ffn, bool shared);
+// Whether launch_decode streams an FP8 shared expert inside its fused
+// one-token launches for this call (layer mode, one token, shapes the fused
+// kernels take); otherwise the caller runs the FP8 expert separately.
+bool decode_fuses_fp8_shared(const DecodeLaunch& d);
 void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s);
 
 void launch_combine(const float* y_rows, const int32_t* inv_row, const float* w,

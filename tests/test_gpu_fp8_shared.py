@@ -151,6 +151,8 @@ def _selected_bank(w, x, wr, bias):
     ("spec5", 6, "gateup_kernel"),
 ])
 def test_layer_fp8_shared_real_shape_few_tokens(name, T, path):
+    # one token streams the FP8 expert inside the fused launches; more tokens
+    # run it first, in its own two launches
     w = S.get(name)
     x = S.gen_tokens(w, 0, T=T) if T != w.T else S.gen_tokens(w, 0)
     wr = S.gen_router(w, 0)
@@ -158,8 +160,38 @@ def test_layer_fp8_shared_real_shape_few_tokens(name, T, path):
                     exp_hi=w.exp_hi)
     routed = _selected_bank(wT, x, wr, None)
     err, names = _fp8_layer_parity(wT, x, wr, None, routed, S.gen_fp8_bank(w, 0))
-    assert names[:2] == ["fp8_gateup_gemv_kernel", "fp8_down_gemv_kernel"]
+    if T == 1:
+        assert names == ["gateup_fused_kernel", "down_stream_kernel"]
+    else:
+        assert names[:2] == ["fp8_gateup_gemv_kernel", "fp8_down_gemv_kernel"]
     assert path in names
+    assert err < 1e-4
+
+
+# one token through the fused launches at shapes where the item counts and
+# the split of the routed rows differ from the real shape's
+ONE_TOKEN_FP8 = [
+    S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_small", 92, T=1, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_wide_k", 94, T=1, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+]
+
+
+@pytest.mark.parametrize("w", ONE_TOKEN_FP8, ids=lambda w: w.name)
+def test_layer_fp8_shared_one_token_fused(w):
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    err, names = _fp8_layer_parity(w, x, wr, None, S.gen_bank(w, 0), S.gen_fp8_bank(w, 0))
+    assert names == ["gateup_fused_kernel", "down_stream_kernel"]
+    assert err < 1e-4
+
+
+def test_layer_fp8_shared_one_token_every_code():
+    # all finite E4M3 bytes (subnormals included) through the fused items
+    w = ONE_TOKEN_FP8[0]
+    x, wr = S.gen_tokens(w, 1), S.gen_router(w, 1)
+    err, names = _fp8_layer_parity(w, x, wr, None, S.gen_bank(w, 1),
+                                   S.gen_fp8_bank(w, 1, all_codes=True))
+    assert names == ["gateup_fused_kernel", "down_stream_kernel"]
     assert err < 1e-4
 
 
