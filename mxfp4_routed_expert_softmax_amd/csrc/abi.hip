@@ -593,6 +593,32 @@ int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (T == 1) {
+    // one token: the fused launches, with NVFP4 items
+    DecodeLaunch d{};
+    d.ffn_mode = 0;
+    d.x = static_cast<const uint16_t*>(x_bf16);
+    d.wr = static_cast<const uint16_t*>(w_router_bf16);
+    d.bias = logit_bias;
+    d.routed = view_nv(routed);
+    d.has_shared = shared != nullptr;
+    if (shared) d.shared = view_nv(shared);
+    d.T = T;
+    d.H = H;
+    d.I = I;
+    d.E = E;
+    d.k = k;
+    d.R = T * k;
+    d.out = out;
+    d.ids_out = topk_ids_out;
+    d.w_out = topk_w_out;
+    if (decode_fuses_nvfp4(d)) {
+      if (ws_bytes < decode_ws_bytes(T, H, I, E, k, T * k, false, shared != nullptr))
+        return MOE_ERR_WORKSPACE;
+      launch_decode(d, ws, stream);
+      return launch_status();
+    }
+  }
   if (ws_bytes < layer_ws(nullptr, T, H, I, E, k).bytes) return MOE_ERR_WORKSPACE;
   const LayerWs L = layer_ws(ws, T, H, I, E, k);
   int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;

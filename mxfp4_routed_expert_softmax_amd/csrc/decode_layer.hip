@@ -999,6 +999,184 @@ __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, 
   if (j == 0 && n < a.H) cst(a.y + (size_t)row * a.H + n, v);
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 banks in the one-token launches (E2M1 codes, one E4M3 scale per 16
+// codes, an fp32 scale per expert and matrix): the same items and register
+// buffers as MXFP4, with a 32-code chunk's two scale bytes taken from one
+// word (rows of K / 16 scale bytes start on a word), each 16-code half of
+// the chunk's dot product multiplied by its own scale and the matrix scale
+// applied to the row sums.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x2_t nv_scale_pair(uint32_t word, uint32_t sh) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((word >> sh) & 0xffffu, 1.0f, false);
+}
+__device__ __forceinline__ float nv_matrix_scale(const BankView& b, int e, int m) {
+  return b.gscale ? b.gscale[e * 3 + m] : 1.0f;
+}
+
+// gate/up weights of 8-row group rb of the expert whose codes / scales
+// start at gbase / sbase ([2][I][H/2], [2][I][H/16])
+__device__ __forceinline__ void gu_issue_nv(const DecodeArgs& a, const uint8_t* gbase,
+                                            const uint8_t* sbase, int rb, GuRegs& r, bool live) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int nr = min(rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes, a.I - 1);
+  const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> 4;
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  gbase = uniform_ptr(gbase);
+  sbase = uniform_ptr(sbase);
+  const uint32_t cb = live ? a.I * crow : 0u, sb = live ? a.I * srow : 0u;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(gbase, cb);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, cb);
+  const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, sb);
+  const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, sb);
+  // chunk j + 32 u has scale bytes 2 j + 64 u and the next: half j % 2 of
+  // the word at 4 (j / 2) + 64 u
+  const int co = nr * crow + j * 16, so = nr * srow + 4 * (j >> 1);
+#pragma unroll
+  for (int u = 0; u < kGuU; ++u) {
+    r.g[u] = bload16(rg, co + u * kGuLanes * 16);
+    r.u[u] = bload16(ru, co + u * kGuLanes * 16);
+    r.sg[u] = bload32(rgs, so + u * kGuLanes * 2);
+    r.su[u] = bload32(rus, so + u * kGuLanes * 2);
+  }
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ void gu_compute_nv(const DecodeArgs& a, int rb, int row, float mg,
+                                              float mu, const GuRegs& r, const uint4* s_x) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & (kGuLanes - 1);
+  const int n = rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes;
+  const int kc = a.H >> 5;
+  const uint32_t sh = 16u * (j & 1);
+  float ag = 0.0f, au = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kGuU; ++u) {
+    const int c = kGuLanes * u + j;
+    if (c < kc) {
+      const uint4* xv = s_x + c;
+      constexpr int P = kGuLanes * kGuU;
+      const uint4 x0 = xv[0], x1 = xv[P], x2 = xv[2 * P], x3 = xv[3 * P];
+      const f32x2_t fg = nv_scale_pair(r.sg[u], sh), fu = nv_scale_pair(r.su[u], sh);
+      float g0 = dot8_fp4_bf16(r.g[u].x, x0, 0.0f);
+      g0 = dot8_fp4_bf16(r.g[u].y, x1, g0);
+      float g1 = dot8_fp4_bf16(r.g[u].z, x2, 0.0f);
+      g1 = dot8_fp4_bf16(r.g[u].w, x3, g1);
+      float u0 = dot8_fp4_bf16(r.u[u].x, x0, 0.0f);
+      u0 = dot8_fp4_bf16(r.u[u].y, x1, u0);
+      float u1 = dot8_fp4_bf16(r.u[u].z, x2, 0.0f);
+      u1 = dot8_fp4_bf16(r.u[u].w, x3, u1);
+      ag = fmaf(g1, fg.y, fmaf(g0, fg.x, ag));
+      au = fmaf(u1, fu.y, fmaf(u0, fu.x, au));
+    }
+  }
+  const float g = group_sum<kGuLanes>(ag) * mg, u = group_sum<kGuLanes>(au) * mu;
+  if (j == 0 && n < a.I) {
+    float* p = a.h + (size_t)row * a.I + n;
+    if (kCoherent)
+      cst(p, silu_mul(g, u));
+    else
+      *p = silu_mul(g, u);
+  }
+}
+
+// routed item `it` (slot-major over gu_items 8-row groups)
+__device__ __forceinline__ void gu_issue_nv_routed(const DecodeArgs& a, const int* tab, int it,
+                                                   GuRegs& r, bool live) {
+  const int s = it / a.gu_items, rb = it - s * a.gu_items;
+  const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + s], 0), a.routed.E - 1));
+  gu_issue_nv(a, a.routed.gu_codes + (size_t)e * 2 * a.I * (a.H >> 1),
+              a.routed.gu_scales + (size_t)e * 2 * a.I * (a.H >> 4), rb, r, live);
+}
+__device__ __forceinline__ void gu_compute_nv_routed(const DecodeArgs& a, const int* tab, int it,
+                                                     const GuRegs& r, const uint4* s_x) {
+  const int s = it / a.gu_items, rb = it - s * a.gu_items;
+  const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
+  const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  gu_compute_nv<false>(a, rb, row, nv_matrix_scale(a.routed, e, 0), nv_matrix_scale(a.routed, e, 1),
+                       r, s_x);
+}
+
+// down: item it of the routed slots (it < nr) or of the shared expert
+struct DnItemNv {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int row, c;
+  float md;
+};
+__device__ __forceinline__ DnItemNv dn_item_nv(const DecodeArgs& a, const int* tab, int nr, int it) {
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 4;
+  if (it >= nr) {
+    const int c = min(it - nr, a.dn_items - 1);
+    return DnItemNv{a.shared.d_codes, a.shared.d_scales, min(a.R, a.rows - 1), c,
+                    nv_matrix_scale(a.shared, 0, 2)};
+  }
+  const int s = it / a.dn_items, c = it - s * a.dn_items;
+  const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + s], 0), a.routed.E - 1));
+  const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
+  return DnItemNv{a.routed.d_codes + (size_t)e * a.H * crow,
+                  a.routed.d_scales + (size_t)e * a.H * srow, row, c,
+                  nv_matrix_scale(a.routed, e, 2)};
+}
+
+__device__ __forceinline__ void dn_issue_nv(const DecodeArgs& a, const int* tab, int n_routed,
+                                            int it, DnRegs& r, bool live = true,
+                                            bool with_h = true) {
+  const DnItemNv d = dn_item_nv(a, tab, n_routed, it);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int nr = min(d.c * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 4;
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(uniform_ptr(d.codes), live ? a.H * crow : 0u);
+  const __amdgpu_buffer_rsrc_t rds = matrix_rsrc(uniform_ptr(d.scales), live ? a.H * srow : 0u);
+  // chunk j + 8 u has scale bytes 2 j + 16 u and the next: half j % 2 of
+  // the word at 4 (j / 2) + 16 u
+  const int co = nr * crow + j * 16, so = nr * srow + 4 * (j >> 1);
+#pragma unroll
+  for (int u = 0; u < kDnU; ++u) {
+    r.w[u] = bload16(rd, co + u * 8 * 16);
+    r.sc[u] = bload32(rds, so + u * 16);
+  }
+  if (with_h) dn_issue_h<false>(a, d.row, r);
+}
+
+__device__ __forceinline__ void dn_compute_nv(const DecodeArgs& a, const int* tab, int nr, int it,
+                                              const DnRegs& r, f32x4_t* s_h) {
+  const int nv = a.I >> 2;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int f = min((int)threadIdx.x + i * kThreads, nv - 1);
+    s_h[(f & 7) * (8 * kDnU) + (f >> 3)] = r.h[i];
+  }
+  __syncthreads();
+  const DnItemNv d = dn_item_nv(a, tab, nr, it);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int j = lane & 7;
+  const int n = d.c * kDnRows + wave * 8 + (lane >> 3);
+  const int kc = a.I >> 5;
+  const uint32_t sh = 16u * (j & 1);
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kDnU; ++u) {
+    const int ch = 8 * u + j;
+    if (ch < kc) {
+      const f32x4_t* hv = s_h + ch;
+      constexpr int P = 8 * kDnU;
+      const f32x2_t f = nv_scale_pair(r.sc[u], sh);
+      float p0 = dot8_fp4_f32(r.w[u].x, hv[0], hv[P], 0.0f);
+      p0 = dot8_fp4_f32(r.w[u].y, hv[2 * P], hv[3 * P], p0);
+      float p1 = dot8_fp4_f32(r.w[u].z, hv[4 * P], hv[5 * P], 0.0f);
+      p1 = dot8_fp4_f32(r.w[u].w, hv[6 * P], hv[7 * P], p1);
+      acc = fmaf(p1, f.y, fmaf(p0, f.x, acc));
+    }
+  }
+  const float v = group_sum<8>(acc) * d.md;
+  if (j == 0 && n < a.H) cst(a.y + (size_t)d.row * a.H + n, v);
+}
+
 // Combine of output columns [32c, 32c + 32) of the one token: the shared
 // row, then the k routed rows in order j = 0..k-1, one fp32 fma each. Rows
 // and weights come from LDS; the y rows were written by other workgroups of
@@ -1174,6 +1352,33 @@ __device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, char*
   if (ok && q == 0) cst(a.y + (size_t)a.R * H + n, acc);
 }
 
+// NVFP4 shared expert, one token: gate/up item (h write-through) and down
+// item (after the gate/up flags), as the MXFP4 ones.
+__device__ void nv_shared_gu_item(const DecodeArgs& a, int item, uint4* s_x) {
+  GuRegs r;
+  gu_issue_nv(a, a.shared.gu_codes, a.shared.gu_scales, item, r, true);
+  stage_rows<uint4>(
+      a.H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+      [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
+  __syncthreads();
+  gu_compute_nv<true>(a, item, min(a.R, a.rows - 1), nv_matrix_scale(a.shared, 0, 0),
+                      nv_matrix_scale(a.shared, 0, 1), r, s_x);
+}
+
+__device__ void nv_shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
+  DnRegs A;
+  dn_issue_nv(a, nullptr, 0, c, A, true, false);
+  if (threadIdx.x < kWave) {
+    uint32_t v[6];
+    poll_tagged<6>(a, shared_flags(a), n_sh, v);
+  }
+  __syncthreads();
+  dn_issue_h<true>(a, min(a.R, a.rows - 1), A);
+  dn_compute_nv(a, nullptr, 0, c, A, reinterpret_cast<f32x4_t*>(lds));
+}
+
+// NV: NVFP4 banks (routed and shared); otherwise MXFP4 (shared possibly FP8).
+template <bool NV>
 __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
                                                                 int n_sd, int G) {
   extern __shared__ __align__(16) char lds[];
@@ -1194,7 +1399,9 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
   if (b0 <= a.nb_router + n_shared) {
     // a shared gate/up item, then its flag once its h stores have landed
     const int item = b0 - a.nb_router - 1;
-    if (a.shared_fp8)
+    if constexpr (NV)
+      nv_shared_gu_item(a, item, reinterpret_cast<uint4*>(lds));
+    else if (a.shared_fp8)
       fp8_shared_gu_item(a, item, reinterpret_cast<uint4*>(lds));
     else
       gateup_item<1, true>(a, shared_slot(a), item, reinterpret_cast<uint4*>(lds), nullptr);
@@ -1204,7 +1411,9 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
     return;
   }
   if (b0 >= a.nb_router + 1 + n_shared + G) {
-    if (a.shared_fp8)
+    if constexpr (NV)
+      nv_shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
+    else if (a.shared_fp8)
       fp8_shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
     else
       shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
@@ -1224,13 +1433,25 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
   // weight loads read nothing (empty resources) and are not used.
   const int mine = b < n ? (n - b + G - 1) / G : 0;
   GuRegs A, B;
-  gu_issue(a, tab, b < n ? b : 0, A, b < n);
+  auto issue = [&](int it, GuRegs& r, bool live) {
+    if constexpr (NV)
+      gu_issue_nv_routed(a, tab, it, r, live);
+    else
+      gu_issue(a, tab, it, r, live);
+  };
+  auto compute = [&](int it, const GuRegs& r) {
+    if constexpr (NV)
+      gu_compute_nv_routed(a, tab, it, r, s_x);
+    else
+      gu_compute(a, tab, it, r, s_x);
+  };
+  issue(b < n ? b : 0, A, b < n);
   for (int kk = 0; kk < mine; kk += 2) {
     const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
-    gu_issue(a, tab, i1 < n ? i1 : i0, B, i1 < n);
-    gu_compute(a, tab, i0, A, s_x);
-    gu_issue(a, tab, i2 < n ? i2 : i0, A, i2 < n);
-    if (i1 < n) gu_compute(a, tab, i1, B, s_x);
+    issue(i1 < n ? i1 : i0, B, i1 < n);
+    compute(i0, A);
+    issue(i2 < n ? i2 : i0, A, i2 < n);
+    if (i1 < n) compute(i1, B);
   }
 }
 
@@ -1239,6 +1460,7 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
 // buffers. After its last item a workgroup drains its y stores and bumps
 // the counters of all the columns it wrote at once; the workgroup that
 // completes a column (every routed slot and the shared expert) combines it.
+template <bool NV>
 __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
   __shared__ int s_last[32];
@@ -1260,13 +1482,25 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
   if (b >= n) return;
   const int mine = (n - b + G - 1) / G;  // <= 32 (the grid is at least n / 32)
   DnRegs A, B;
-  dn_issue(a, tab, nr, b, A);
+  auto issue = [&](int it, DnRegs& r, bool live) {
+    if constexpr (NV)
+      dn_issue_nv(a, tab, nr, it, r, live);
+    else
+      dn_issue(a, tab, nr, it, r, live);
+  };
+  auto compute = [&](int it, const DnRegs& r) {
+    if constexpr (NV)
+      dn_compute_nv(a, tab, nr, it, r, s_h);
+    else
+      dn_compute(a, tab, nr, it, r, s_h);
+  };
+  issue(b, A, true);
   for (int k = 0; k < mine; k += 2) {
     const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
-    dn_issue(a, tab, nr, i1 < n ? i1 : i0, B, i1 < n);
-    dn_compute(a, tab, nr, i0, A, s_h);
-    dn_issue(a, tab, nr, i2 < n ? i2 : i0, A, i2 < n);
-    if (i1 < n) dn_compute(a, tab, nr, i1, B, s_h);
+    issue(i1 < n ? i1 : i0, B, i1 < n);
+    compute(i0, A);
+    issue(i2 < n ? i2 : i0, A, i2 < n);
+    if (i1 < n) compute(i1, B);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -1932,6 +2166,12 @@ static bool stream_path(const DecodeLaunch& d, const DecodeLayout& L) {
          (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
 }
 
+bool decode_fuses_nvfp4(const DecodeLaunch& d) {
+  if (d.ffn_mode != 0 || d.T != 1) return false;
+  const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, false, d.has_shared);
+  return stream_path(d, L);
+}
+
 bool decode_fuses_fp8_shared(const DecodeLaunch& d) {
   if (d.ffn_mode != 0 || d.T != 1) return false;
   const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, false, true);
@@ -2003,13 +2243,14 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
     const int n_sh = shared ? L.gu_items : 0;
     const int n_sd = shared ? L.dn_items : 0;
     const int gg = routed_gu < kStreamBlocks ? routed_gu : kStreamBlocks;
-    launch("gateup_fused_kernel", gateup_fused_kernel,
+    const bool nv = d.routed.codec == kCodecNvfp4;
+    launch("gateup_fused_kernel", nv ? gateup_fused_kernel<true> : gateup_fused_kernel<false>,
            dim3(L.nb_router + 1 + n_sh + gg + n_sd), dim3(kThreads), kLdsBytes, s, a, n_sh, n_sd,
            gg);
     const int nd = L.max_slots * L.dn_items;
     const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
-    launch("down_stream_kernel", down_stream_kernel, dim3(gd), dim3(kThreads), kLdsBytes, s, a,
-           gd);
+    launch("down_stream_kernel", nv ? down_stream_kernel<true> : down_stream_kernel<false>,
+           dim3(gd), dim3(kThreads), kLdsBytes, s, a, gd);
     return;
   }
   // A block of 2..5 or 8 tokens: router + routing, then the streaming

@@ -147,6 +147,9 @@ size_t decode_ws_bytes(int T, int H, int I, int E, int k, int R, bool ffn, bool 
 // one-token launches for this call (layer mode, one token, shapes the fused
 // kernels take); otherwise the caller runs the FP8 expert separately.
 bool decode_fuses_fp8_shared(const DecodeLaunch& d);
+// Whether launch_decode takes this call with NVFP4 banks (BankView codec):
+// only the one-token fused launches hold NVFP4 items.
+bool decode_fuses_nvfp4(const DecodeLaunch& d);
 void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s);
 
 void launch_combine(const float* y_rows, const int32_t* inv_row, const float* w,

@@ -132,12 +132,35 @@ def _selected(w, x, wr):
     return sorted(sel)
 
 
+FUSED = ["gateup_fused_kernel", "down_stream_kernel"]
+
+
 @pytest.mark.parametrize("name", ["decode", "spec5"])
 def test_layer_real_shape_few_tokens(name):
+    # one token takes the fused launches with NVFP4 items; more tokens the
+    # separate ones
     w = S.get(name)
     x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
     routed = S.gen_nvfp4_bank(w, 0, experts=_selected(w, x, wr))
     assert _parity(w, x, wr, None, routed, S.gen_nvfp4_bank(w, 0, shared=True)) < 1e-4
+    assert (_names() == FUSED) == (w.T == 1)
+
+
+ONE_TOKEN_NV = [
+    S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_small", 92, T=1, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_wide_k", 94, T=1, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+]
+
+
+@pytest.mark.parametrize("w", ONE_TOKEN_NV, ids=lambda w: w.name)
+@pytest.mark.parametrize("shared", [True, False], ids=["shared", "no_shared"])
+def test_layer_one_token_fused(w, shared):
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    sh = S.gen_nvfp4_bank(w, 0, shared=True) if shared else None
+    bias = None if shared else np.linspace(-1, 1, w.E).astype(np.float32)
+    assert _parity(w, x, wr, bias, S.gen_nvfp4_bank(w, 0), sh) < 1e-4
+    assert _names() == FUSED
 
 
 def test_layer_gemm_ragged_and_prefill_sampled():
