@@ -212,3 +212,22 @@ def test_layer_fp8_shared_is_bitwise_deterministic():
     b = run_layer_fp8(x, wr, None, rd, sd, w.k)
     for u, v in zip(a[:3], b[:3]):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_layer_fp8_shared_one_token_deterministic_and_garbage_workspace():
+    w = ONE_TOKEN_FP8[0]
+    x, wr = S.gen_tokens(w, 2), S.gen_router(w, 2)
+    rd = HP.bank_to_dev(S.gen_bank(w, 2))
+    sd = M.Fp8BankTensors.from_numpy(S.gen_fp8_bank(w, 2), HP.dev())
+    outs = []
+    for fill in (None, 0xFF, 0x00):
+        ws = M.workspace(w.T, w.H, w.I, w.E, w.k, HP.dev())
+        if fill is not None:
+            ws.fill_(fill)
+        out = torch.empty((w.T, w.H), dtype=torch.float32, device=HP.dev())
+        M.moe_layer_forward_fp8_shared(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, None,
+                                       None, ws)
+        assert _launch_names() == ["gateup_fused_kernel", "down_stream_kernel"]
+        outs.append(_np(out))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))

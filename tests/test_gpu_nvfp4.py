@@ -182,3 +182,23 @@ def test_layer_is_bitwise_deterministic():
     b = run_layer(x, wr, None, routed, shared, w.k)
     for u, v in zip(a[:3], b[:3]):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_one_token_fused_deterministic_and_garbage_workspace():
+    # the fused launches hand data between workgroups through tagged words in
+    # the workspace: whatever the workspace held before must not matter
+    w = ONE_TOKEN_NV[0]
+    x, wr = S.gen_tokens(w, 2), S.gen_router(w, 2)
+    rd = M.NvBankTensors.from_numpy(S.gen_nvfp4_bank(w, 2), HP.dev())
+    sd = M.NvBankTensors.from_numpy(S.gen_nvfp4_bank(w, 2, shared=True), HP.dev())
+    outs = []
+    for fill in (None, 0xFF, 0x00):
+        ws = M.workspace(w.T, w.H, w.I, w.E, w.k, HP.dev())
+        if fill is not None:
+            ws.fill_(fill)
+        out = torch.empty((w.T, w.H), dtype=torch.float32, device=HP.dev())
+        M.moe_layer_forward_nvfp4(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, None, None, ws)
+        assert _names() == FUSED
+        outs.append(_np(out))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))
