@@ -104,8 +104,102 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Router GEMM staged through LDS (H a multiple of 64): the same 128 x 128
+// tile and 64 x 64 wave blocks, but each K step of 64 is copied into LDS by
+// direct global -> LDS loads in which 8 lanes cover a row's 128 contiguous
+// bytes (whole cache lines), double buffered, so the fragment reads hit LDS
+// instead of scattering 64-byte pieces of 16 rows over the cache. Piece p of
+// row r sits at slot p ^ (r % 8).
+// ---------------------------------------------------------------------------
+constexpr int kRtBK = 64;
+constexpr int kRtStage = 2 * 128 * kRtBK * 2;  // A and B tiles, bf16: 32 KB
+
+__device__ __forceinline__ void rt_lds_load16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+               :
+               : "v"(voff), "s"(lds), "s"(base)
+               : "memory");
+}
+
+__global__ __launch_bounds__(256) void router_mfma_lds_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
+  __shared__ __align__(16) char lds[2 * kRtStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, c = lane & 15, g = lane >> 4;
+  const int mt = blockIdx.x * 128, nt = blockIdx.y * 128;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  // thread tid copies slots (row 32 u + tid / 8, slot tid % 8) of A and of B
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 32 * u + (tid >> 3);
+    const int piece = (tid & 7) ^ (r & 7);
+    a_off[u] = ((uint32_t)min(mt + r, T - 1) * (uint32_t)H + (uint32_t)(piece * 8)) * 2u;
+    b_off[u] = ((uint32_t)min(nt + r, E - 1) * (uint32_t)H + (uint32_t)(piece * 8)) * 2u;
+  }
+  auto issue = [&](int st, int k0) {
+    const uint32_t base = lds_base + (uint32_t)(st * kRtStage);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      rt_lds_load16(x, a_off[u] + 2u * k0, base + (uint32_t)((u * 256 + 64 * wave) * 16));
+      rt_lds_load16(wr, b_off[u] + 2u * k0, base + 16384u + (uint32_t)((u * 256 + 64 * wave) * 16));
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int steps = H / kRtBK;
+  issue(0, 0);
+  for (int ks = 0; ks < steps; ++ks) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + 1 < steps) issue((ks + 1) & 1, (ks + 1) * kRtBK);
+    const uint4* sa = reinterpret_cast<const uint4*>(lds + (ks & 1) * kRtStage);
+    const uint4* sb = sa + 1024;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = 64 * wm + 16 * i + c, rb = 64 * wn + 16 * i + c;
+        a[i] = __builtin_bit_cast(bf16x8_t, sa[ra * 8 + ((4 * sub + g) ^ (ra & 7))]);
+        b[i] = __builtin_bit_cast(bf16x8_t, sb[rb * 8 + ((4 * sub + g) ^ (rb & 7))]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = nt + 64 * wn + 16 * j + c;
+    if (n >= E) continue;
+    const float bn = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = mt + 64 * wm + 16 * i + 4 * g + v;
+        if (m < T) logits[(size_t)m * E + n] = acc[i][j][v] + bn;
+      }
+  }
+}
+
 void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
                           int T, int H, int E, float* logits, hipStream_t s) {
+  if (T > kRouterGemvMaxT && H % kRtBK == 0 && (size_t)T * H * 2 < (1ull << 32) &&
+      (size_t)E * H * 2 < (1ull << 32)) {
+    launch("router_mfma_kernel", router_mfma_lds_kernel, dim3((T + 127) / 128, (E + 127) / 128),
+           dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+    return;
+  }
   if (T <= kRouterGemvMaxT) {
     launch("router_gemv_kernel", router_gemv_kernel, dim3((E + 3) / 4), dim3(256), 0, s,
                        x, wr, bias, T, H, E, logits);
