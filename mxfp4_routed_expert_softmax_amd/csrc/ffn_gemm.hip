@@ -99,6 +99,10 @@ __device__ __forceinline__ Bucket bucket_of(const GemmArgs& g, int b) {
   return Bucket{b, lo, hi - lo, false};
 }
 
+// Workgroups of the plan kernel: each repeats the (small) scan over the
+// buckets and writes every kPlanBlocks-th stretch of 1024 tiles.
+constexpr int kPlanBlocks = 64;
+
 // Tile lists of both GEMMs, in an order that keeps shared data in one L2:
 // buckets in order (routed experts by id, then the shared expert); each
 // bucket's 128-row blocks in chunks of up to `chunk` blocks; inside a chunk
@@ -106,7 +110,7 @@ __device__ __forceinline__ Bucket bucket_of(const GemmArgs& g, int b) {
 // chunk (A, re-read by every column block) stay in cache while its column
 // blocks go by, and the row blocks sharing a weight tile (B) run together.
 // The GEMMs hand consecutive stretches of this list to each XCD.
-// One workgroup of 1024 threads (at most 1025 buckets).
+// Workgroups of 1024 threads (at most 1025 buckets).
 __device__ __forceinline__ int plan_chunk(int K) {
   // row blocks whose activations take about 2.5 MB (L2 is 4 MB per XCD)
   return min(max((5 << 19) / (kBM * K * 2), 1), 8);
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
     const int ncol = kind == 0 ? g.I / (kWRows / 2) : g.H / kWRows;
     const int chunk = plan_chunk(kind == 0 ? g.H : g.I);
     const int total = total_rb * ncol;
-    for (int q = threadIdx.x; q < total; q += 1024) {
+    for (int q = blockIdx.x * 1024 + threadIdx.x; q < total; q += gridDim.x * 1024) {
       // bucket: the last b with s_rb[b] * ncol <= q (buckets without rows
       // have equal bases; the search lands on the one that owns q)
       int lo = 0, hi = nb;  // invariant: s_rb[lo] * ncol <= q < s_rb[hi] * ncol
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
       g.tile_b[kind][q] = lo;
       g.tile_mn[kind][q] = (mt << 8) | nt;
     }
-    if (threadIdx.x == 0) g.tile_count[kind] = total;
+    if (blockIdx.x == 0 && threadIdx.x == 0) g.tile_count[kind] = total;
   }
 }
 
@@ -1133,7 +1137,7 @@ void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s) {
   g.xs = L.xs;
   g.hq = L.hq;
   g.hs = L.hs;
-  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   launch_quant_mxfp8(p.x, (long)p.T * p.H / 32, L.xq, L.xs, s);
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
   // gate/up: the deepest pipeline that fits beside the full-K scales (3
@@ -1175,7 +1179,7 @@ void launch_fp8_gemm(const Fp8Ffn& p, void* ws, hipStream_t s) {
   g.max_rb = L.max_rb;
   g.h = L.h;
   g.y_sh = p.y;
-  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
   launch("gemm_fp8w_gateup_kernel", gemm_fp8w_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
   launch("gemm_fp8w_down_kernel", gemm_fp8w_kernel<false>, dim3(grid_dn), dim3(kThreads), 0, s, g);
@@ -1217,7 +1221,7 @@ void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   g.h = L.h;
   g.y = p.y;
   g.y_sh = p.y_sh;
-  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(1), dim3(1024), 0, s, g);
+  launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   // grids: every tile the lists can hold, rounded up to the 8 XCDs
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
   const bool nv = p.routed.codec == kCodecNvfp4;
