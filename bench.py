@@ -197,6 +197,20 @@ def main() -> int:
     tokens_s = K * w.T / (ms / 1e3)
     log(f"[bench] layer: {ms_step * 1e3:.2f} us/step, {tokens_s:,.0f} tokens/s")
 
+    # ---- expert load of the last batch (rows per expert) ------------------
+    load = None
+    if w.T > 16:
+        cnt = torch.bincount(ids.reshape(-1).long(), minlength=w.E).cpu().numpy()
+        act = cnt[cnt > 0]
+        load = dict(active_experts=int(act.size), rows=int(cnt.sum()),
+                    rows_per_active_expert=dict(
+                        mean=round(float(act.mean()), 1), max=int(act.max()),
+                        p50=int(np.percentile(act, 50)), p90=int(np.percentile(act, 90)),
+                        p99=int(np.percentile(act, 99))),
+                    rows_in_top_10pct_experts=round(float(np.sort(act)[::-1][: max(1, act.size // 10)].sum()
+                                                          / cnt.sum()), 3))
+        log(f"[bench] expert load: {load}")
+
     # ---- roofline: the dominant kernel, timed with HIP events --------------
     # A second loop makes the same calls as the timed one with the library's
     # timing hook set: every kernel launch then carries a start and a stop
@@ -288,6 +302,8 @@ def main() -> int:
     }
     if mx_err is not None:
         line["mxfp8_act_error"] = mx_err
+    if load is not None:
+        line["expert_load"] = load
     print(json.dumps(line), flush=True)
     return 0
 
@@ -568,6 +584,7 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
     sh = not shared8
     nv = bool(getattr(args, "nvfp4", False))
     bound, _ = kernel_work(name, w, 1, sh, nv, shared8)
+    bound_kind = bound
     if bound is None:
         log(f"[bench] dominant kernel {name}: no algorithmic work model, roofline omitted")
         return None
@@ -581,6 +598,9 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         work = fl if bound == "mfma" else by
         log(f"[bench] {name}: {fl / 1e12:.3f} TFLOP, {by / 1e9:.2f} GB unavoidable -> "
             f"bound by {bound.upper()}")
+        # both fractions, whichever bounds the kernel
+        both = dict(mfma_frac=round(fl / (t_ms / 1e3) / (mpeak * 1e12), 4),
+                    hbm_frac=round(by / (t_ms / 1e3) / (HBM_PEAK_GBS * 1e9), 4))
     else:
         work = float(np.mean([kernel_work(name, w, U[(W + i) % P], sh, nv, shared8)[1] for i in range(K)]))
     if bound == "hbm":
@@ -594,9 +614,12 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         peak, unit = MFMA_PEAK_OF.get(name, MFMA_16BIT_PEAK_TFLOPS), "TFLOP/s"
         log(f"[bench] {name}: {t_ms:.3f} ms/launch, {work / 1e12:.3f} TFLOP -> "
             f"{ach:,.1f} TFLOP/s")
-    return dict(bound=bound, achieved=round(ach, 1), peak=peak, unit=unit,
-                frac=round(ach / peak, 4), traffic=recorded_traffic(name, w.name), kernel=name,
-                kernel_us=round(t_ms * 1e3, 2))
+    out = dict(bound=bound, achieved=round(ach, 1), peak=peak, unit=unit,
+               frac=round(ach / peak, 4), traffic=recorded_traffic(name, w.name), kernel=name,
+               kernel_us=round(t_ms * 1e3, 2))
+    if bound_kind == "gemm":
+        out.update(both)
+    return out
 
 
 def recorded_traffic(kernel, workload):
