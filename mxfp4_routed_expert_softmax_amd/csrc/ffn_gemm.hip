@@ -891,12 +891,10 @@ __global__ __launch_bounds__(kThreads, PS ? 2 : 1) void gemm_mx_kernel(GemmArgs 
   // PS: thread tid < 256 copies weight row tid's 4 scale bytes of the step,
   // 256 <= tid < 384 activation row tid - 256's
   uint32_t ps_off = 0;
-  const uint8_t* ps_src = sbase;
   if constexpr (PS) {
     if (tid < kWRows)
       ps_off = wrow(tid) * srow;
     else if (tid < kWRows + kBM) {
-      ps_src = as_src;
       ps_off = (uint32_t)act_row(tid - kWRows) * srow;
     }
   }
