@@ -1,4 +1,10 @@
-// The layer for a few tokens (decode, verification blocks) in three launches.
+// The layer for a few tokens (decode, verification blocks). One token runs
+// in two launches: the router rows, the routing wave, the shared expert and
+// the routed gate/up stream share the first, and the routed down rows with
+// the combine make the second. Verification blocks of 2-5 or 8 tokens run
+// the block kernels further down, which follow the same plan over the
+// union of the block's experts. Other counts up to 16 run the three-launch
+// chain below, whose layout the other two forms grew from.
 //
 // Decode moves ~132 MB of expert weights per token, about 17 us of HBM time
 // at 8 TB/s; the pages' own decode model is bandwidth over routed expert
