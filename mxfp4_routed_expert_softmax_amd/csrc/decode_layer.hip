@@ -686,6 +686,10 @@ __device__ void combine_column(const DecodeArgs& a, int c) {
 // one-shot kernels.)
 // ---------------------------------------------------------------------------
 constexpr int kStreamBlocks = 768;  // persistent workgroups per streaming kernel
+// The one-token gate/up stream gives each workgroup the same number of items,
+// two (one pass of its two-buffer loop) wherever at most this many
+// workgroups then cover the routed items.
+constexpr int kGuStreamMax = 896;
 
 // sg / su: the words holding the lane's scale bytes (byte lane % 4 of each).
 struct GuRegs {
@@ -2248,7 +2252,8 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   if (stream) {
     const int n_sh = shared ? L.gu_items : 0;
     const int n_sd = shared ? L.dn_items : 0;
-    const int gg = routed_gu < kStreamBlocks ? routed_gu : kStreamBlocks;
+    const int per = max(2, (routed_gu + kGuStreamMax - 1) / kGuStreamMax);
+    const int gg = (routed_gu + per - 1) / per;
     const bool nv = d.routed.codec == kCodecNvfp4;
     launch("gateup_fused_kernel", nv ? gateup_fused_kernel<true> : gateup_fused_kernel<false>,
            dim3(L.nb_router + 1 + n_sh + gg + n_sd), dim3(kThreads), kLdsBytes, s, a, n_sh, n_sd,
