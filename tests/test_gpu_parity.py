@@ -326,13 +326,16 @@ def test_layer_decode_token_pool_real_shape():
 
 
 # One token in one launch, at shapes where the worker count, the shared
-# gate/up items per worker (0 to 3) and the byte-balanced split of the routed
-# rows all differ from the real shape's.
+# gate/up items per worker (0 to 3), the routed gate/up items per streaming
+# workgroup (2, or 3 once 896 workgroups of two no longer cover them, as at
+# k = 8 with I = 2304) and the byte-balanced split of the routed rows all
+# differ from the real shape's.
 ONE_TOKEN = [
     S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
     S.Workload("one_small", 92, T=1, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3),
     S.Workload("one_narrow", 93, T=1, H=256, E=16, k=2, I=256, exp_lo=-6, exp_hi=-3),
     S.Workload("one_wide_k", 94, T=1, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+    S.Workload("one_three_items", 104, T=1, H=1024, E=32, k=8, I=2304, exp_lo=-6, exp_hi=-3),
 ]
 
 
