@@ -286,7 +286,7 @@ __device__ __forceinline__ uint64_t wave_max_key_f64(uint64_t k) {
 // (E <= 64 NK). Weights: softmax over the k chosen logits, summed over
 // j = 0..k-1 in order.
 template <int NK, int NR>
-__device__ void topk_rows_f64(const float* const* L, int E, int k, int* const* ids,
+__device__ void topk_rows_f64(const float (&lv)[NR][NK], int E, int k, int* const* ids,
                               float* const* w) {
   // NR rows at once (independent exchanges interleave, so two rows cost
   // little more than one)
@@ -297,7 +297,7 @@ __device__ void topk_rows_f64(const float* const* L, int E, int k, int* const* i
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = lane + kWave * i;
-      key[r][i] = __longlong_as_double(e < E ? (long long)topk_key_f64(cld(L[r] + e), e) : 0);
+      key[r][i] = __longlong_as_double(e < E ? (long long)topk_key_f64(lv[r][i], e) : 0);
     }
   float my_val[NR], top[NR];
   int my_id[NR];
@@ -345,28 +345,57 @@ __device__ void topk_rows_f64(const float* const* L, int E, int k, int* const* i
 }
 
 template <int NK>
+__device__ void poll_tagged(const DecodeArgs& a, const uint64_t* src, int n, uint32_t* out);
+
+// One token's logits, lane l holding experts l, l + 64, ...: polled as
+// tagged words, which carry their own proof of being this launch's (the
+// block path), or read once the router flags are up (the chain).
+template <int NK, bool TAGGED>
+__device__ __forceinline__ void row_logits(const DecodeArgs& a, int t, float (&lv)[NK]) {
+  if constexpr (TAGGED) {
+    uint32_t raw[NK];
+    poll_tagged<NK>(a, a.tagged + (size_t)t * a.E, a.E, raw);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) lv[i] = __uint_as_float(raw[i]);
+  } else {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = lane + kWave * i;
+      lv[i] = e < a.E ? cld(a.logits + (size_t)t * a.E + e) : 0.0f;
+    }
+  }
+}
+
+template <int NK, bool TAGGED>
 __device__ void topk_block_rows(const DecodeArgs& a, int* s_ids, float* s_w) {
   // wave w: token w, and token w + 4 alongside it when there is one
   const int w = threadIdx.x >> 6;
   for (int t = w; t < a.T; t += 2 * (kThreads / kWave)) {
     const int t2 = t + kThreads / kWave;
     if (t2 < a.T) {
-      const float* L[2] = {a.logits + (size_t)t * a.E, a.logits + (size_t)t2 * a.E};
+      float lv[2][NK];
+      row_logits<NK, TAGGED>(a, t, lv[0]);
+      row_logits<NK, TAGGED>(a, t2, lv[1]);
       int* ids[2] = {s_ids + t * a.k, s_ids + t2 * a.k};
       float* ws[2] = {s_w + t * a.k, s_w + t2 * a.k};
-      topk_rows_f64<NK, 2>(L, a.E, a.k, ids, ws);
+      topk_rows_f64<NK, 2>(lv, a.E, a.k, ids, ws);
     } else {
-      const float* L[1] = {a.logits + (size_t)t * a.E};
+      float lv[1][NK];
+      row_logits<NK, TAGGED>(a, t, lv[0]);
       int* ids[1] = {s_ids + t * a.k};
       float* ws[1] = {s_w + t * a.k};
-      topk_rows_f64<NK, 1>(L, a.E, a.k, ids, ws);
+      topk_rows_f64<NK, 1>(lv, a.E, a.k, ids, ws);
     }
   }
 }
 
+// TAGGED: the block path, whose router publishes tagged logits (no flags);
+// otherwise the chain, whose router raises one flag per workgroup.
+template <bool TAGGED>
 __device__ void routing(const DecodeArgs& a, char* lds) {
   // router flags, polled in parallel by this one workgroup
-  for (long it = 0;; ++it) {
+  for (long it = 0; !TAGGED; ++it) {
     bool ok = true;
     for (int i = threadIdx.x; i < a.nb_router; i += kThreads) ok &= cld(a.flags + i) == a.epoch;
     if (__syncthreads_and(ok)) break;
@@ -382,9 +411,9 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
   int* s_first = reinterpret_cast<int*>(s_w + R);
   int* s_tmp = s_first + R;
   if (a.E <= 6 * kWave)
-    topk_block_rows<6>(a, s_ids, s_w);
+    topk_block_rows<6, TAGGED>(a, s_ids, s_w);
   else
-    topk_block_rows<16>(a, s_ids, s_w);
+    topk_block_rows<16, TAGGED>(a, s_ids, s_w);
   __syncthreads();
   // Stable counting sort by ranks, no atomics: pair p (token p / k) of
   // expert e goes to row (#pairs with a smaller expert) + (#earlier pairs
@@ -1689,7 +1718,9 @@ __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkIte
 }
 
 // Block router rows: a wave per expert row, the row's loads issued before
-// the block's T token rows are staged in LDS, then T dot products.
+// the block's T token rows are staged in LDS, then T dot products. Each
+// logit goes out as one tagged word, which the routing wave's poll returns
+// with its value: no flag, and no second read once the flags are seen.
 __device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
   const int lane = lane_id();
   const int e0 = b * 4 + (int)(threadIdx.x >> 6);
@@ -1717,11 +1748,9 @@ __device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
     for (int i = 0; i < kRouterV; ++i)
       if (lane + kWave * i < nv) acc = dot8_bf16(wv[i], s_x[t * nv + lane + kWave * i], acc);
     acc = wave_sum(acc);
-    if (lane == 0 && e0 < a.E) cst(a.logits + (size_t)t * a.E + e, acc + bb);
+    if (lane == 0 && e0 < a.E)
+      cst(a.tagged + (size_t)t * a.E + e, ((uint64_t)a.tag << 32) | __float_as_uint(acc + bb));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) cst(a.flags + b, a.epoch);
 }
 
 // The block's T token rows into LDS (row t at s_x + t * kXRow, chunk-
@@ -1766,7 +1795,7 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int
   if (b < a.nb_router) {
     router_rows_blk(a, b, reinterpret_cast<uint4*>(lds));
   } else if (b == a.nb_router) {
-    routing(a, lds);
+    routing<true>(a, lds);
   } else {
     uint4* s_x = reinterpret_cast<uint4*>(lds);
     stage_block_rows(a, s_x);
@@ -2015,7 +2044,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(DecodeArgs a) {
   if (b < a.nb_router) {
     router_rows(a, b);
   } else if (b == a.nb_router) {
-    routing(a, lds);
+    routing<false>(a, lds);
   } else {
     gateup_item<MT>(a, shared_slot(a), b - a.nb_router - 1, reinterpret_cast<uint4*>(lds), nullptr);
   }
@@ -2104,9 +2133,10 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   L.off_inv = o;
   o += al(sizeof(int32_t) * (size_t)R);
   L.off_tagged = o;
-  // [E] tagged logits, kReplicas routing copies, the shared items' flags
+  // one token: [E] tagged logits, kReplicas routing copies, the shared
+  // items' flags; more tokens: [T][E] tagged logits (the block path's)
   o += al(sizeof(uint64_t) *
-          (ffn || T != 1 ? 0 : (size_t)E + kReplicas * kReplicaWords + L.gu_items));
+          (ffn ? 0 : T == 1 ? (size_t)E + kReplicas * kReplicaWords + L.gu_items : (size_t)T * E));
   L.off_logits = o;
   o += al(sizeof(float) * (size_t)T * E);
   L.off_w = o;
