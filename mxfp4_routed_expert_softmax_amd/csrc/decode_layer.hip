@@ -880,6 +880,13 @@ __device__ void route_token_tagged(const DecodeArgs& a) {
     }
     if (j == 0) top = val;
   }
+  // the gate/up workgroups wait on the ids alone: publish them before the
+  // weights and the down launch's table are worked out
+  if (lane < k) {
+    uint64_t* rep0 = a.tagged + a.E;
+    for (int r = 0; r < kReplicas; ++r)
+      cst(rep0 + (size_t)r * kReplicaWords + lane, ((uint64_t)a.tag << 32) | (uint32_t)my_id);
+  }
   // weights and slots from the k chosen lanes, read lane by lane (cheaper
   // than shuffles through LDS); the sum runs over j = 0..k-1 in order
   const float z = lane < k ? expf(my_val - top) : 0.0f;
@@ -899,9 +906,6 @@ __device__ void route_token_tagged(const DecodeArgs& a) {
     a.route_w[lane] = wj;
     if (a.ids_out) a.ids_out[lane] = my_id;
     if (a.w_out) a.w_out[lane] = wj;
-    uint64_t* rep0 = a.tagged + a.E;
-    for (int r = 0; r < kReplicas; ++r)
-      cst(rep0 + (size_t)r * kReplicaWords + lane, ((uint64_t)a.tag << 32) | (uint32_t)my_id);
   }
   if (lane == 0) a.tab[0] = k;
   for (int i = lane; i < a.dn_items; i += kWave) a.cnt_dn[i] = 0;
