@@ -922,7 +922,7 @@ __device__ void load_routing_tagged(const DecodeArgs& a, int r, int* s_tab) {
     poll_tagged<1>(a, a.tagged + a.E + (size_t)r * kReplicaWords, k, v);
     const int my_id = lane < k ? min(max((int)v[0], 0), a.E - 1) : 0x7fffffff;
     int slot = 0;
-    for (int q = 0; q < k; ++q) slot += __shfl(my_id, q, kWave) < my_id;
+    for (int q = 0; q < k; ++q) slot += __builtin_amdgcn_readlane(my_id, q) < my_id;
     if (lane < k) {
       s_tab[1 + slot] = my_id;
       s_tab[1 + ms + slot] = slot;
