@@ -82,8 +82,8 @@ def log(*a):
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path (the layer would "
-            "shard by expert parallelism; see the design notes). Run with --gpus 1.")
+        log("bench.py measures one GPU: there is no multi-GPU path (the layer would "
+            "shard by expert parallelism). Run with --gpus 1.")
         return 2
 
     import numpy as np
