@@ -91,7 +91,30 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                        0xf, 0xf, false));
+}
+
+// Sum over the wave, in every lane, without the LDS pipe: DPP within each
+// row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror; each step
+// pairs lanes that already hold equal partial sums), then the gfx950 lane
+// swaps across rows (16 apart, then 32), each of which hands every lane its
+// own value and its partner's. Both operands of every add are the same pair
+// in the two lanes, so all lanes end with the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  const uint32_t u = __float_as_uint(v);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
 
 // Inclusive prefix sum across the wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
