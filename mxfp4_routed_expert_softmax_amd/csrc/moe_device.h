@@ -82,39 +82,40 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-// Butterfly sum over groups of G consecutive lanes (G a power of two <= 64);
-// every lane of the group ends with the group sum.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
                                                         0xf, 0xf, false));
 }
 
-// Sum over the wave, in every lane, without the LDS pipe: DPP within each
-// row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror; each step
-// pairs lanes that already hold equal partial sums), then the gfx950 lane
-// swaps across rows (16 apart, then 32), each of which hands every lane its
-// own value and its partner's. Both operands of every add are the same pair
-// in the two lanes, so all lanes end with the same bits.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = dpp_add<0xB1>(v);
-  v = dpp_add<0x4E>(v);
-  v = dpp_add<0x141>(v);
-  v = dpp_add<0x140>(v);
-  const uint32_t u = __float_as_uint(v);
-  const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-  const uint32_t w = __float_as_uint(v);
-  const auto s32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+// Sum over groups of G consecutive lanes (G a power of two <= 64), in every
+// lane of the group, without the LDS pipe: DPP within each row of 16 lanes
+// (xor 1, xor 2, half-row mirror, row mirror; each step pairs lanes that
+// already hold equal partial sums), then the gfx950 lane swaps across rows
+// (16 apart, then 32), each of which hands every lane its own value and its
+// partner's. Both operands of every add are the same pair in the two lanes,
+// so all lanes of a group end with the same bits.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "G: a power of two up to 64");
+  if constexpr (G >= 2) v = dpp_add<0xB1>(v);
+  if constexpr (G >= 4) v = dpp_add<0x4E>(v);
+  if constexpr (G >= 8) v = dpp_add<0x141>(v);
+  if constexpr (G >= 16) v = dpp_add<0x140>(v);
+  if constexpr (G >= 32) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  }
+  if constexpr (G >= 64) {
+    const uint32_t u = __float_as_uint(v);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  }
+  return v;
 }
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
 
 // Inclusive prefix sum across the wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
