@@ -87,10 +87,11 @@ typedef struct moe_mxfp4_bank {
 
 /*
  * An FP8 expert bank: the reference checkpoint's dense format, fp8 weights
- * in 32 x 32 blocks with ue8m0 scales (llama.cpp discussion #28766, "Is it
- * supported?"; the same page and the comment pointing at the port's list of
- * V4 -> V4.1 differences warn that 128 x 128 blocks here mis-scale every
- * weight without any error). Used for the shared expert, so E must be 1.
+ * in 32 x 32 blocks with ue8m0 scales (FreeToken issue #444, "Is the
+ * quantization already supported"). 128 x 128 blocks here would mis-scale
+ * every weight without any error (ai.rs article on DeepSeek-V4.1-Flash, "The
+ * defect that never raised an error"; FreeToken issue #444, angelbaba01L's
+ * comment). Used for the shared expert, so E must be 1.
  *
  *   gate_up_w      [E][2][I][H]       E4M3 bytes, matrix 0 = gate, 1 = up
  *   gate_up_scales [E][2][I/32][H/32] E8M0: block (i, j) covers rows
@@ -114,10 +115,10 @@ typedef struct moe_fp8_bank {
 /*
  * An NVFP4 expert bank, the expert format other engines load V4.1 in
  * (FreeToken issue #444, the comment on the other pull request: "NVFP4
- * experts"; llama.cpp discussion #28766, "Is it supported?"): E2M1 codes with
- * one E4M3 scale per 16 (the layout the same issue gives for the model's fp4
- * KV cache, in the architecture list under janit's comment), plus one fp32
- * scale per expert and matrix.
+ * experts"; the same issue, "Is the quantization already supported"): E2M1
+ * codes with one E4M3 scale per 16 (the layout the same issue gives for the
+ * model's fp4 KV cache, "Architecture delta vs deepseek_v4", its list of
+ * what is new), plus one fp32 scale per expert and matrix.
  *
  *   gate_up_codes  [E][2][I][H/2]   packed as in moe_mxfp4_bank
  *   gate_up_scales [E][2][I][H/16]  E4M3 (OCP fp8) bytes, one per 16 codes
@@ -271,7 +272,7 @@ int moe_expert_ffn_fp8(const void* x_bf16, const moe_fp8_bank* bank, int T, floa
 /*
  * moe_layer_forward with the shared expert in the FP8 format above (the
  * reference checkpoint's layout: FP4 routed experts, FP8 dense weights;
- * llama.cpp discussion #28766, "Is it supported?"). Routing, routed experts,
+ * FreeToken issue #444, "Is the quantization already supported"). Routing, routed experts,
  * ordering and determinism are those of moe_layer_forward; the shared row
  * is added first in the combine, with weight 1. `shared` is required.
  * moe_workspace_bytes covers its workspace.
@@ -309,8 +310,8 @@ int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
  * Opt-in mode with MXFP8 activations on the scaled matrix cores.
  *
  * The reference model runs its linear layers in fp8 with block scales and
- * activations rounded on the fly (llama.cpp discussion #28766, "Is it
- * supported?": a dynamic activation scheme with ue8m0 scales); the pages
+ * activations rounded on the fly (FreeToken issue #444, "Is the quantization
+ * already supported": a dynamic activation scheme with ue8m0 scales); the pages
  * also tabulate what that rounding costs against full precision, about
  * 1.45 % relative error for one fp8 linear layer (ai.rs article on
  * DeepSeek-V4.1-Flash, "What remains is the reference rounding itself").

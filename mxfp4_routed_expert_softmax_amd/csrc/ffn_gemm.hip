@@ -239,13 +239,13 @@ __device__ __forceinline__ void lds_load16(const void* base, uint32_t voff, uint
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
                :
                : "v"(voff), "s"(lds), "s"(base)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ __forceinline__ void lds_load4(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, %2"
                :
                : "v"(voff), "s"(lds), "s"(base)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Weight-row tiling of a workgroup's 256 rows r, and the output columns

@@ -1,7 +1,7 @@
 // One FP8 expert (E4M3 elements, one E8M0 scale per 32 x 32 block) over a
 // few tokens: the checkpoint's dense format, used here for the shared
-// expert (llama.cpp discussion #28766, "Is it supported?": fp8 dense
-// weights with 32 x 32 blocks and ue8m0 scales; the shared expert takes the
+// expert (FreeToken issue #444, "Is the quantization already supported": fp8
+// dense weights with 32 x 32 blocks and ue8m0 scales; the shared expert takes the
 // same input as the routed ones: ai.rs article on DeepSeek-V4.1-Flash, "What
 // remains is the reference rounding itself").
 //

@@ -6,11 +6,12 @@ smoke check and bench.py's CPU-baseline leg use it; the HIP library never does.
 
 The pages: the reference checkpoint stores its dense weights in fp8 with
 32 x 32 weight blocks and ue8m0 scales, and its routed experts in fp4
-(llama.cpp discussion #28766, "Is it supported?"); moving from 128 x 128 to
-32 x 32 scale blocks is one of the silent incompatibilities they warn about,
-since every shape stays valid while each dequantised weight comes out
-mis-scaled (same discussion, the port's list of V4 -> V4.1 differences, and
-the comment pointing at it). The shared expert gets the same input and
+(FreeToken issue #444, "Is the quantization already supported"); moving
+from 128 x 128 to 32 x 32 scale blocks is one of the silent
+incompatibilities they warn about, since every shape stays valid while each
+dequantised weight comes out mis-scaled (ai.rs article on
+DeepSeek-V4.1-Flash, "The defect that never raised an error"; FreeToken
+issue #444, angelbaba01L's comment pointing at the port's write-up). The shared expert gets the same input and
 arithmetic as the routed ones (ai.rs article on DeepSeek-V4.1-Flash, "What
 remains is the reference rounding itself").
 

@@ -134,12 +134,6 @@ def select_topk(L: np.ndarray, k: int):
     return ids, margin
 
 
-def softmax(L: np.ndarray) -> np.ndarray:
-    """Full softmax over the last axis, fp64."""
-    z = np.exp(L - L.max(axis=-1, keepdims=True))
-    return z / z.sum(axis=-1, keepdims=True)
-
-
 def topk_weights(L: np.ndarray, ids: np.ndarray) -> np.ndarray:
     """Routing weights of the chosen experts: the full softmax renormalised
     over the chosen set, written as a softmax over the chosen logits (the

@@ -8,9 +8,9 @@ elements with one E8M0 scale per 32 along the reduction dimension), so that
 both operands of every expert product are microscaled and the matrix cores
 can take the MXFP4 weight codes as they are. The pages describe the
 reference model running its linear layers in fp8 with block scales and
-dynamically rounded activations (llama.cpp discussion #28766, "Is it
-supported?": the checkpoint's quantisation config with a dynamic activation
-scheme and ue8m0 scales; ai.rs article on DeepSeek-V4.1-Flash, "What remains
+dynamically rounded activations (FreeToken issue #444, "Is the quantization
+already supported": the checkpoint's quantisation config with a dynamic
+activation scheme and ue8m0 scales; ai.rs article on DeepSeek-V4.1-Flash, "What remains
 is the reference rounding itself", which also tabulates what one fp8 linear
 layer's rounding costs against full precision). Which activations are
 rounded, and how, the pages leave open; the readings taken here:

@@ -5,11 +5,12 @@ smoke check and bench.py's CPU-baseline leg use it; the HIP library never does.
 
 The pages name NVFP4 as a format other engines load V4.1's experts in
 (FreeToken issue #444, the comment listing what another pull request covers:
-"NVFP4 experts"; llama.cpp discussion #28766, "Is it supported?": FP8 and
-NVFP4 among the formats an engine supports; ai.rs article, its reading list)
+"NVFP4 experts"; the same issue, "Is the quantization already supported":
+FP8 and NVFP4 among the formats the engine supports; ai.rs article, its
+reading list)
 and describe its element-and-scale layout where they describe the model's
 fp4 KV cache: E2M1 elements with one E4M3 scale per 16 (FreeToken issue #444,
-the architecture list under janit's comment).
+"Architecture delta vs deepseek_v4", its list of what is new).
 
 Readings (the pages give no more than that):
 * codes are packed exactly like the MXFP4 banks (byte b of a row holds
