@@ -59,7 +59,9 @@ enum {
   MOE_ERR_INVALID_ARG = -1, /* null required pointer, misalignment, bad size */
   MOE_ERR_UNSUPPORTED = -2, /* well-formed but outside the compiled limits  */
   MOE_ERR_WORKSPACE = -3,   /* ws_bytes smaller than the call needs          */
-  MOE_ERR_HIP = -4          /* a kernel launch failed                        */
+  MOE_ERR_HIP = -4,         /* a kernel launch failed                        */
+  MOE_ERR_TIMEOUT = -5      /* a bounded in-kernel wait gave up (reported by
+                               moe_workspace_status, never by a launch call) */
 };
 
 /*
@@ -156,6 +158,33 @@ const char* moe_status_str(int status);
  * n > 0.
  */
 int moe_set_kernel_events(hipEvent_t* events, int n);
+
+/*
+ * Status of the bounded waits of the last few-token call made with the
+ * workspace `ws`: the layer entry points at T <= 16 tokens run persistent
+ * kernels whose workgroups hand data to one another inside a launch and wait
+ * for it with a bounded number of polls. If one of those waits gives up
+ * (which a correct run never does), the call still finishes with every
+ * access in bounds, and its last launch writes NaN to every element of
+ * `out`, -1 to `topk_ids_out` and NaN to `topk_w_out`, so the failure shows
+ * in the outputs themselves. This call reads the result recorded in the
+ * first 16 bytes of `ws` with a blocking device-to-host copy: synchronise
+ * the call's stream first, and pass the same workspace before reusing it.
+ * Returns MOE_OK (every wait completed, or the last call made with `ws` had
+ * no bounded waits), MOE_ERR_TIMEOUT, MOE_ERR_INVALID_ARG (ws NULL) or
+ * MOE_ERR_HIP (the copy failed).
+ */
+int moe_workspace_status(const void* ws);
+
+/*
+ * Test hook for the reporting above (never needed in use). While `on` is
+ * nonzero, the first bounded wait of the routing in every few-token layer
+ * call made from this host thread expects a tag no word carries and gives up
+ * after 256 polls; every other wait and kernel runs as usual, so each
+ * launch still ends normally. moe_set_wait_test(0) restores normal waits.
+ * Returns MOE_OK.
+ */
+int moe_set_wait_test(int on);
 
 /* Number of kernels the last call from this host thread launched. */
 int moe_last_call_launches(void);

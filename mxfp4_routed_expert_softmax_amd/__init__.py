@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     NvBank,
     NvBankTensors,
     MOE_ERR_HIP,
+    MOE_ERR_TIMEOUT,
     MOE_ERR_INVALID_ARG,
     MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE,
@@ -34,6 +35,8 @@ from ._lib import (  # noqa: F401
     moe_quantize_mxfp8,
     moe_router_topk,
     moe_set_kernel_events,
+    moe_set_wait_test,
+    moe_workspace_status,
     moe_workspace_bytes,
     status_str,
     workspace,

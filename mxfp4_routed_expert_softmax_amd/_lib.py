@@ -24,6 +24,7 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_TIMEOUT = -5
 
 
 class MoeError(RuntimeError):
@@ -98,6 +99,8 @@ _SIGS = {
                                            _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_set_kernel_events": (_I, [_P, _I]),
     "moe_last_call_launches": (_I, []),
+    "moe_workspace_status": (_I, [_P]),
+    "moe_set_wait_test": (_I, [_I]),
     "moe_launch_name": (ctypes.c_char_p, [_I]),
 }
 
@@ -435,3 +438,19 @@ def moe_last_call_launches() -> int:
 def moe_launch_name(i: int) -> str | None:
     r = lib().moe_launch_name(i)
     return None if r is None else r.decode()
+
+
+def moe_workspace_status(ws) -> int:
+    """Wait status of the last few-token call made with workspace `ws`
+    (MOE_OK or MOE_ERR_TIMEOUT); a blocking 16-byte copy, so synchronise
+    the call's stream first. Raises on other errors."""
+    st = lib().moe_workspace_status(_ptr(ws))
+    if st not in (MOE_OK, MOE_ERR_TIMEOUT):
+        _check("moe_workspace_status", st)
+    return st
+
+
+def moe_set_wait_test(on: bool) -> None:
+    """Test hook: while on, the routing's first bounded wait of every
+    few-token layer call from this thread gives up after a few polls."""
+    _check("moe_set_wait_test", lib().moe_set_wait_test(1 if on else 0))

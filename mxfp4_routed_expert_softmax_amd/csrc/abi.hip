@@ -211,6 +211,17 @@ int moe_set_kernel_events(hipEvent_t* events, int n) {
 
 int moe_last_call_launches(void) { return g_log.n; }
 
+int moe_workspace_status(const void* ws) {
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const int code = read_decode_status(ws);
+  return code < 0 ? MOE_ERR_HIP : code == 0 ? MOE_OK : MOE_ERR_TIMEOUT;
+}
+
+int moe_set_wait_test(int on) {
+  set_force_wait_timeout(on != 0);
+  return MOE_OK;
+}
+
 const char* moe_launch_name(int i) {
   return (i >= 0 && i < g_log.n && i < kMaxLogged) ? g_log.names[i] : nullptr;
 }
@@ -238,6 +249,7 @@ const char* moe_status_str(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_TIMEOUT: return "MOE_ERR_TIMEOUT";
     default: return "MOE_ERR_UNKNOWN";
   }
 }

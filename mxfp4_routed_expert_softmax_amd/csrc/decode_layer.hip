@@ -24,10 +24,12 @@
 // Within `route`, the routing workgroup waits for the router workgroups'
 // flags; those have lower indices, and the dispatcher starts workgroups in
 // index order, so they have started and finish: no deadlock whatever the
-// occupancy. A flag holds a 64-bit epoch unique to the launch, so the
+// occupancy. A flag holds a 48-bit tag unique to the call, so the
 // workspace needs no initialisation; the wait is bounded (on timeout it
-// records the failure in a status word and goes on with whatever logits it
-// has, which cannot make an access go out of bounds). Data crossing
+// records the failure in the workspace's status word and goes on with
+// whatever logits it has, which cannot make an access go out of bounds;
+// the call's last launch then fills the outputs with NaN and -1, so a
+// timed-out call never returns plausible numbers). Data crossing
 // workgroups inside a launch (logits, y rows for the combine) moves through
 // agent-scope relaxed atomics, which are performed at the device coherence
 // point, and a producer drains its stores (s_waitcnt) before it raises a
@@ -67,6 +69,18 @@ constexpr int kReplicas = 16;        // copies of the one-token routing table
 constexpr int kReplicaWords = 512;   // 4 KB apart, so readers spread over channels
 constexpr int kRouterV = 16;    // router: 16-byte vectors per lane (H <= 8192)
 constexpr long kSpinLimit = 1L << 20;  // polls (with s_sleep) before giving up
+// A tagged word: the call's 48-bit tag above a 16-bit payload. A reader
+// takes a word as this call's only if it carries the tag, so a stale word
+// from an earlier call (a different tag) or foreign bytes in a fresh
+// workspace (a chance of 2^-48 per word) are never taken for new data.
+constexpr int kTagShift = 16;
+// Codes of the waits, recorded in the status word when one gives up.
+constexpr uint32_t kWaitRouterFlags = 1;  // chain routing: router flags
+constexpr uint32_t kWaitLogits = 2;       // routing: tagged logits
+constexpr uint32_t kWaitTable = 3;        // one-token gate/up: routing table copy
+constexpr uint32_t kWaitShared = 4;       // one-token shared down: shared gate/up flags
+// Result word of a few-token call: this magic above the wait code (0 = OK).
+constexpr uint32_t kResultMagic = 0x57414954u;
 
 constexpr int kLdsGu = kMT * kGuLanes * kGuU * 64;  // bf16 x chunks
 constexpr int kLdsDn = kMT * 8 * kDnU * 128;        // fp32 h chunks
@@ -162,13 +176,18 @@ struct DecodeArgs {
   int32_t* inv_row;    // [T][k]
   float* h;            // [rows][I]
   float* y;            // [rows][H]
-  uint64_t* flags;     // [nb_router] router flags
-  uint64_t* tagged;    // one-token path: [E] logits, then kReplicas routing tables,
-                       // each word (tag << 32 | 32-bit value)
-  uint32_t tag;        // this launch's tag
+  uint64_t* flags;     // [nb_router] router flags (tagged words)
+  uint64_t* tagged;    // tagged words (tag << 16 | 16-bit payload). One token:
+                       // [2][E] logit halves (low, high), kReplicas routing
+                       // tables, the shared items' flags; blocks: [T][2][E]
+  uint64_t tag;        // this call's 48-bit tag (never 0)
+  uint64_t wait_tag;   // the tag the routing's first wait expects: `tag`, or
+                       // (test hook) one that no word carries
+  long wait_limit;     // polls before the routing's first wait gives up
+                       // (every other wait: kSpinLimit)
+  uint64_t* wstat;     // [0] status word: tag << 16 | the code of a wait that
+                       // gave up; [1] result word (kResultMagic << 32 | code)
   int32_t* cnt_dn;     // [dn_items] routed down items finished per column
-  uint64_t epoch;
-  int32_t* status;
   int max_slots;       // routed slots
   int rows;            // rows of h and y (routed rows, then T shared rows)
   int nb_router, gu_items, dn_items;
@@ -192,6 +211,39 @@ __device__ __forceinline__ Slot load_slot(const DecodeArgs& a, int s) {
 
 __device__ __forceinline__ Slot shared_slot(const DecodeArgs& a) {
   return Slot{0, a.R, a.T, true};
+}
+
+__device__ __forceinline__ uint64_t tag_word(uint64_t tag, uint32_t payload) {
+  return (tag << kTagShift) | (payload & 0xffffu);
+}
+
+// A bounded wait gave up: record it for the call's last launch.
+__device__ __forceinline__ void report_timeout(const DecodeArgs& a, uint32_t code) {
+  cst(a.wstat, tag_word(a.tag, code));
+}
+
+// In the call's last launch (every wait of the call ran in earlier
+// launches): the code of a wait that gave up during this call, or 0.
+__device__ __forceinline__ uint32_t call_wait_code(const DecodeArgs& a) {
+  const uint64_t v = cld(a.wstat);
+  return (v >> kTagShift) == a.tag ? (uint32_t)(v & 0xffffu) : 0u;
+}
+
+// The last launch of a call whose wait gave up: NaN outputs, ids -1 and
+// weights NaN (workgroup b of nb covers its share of out); workgroup 0
+// records the call's result for moe_workspace_status.
+__device__ void finish_call(const DecodeArgs& a, uint32_t code, int b, int nb) {
+  if (code) {
+    const long n = (long)a.T * a.H;
+    for (long i = (long)b * kThreads + threadIdx.x; i < n; i += (long)nb * kThreads)
+      a.out[i] = __builtin_nanf("");
+    if (b == 0)
+      for (int i = threadIdx.x; i < a.R; i += kThreads) {
+        if (a.ids_out) a.ids_out[i] = -1;
+        if (a.w_out) a.w_out[i] = __builtin_nanf("");
+      }
+  }
+  if (b == 0 && threadIdx.x == 0) a.wstat[1] = ((uint64_t)kResultMagic << 32) | code;
 }
 
 // ---------------------------------------------------------------------------
@@ -222,7 +274,7 @@ __device__ void router_rows(const DecodeArgs& a, int b) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) cst(a.flags + b, a.epoch);
+  if (threadIdx.x == 0) cst(a.flags + b, tag_word(a.tag, 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -344,8 +396,9 @@ __device__ void topk_rows_f64(const float (&lv)[NR][NK], int E, int k, int* cons
   }
 }
 
-template <int NK>
-__device__ void poll_tagged(const DecodeArgs& a, const uint64_t* src, int n, uint32_t* out);
+template <int NK, int HALVES>
+__device__ void poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, uint32_t code,
+                            const uint64_t* src, int n, uint32_t* out);
 
 // One token's logits, lane l holding experts l, l + 64, ...: polled as
 // tagged words, which carry their own proof of being this launch's (the
@@ -354,7 +407,8 @@ template <int NK, bool TAGGED>
 __device__ __forceinline__ void row_logits(const DecodeArgs& a, int t, float (&lv)[NK]) {
   if constexpr (TAGGED) {
     uint32_t raw[NK];
-    poll_tagged<NK>(a, a.tagged + (size_t)t * a.E, a.E, raw);
+    poll_tagged<NK, 2>(a, a.wait_tag, a.wait_limit, kWaitLogits, a.tagged + (size_t)t * 2 * a.E,
+                       a.E, raw);
 #pragma unroll
     for (int i = 0; i < NK; ++i) lv[i] = __uint_as_float(raw[i]);
   } else {
@@ -397,10 +451,11 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
   // router flags, polled in parallel by this one workgroup
   for (long it = 0; !TAGGED; ++it) {
     bool ok = true;
-    for (int i = threadIdx.x; i < a.nb_router; i += kThreads) ok &= cld(a.flags + i) == a.epoch;
+    for (int i = threadIdx.x; i < a.nb_router; i += kThreads)
+      ok &= cld(a.flags + i) == tag_word(a.wait_tag, 1);
     if (__syncthreads_and(ok)) break;
-    if (it > kSpinLimit) {
-      if (threadIdx.x == 0) cst(a.status, 1);
+    if (it >= a.wait_limit) {
+      if (threadIdx.x == 0) report_timeout(a, kWaitRouterFlags);
       break;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -683,8 +738,9 @@ __device__ void down_item(const DecodeArgs& a, const Slot& sd, int rb, f32x4_t* 
 
 // Combine of output columns [32c, 32c + 32): the shared row, then the k
 // routed rows in slot order j = 0..k-1, one fp32 fma each (coherent loads:
-// rows may have been written by other workgroups of this launch).
-__device__ void combine_column(const DecodeArgs& a, int c) {
+// rows may have been written by other workgroups of this launch). `failed`:
+// a wait of this call gave up, so the column is NaN.
+__device__ void combine_column(const DecodeArgs& a, int c, bool failed) {
   const int n = c * kDnRows + (threadIdx.x & 31);
   if (n >= a.H) return;
   for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
@@ -701,7 +757,7 @@ __device__ void combine_column(const DecodeArgs& a, int c) {
       for (int u = 0; u < 8; ++u)
         if (j0 + u < a.k) v = fmaf(a.route_w[t * a.k + j0 + u], yv[u], v);
     }
-    a.out[(size_t)t * a.H + n] = v;
+    a.out[(size_t)t * a.H + n] = failed ? __builtin_nanf("") : v;
   }
 }
 
@@ -812,30 +868,38 @@ __device__ void router_rows_one(const DecodeArgs& a, int b, uint4* s_x) {
     if (lane + kWave * i < nv) acc = dot8_bf16(wv[i], s_x[lane + kWave * i], acc);
   acc = wave_sum(acc);
   if (lane == 0 && b * 4 + (int)(threadIdx.x >> 6) < a.E) {
-    const float v = acc + (a.bias ? a.bias[e] : 0.0f);
-    cst(a.tagged + e, ((uint64_t)a.tag << 32) | __float_as_uint(v));
+    const uint32_t v = __float_as_uint(acc + (a.bias ? a.bias[e] : 0.0f));
+    cst(a.tagged + e, tag_word(a.tag, v));
+    cst(a.tagged + a.E + e, tag_word(a.tag, v >> 16));
   }
 }
 
-// Polls `n` tagged words at `src` (lane i holds words i, i + 64, ...) until
-// every one carries `tag`; returns the values through `out` (NK per lane).
-// Bounded: a timeout sets the status word and returns what was read, which
-// every consumer clamps.
-template <int NK>
-__device__ void poll_tagged(const DecodeArgs& a, const uint64_t* src, int n, uint32_t* out) {
+// Polls `n` values at `src` (lane i holds values i, i + 64, ...) until every
+// word carries the tag `expect`; each value is HALVES tagged words, its
+// 16-bit pieces at src + h n (h = 0 the low piece). Returns the values
+// through `out` (NK per lane). Bounded: a timeout records `code` in the
+// status word and returns what was read, which every consumer clamps.
+template <int NK, int HALVES>
+__device__ void poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, uint32_t code,
+                            const uint64_t* src, int n, uint32_t* out) {
   const int lane = lane_id();
   for (long it = 0;; ++it) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int q = lane + kWave * i;
-      const uint64_t v = q < n ? cld(src + q) : ((uint64_t)a.tag << 32);
-      out[i] = (uint32_t)v;
-      ok &= (uint32_t)(v >> 32) == a.tag;
+      uint32_t val = 0;
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h) {
+        const uint64_t v = q < n ? cld(src + (size_t)h * n + q) : tag_word(expect, 0);
+        val |= (uint32_t)(v & 0xffffu) << (16 * h);
+        ok &= (v >> kTagShift) == expect;
+      }
+      out[i] = val;
     }
     if (__all(ok)) return;
-    if (it > kSpinLimit) {
-      if (lane == 0) cst(a.status, 2);
+    if (it >= limit) {
+      if (lane == 0) report_timeout(a, code);
       return;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -851,7 +915,7 @@ template <int NK>
 __device__ void route_token_tagged(const DecodeArgs& a) {
   const int lane = lane_id(), k = a.k, ms = a.max_slots;
   uint32_t raw[NK];
-  poll_tagged<NK>(a, a.tagged, a.E, raw);
+  poll_tagged<NK, 2>(a, a.wait_tag, a.wait_limit, kWaitLogits, a.tagged, a.E, raw);
   // k rounds of: each lane's best remaining key, the wave's best of those
   // (fp64 max on the keys' bits), and that key taken out
   double key[NK];
@@ -883,9 +947,9 @@ __device__ void route_token_tagged(const DecodeArgs& a) {
   // the gate/up workgroups wait on the ids alone: publish them before the
   // weights and the down launch's table are worked out
   if (lane < k) {
-    uint64_t* rep0 = a.tagged + a.E;
+    uint64_t* rep0 = a.tagged + 2 * a.E;
     for (int r = 0; r < kReplicas; ++r)
-      cst(rep0 + (size_t)r * kReplicaWords + lane, ((uint64_t)a.tag << 32) | (uint32_t)my_id);
+      cst(rep0 + (size_t)r * kReplicaWords + lane, tag_word(a.tag, (uint32_t)my_id));
   }
   // weights and slots from the k chosen lanes, read lane by lane (cheaper
   // than shuffles through LDS); the sum runs over j = 0..k-1 in order
@@ -919,7 +983,8 @@ __device__ void load_routing_tagged(const DecodeArgs& a, int r, int* s_tab) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     uint32_t v[1];
-    poll_tagged<1>(a, a.tagged + a.E + (size_t)r * kReplicaWords, k, v);
+    poll_tagged<1, 1>(a, a.tag, kSpinLimit, kWaitTable,
+                      a.tagged + 2 * a.E + (size_t)r * kReplicaWords, k, v);
     const int my_id = lane < k ? min(max((int)v[0], 0), a.E - 1) : 0x7fffffff;
     int slot = 0;
     for (int q = 0; q < k; ++q) slot += __builtin_amdgcn_readlane(my_id, q) < my_id;
@@ -1225,7 +1290,7 @@ __device__ __forceinline__ void dn_compute_nv(const DecodeArgs& a, const int* ta
 // and weights come from LDS; the y rows were written by other workgroups of
 // this launch (coherent loads, all issued together).
 __device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
-                                   const float* s_w) {
+                                   const float* s_w, bool failed) {
   const int n = c * kDnRows + (int)threadIdx.x;
   if (threadIdx.x >= kDnRows || n >= a.H) return;
   float v = a.y_shared_ext ? a.y_shared_ext[n]
@@ -1241,7 +1306,7 @@ __device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
     for (int u = 0; u < 8; ++u)
       if (j0 + u < a.k) v = fmaf(s_w[j0 + u], y[u], v);
   }
-  a.out[n] = v;
+  a.out[n] = failed ? __builtin_nanf("") : v;
 }
 
 // Decode gate/up, one launch: [router rows | the routing workgroup |
@@ -1253,7 +1318,7 @@ __device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
 // Completion flags of the shared expert's gate/up items in the one-token
 // launch: one tagged word per item, after the routing copies.
 __device__ __forceinline__ uint64_t* shared_flags(const DecodeArgs& a) {
-  return a.tagged + a.E + (size_t)kReplicas * kReplicaWords;
+  return a.tagged + 2 * a.E + (size_t)kReplicas * kReplicaWords;
 }
 
 // The shared expert's down item c (32 output rows) inside the one-token
@@ -1265,7 +1330,7 @@ __device__ __forceinline__ uint64_t* shared_flags(const DecodeArgs& a) {
 __device__ void shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
   if (threadIdx.x < kWave) {
     uint32_t v[6];
-    poll_tagged<6>(a, shared_flags(a), n_sh, v);
+    poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
   }
   __syncthreads();
   DnRegs A;
@@ -1361,7 +1426,7 @@ __device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, char*
   }
   if (threadIdx.x < kWave) {
     uint32_t v[6];
-    poll_tagged<6>(a, shared_flags(a), n_sh, v);
+    poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
   }
   __syncthreads();
   f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds);
@@ -1413,7 +1478,7 @@ __device__ void nv_shared_down_item(const DecodeArgs& a, int c, int n_sh, char* 
   dn_issue_nv(a, nullptr, 0, c, A, true, false);
   if (threadIdx.x < kWave) {
     uint32_t v[6];
-    poll_tagged<6>(a, shared_flags(a), n_sh, v);
+    poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
   }
   __syncthreads();
   dn_issue_h<true>(a, min(a.R, a.rows - 1), A);
@@ -1450,7 +1515,7 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
       gateup_item<1, true>(a, shared_slot(a), item, reinterpret_cast<uint4*>(lds), nullptr);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) cst(shared_flags(a) + item, ((uint64_t)a.tag << 32) | 1u);
+    if (threadIdx.x == 0) cst(shared_flags(a) + item, tag_word(a.tag, 1));
     return;
   }
   if (b0 >= a.nb_router + 1 + n_shared + G) {
@@ -1516,6 +1581,9 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
     s_inv[i] = a.inv_row[i];
     s_w[i] = a.route_w[i];
   }
+  // every wait of the call ran in launch 1
+  const uint32_t code = call_wait_code(a);
+  finish_call(a, code, blockIdx.x, gridDim.x);
   __syncthreads();
   const int ns = min(max(tab[0], 0), a.max_slots);
   const int nr = ns * a.dn_items;
@@ -1555,7 +1623,7 @@ __global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int
   }
   __syncthreads();
   for (int t = 0; t < min(mine, 32); ++t)
-    if (s_last[t]) combine_column_one(a, (b + t * G) % a.dn_items, s_inv, s_w);
+    if (s_last[t]) combine_column_one(a, (b + t * G) % a.dn_items, s_inv, s_w, code != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1752,8 +1820,11 @@ __device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
     for (int i = 0; i < kRouterV; ++i)
       if (lane + kWave * i < nv) acc = dot8_bf16(wv[i], s_x[t * nv + lane + kWave * i], acc);
     acc = wave_sum(acc);
-    if (lane == 0 && e0 < a.E)
-      cst(a.tagged + (size_t)t * a.E + e, ((uint64_t)a.tag << 32) | __float_as_uint(acc + bb));
+    if (lane == 0 && e0 < a.E) {
+      const uint32_t v = __float_as_uint(acc + bb);
+      cst(a.tagged + (size_t)t * 2 * a.E + e, tag_word(a.tag, v));
+      cst(a.tagged + (size_t)t * 2 * a.E + a.E + e, tag_word(a.tag, v >> 16));
+    }
   }
 }
 
@@ -1835,12 +1906,18 @@ __device__ __forceinline__ void dn_issue_blk(const DecodeArgs& a, const BlkItem&
 // Direct global -> LDS copy: lane l's 16 bytes at base + voff land at LDS
 // byte address lds + 16 l (lds wave-uniform). Invisible to the compiler's
 // wait counting: the caller waits for it explicitly.
+// m0 is named as clobbered so the compiler keeps nothing there and puts
+// the needed wait state between a copy and the next write of m0 (clang's
+// warning that m0 is reserved is silenced here only).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
                :
                : "v"(voff), "s"(lds), "s"(base)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 constexpr int kHRow = 8 * kDnU * 8;    // f32x4_t per staged h row (I <= 2304)
 constexpr int kDnIssueLoads = 2 * kDnU;  // vector loads of one dn_issue_blk
@@ -2035,7 +2112,9 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
 // Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
 // token in fixed order (shared row, then j = 0..k-1).
 __global__ __launch_bounds__(kThreads) void combine_block_kernel(DecodeArgs a) {
-  combine_column(a, blockIdx.x);
+  const uint32_t code = call_wait_code(a);  // every wait of the call ran in launch 1
+  finish_call(a, code, blockIdx.x, gridDim.x);
+  combine_column(a, blockIdx.x, code != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -2076,6 +2155,10 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int combin
   __shared__ int s_last;
   const int b = blockIdx.x;
   const int s = b % a.max_slots, c = b / a.max_slots;
+  // the last launch of the call: every wait ran in the route launch (the
+  // FFN mode has none)
+  const uint32_t code = combine ? call_wait_code(a) : 0u;
+  finish_call(a, code, b, gridDim.x);
   const int ns = load_nslots(a);
   if (s >= ns) return;
   down_item<MT>(a, load_slot(a, s), c, reinterpret_cast<f32x4_t*>(lds), a.y, combine != 0);
@@ -2086,7 +2169,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int combin
     s_last = __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              ns - 1;
   __syncthreads();
-  if (s_last) combine_column(a, c);
+  if (s_last) combine_column(a, c, code != 0);
 }
 
 }  // namespace
@@ -2096,21 +2179,30 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int combin
 // ---------------------------------------------------------------------------
 
 namespace {
-uint64_t next_epoch() {
-  // 64-bit tags unique per launch: the high bits come from the start time of
-  // the process, so stale flags left in a reused workspace never match.
+constexpr uint64_t kTagMask = (1ull << 48) - 1;
+
+// 48-bit tags unique per call: a counter on a base drawn from the process's
+// start time and id, so words left in a reused workspace by earlier calls
+// (of this or another process) never carry the tag of a new call.
+uint64_t next_tag() {
   static std::atomic<uint64_t> counter{0};
   static const uint64_t base = [] {
     const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-    return (t << 20) ^ ((uint64_t)getpid() << 44);
+    return (t << 16) ^ ((uint64_t)getpid() << 28) ^ (t >> 20);
   }();
-  uint64_t v = base + (++counter);
+  const uint64_t v = (base + (++counter)) & kTagMask;
   return v == 0 ? 1 : v;
 }
 
+// Test hook (moe_set_wait_test): the routing's first wait of each call
+// expects a tag no word carries and gives up after a few polls; every other
+// wait keeps its usual limit and completes.
+thread_local int g_force_timeout = 0;
+constexpr long kForcedSpinLimit = 256;
+
 struct DecodeLayout {
   int max_slots, rows, gu_items, dn_items, nb_router;
-  size_t off_flags, off_cnt, off_status, off_tab, off_rt, off_inv, off_logits, off_w, off_h, off_y,
+  size_t off_wstat, off_flags, off_cnt, off_tab, off_rt, off_inv, off_logits, off_w, off_h, off_y,
       off_tagged, bytes;
 };
 
@@ -2124,12 +2216,12 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   L.dn_items = (H + kDnRows - 1) / kDnRows;
   L.nb_router = ffn ? 0 : (E + 3) / 4;
   size_t o = 0;
+  L.off_wstat = o;  // first, at a fixed place: moe_workspace_status reads it
+  o += al(2 * sizeof(uint64_t));
   L.off_flags = o;
   o += al(sizeof(uint64_t) * (L.nb_router + 1));
   L.off_cnt = o;
   o += al(sizeof(int32_t) * (size_t)L.dn_items);
-  L.off_status = o;
-  o += al(sizeof(int32_t));
   L.off_tab = o;
   o += al(sizeof(int32_t) * (1 + 3 * (size_t)L.max_slots));
   L.off_rt = o;
@@ -2137,10 +2229,11 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   L.off_inv = o;
   o += al(sizeof(int32_t) * (size_t)R);
   L.off_tagged = o;
-  // one token: [E] tagged logits, kReplicas routing copies, the shared
-  // items' flags; more tokens: [T][E] tagged logits (the block path's)
+  // one token: [2][E] tagged logit halves, kReplicas routing copies, the
+  // shared items' flags; more tokens: [T][2][E] (the block path's)
   o += al(sizeof(uint64_t) *
-          (ffn ? 0 : T == 1 ? (size_t)E + kReplicas * kReplicaWords + L.gu_items : (size_t)T * E));
+          (ffn ? 0 : T == 1 ? 2 * (size_t)E + kReplicas * kReplicaWords + L.gu_items
+                            : 2 * (size_t)T * E));
   L.off_logits = o;
   o += al(sizeof(float) * (size_t)T * E);
   L.off_w = o;
@@ -2156,6 +2249,15 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
 
 size_t decode_ws_bytes(int T, int H, int I, int E, int k, int R, bool ffn, bool shared) {
   return layout(T, H, I, E, k, R, ffn, shared).bytes;
+}
+
+void set_force_wait_timeout(int on) { g_force_timeout = on; }
+
+int read_decode_status(const void* ws) {
+  uint64_t v[2] = {0, 0};
+  if (hipMemcpy(v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  if ((uint32_t)(v[1] >> 32) != kResultMagic) return 0;  // no few-token call recorded
+  return (int)(uint32_t)v[1];
 }
 
 template <int MT>
@@ -2255,7 +2357,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.flags = reinterpret_cast<uint64_t*>(w + L.off_flags);
   a.tagged = reinterpret_cast<uint64_t*>(w + L.off_tagged);
   a.cnt_dn = reinterpret_cast<int32_t*>(w + L.off_cnt);
-  a.status = reinterpret_cast<int32_t*>(w + L.off_status);
+  a.wstat = reinterpret_cast<uint64_t*>(w + L.off_wstat);
   a.tab = reinterpret_cast<int32_t*>(w + L.off_tab);
   a.row_token = reinterpret_cast<int32_t*>(w + L.off_rt);
   a.inv_row = reinterpret_cast<int32_t*>(w + L.off_inv);
@@ -2263,11 +2365,9 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.route_w = reinterpret_cast<float*>(w + L.off_w);
   a.h = reinterpret_cast<float*>(w + L.off_h);
   a.y = ffn ? d.y_rows : reinterpret_cast<float*>(w + L.off_y);
-  a.epoch = next_epoch();
-  // 32-bit tag of the launch: consecutive launches differ in the low bits
-  // of the epoch, hence in the tag; zero (a cleared workspace) is never used.
-  a.tag = (uint32_t)(a.epoch ^ (a.epoch >> 32));
-  if (a.tag == 0) a.tag = 0x9e3779b9u;
+  a.tag = next_tag();
+  a.wait_tag = g_force_timeout ? (a.tag ^ 1) : a.tag;
+  a.wait_limit = g_force_timeout ? kForcedSpinLimit : kSpinLimit;
   a.max_slots = L.max_slots;
   a.rows = L.rows;
   a.nb_router = L.nb_router;

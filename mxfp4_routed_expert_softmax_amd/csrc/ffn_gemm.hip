@@ -235,6 +235,12 @@ __device__ __forceinline__ uint32_t word_of(uint4 v, int s) {
 // them: the kernel waits explicitly (vmcnt + barrier) before reading a
 // stage. The compiler's own waits for register loads stay correct, as
 // vector loads complete in issue order.
+// m0 is named as clobbered so the compiler knows each copy rewrites it: it
+// then keeps no value of its own there and puts the wait state the
+// hardware needs between a copy and the next write of m0. (clang warns that
+// m0 is a reserved register; the warning is silenced for these two only.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_load16(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
                :
@@ -247,6 +253,7 @@ __device__ __forceinline__ void lds_load4(const void* base, uint32_t voff, uint3
                : "v"(voff), "s"(lds), "s"(base)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Weight-row tiling of a workgroup's 256 rows r, and the output columns
 // (n0 = tile column offset): gate/up: r < 128 -> gate row n0 + r, else the

@@ -151,6 +151,12 @@ bool decode_fuses_fp8_shared(const DecodeLaunch& d);
 // only the one-token fused launches hold NVFP4 items.
 bool decode_fuses_nvfp4(const DecodeLaunch& d);
 void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s);
+// Test hook: while on, the routing's first bounded wait of each few-token
+// layer call gives up after a few polls (calling thread only).
+void set_force_wait_timeout(int on);
+// Wait code recorded by the last few-token call made with workspace `ws`
+// (0 = every wait completed; blocking 16-byte copy), or -1 if the copy fails.
+int read_decode_status(const void* ws);
 
 void launch_combine(const float* y_rows, const int32_t* inv_row, const float* w,
                     const float* y_shared, int T, int k, int H, int R, float* out,

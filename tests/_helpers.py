@@ -47,6 +47,16 @@ def bank_to_dev(arrs: dict):
     return M.BankTensors.from_numpy(arrs, dev())
 
 
+def assert_waits_ok(ws) -> None:
+    """The call just made with workspace `ws` finished with every bounded
+    in-kernel wait completed (moe_workspace_status after a stream sync)."""
+    import torch
+    import mxfp4_routed_expert_softmax_amd as M
+    torch.cuda.synchronize()
+    st = M.moe_workspace_status(ws)
+    assert st == M.MOE_OK, M.status_str(st)
+
+
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

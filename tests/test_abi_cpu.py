@@ -21,7 +21,8 @@ def test_library_exports_every_header_function():
                           "moe_last_call_launches", "moe_launch_name",
                           "moe_quantize_mxfp8", "moe_layer_forward_mxfp8_act",
                           "moe_expert_ffn_fp8", "moe_layer_forward_fp8_shared",
-                          "moe_expert_ffn_nvfp4", "moe_layer_forward_nvfp4"}
+                          "moe_expert_ffn_nvfp4", "moe_layer_forward_nvfp4",
+                          "moe_workspace_status", "moe_set_wait_test"}
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -34,6 +35,7 @@ def test_library_exports_every_header_function():
 def test_status_strings():
     assert M.status_str(0) == "MOE_OK"
     assert M.status_str(-3) == "MOE_ERR_WORKSPACE"
+    assert M.status_str(-5) == "MOE_ERR_TIMEOUT"
     assert M.status_str(99) == "MOE_ERR_UNKNOWN"
 
 
@@ -192,3 +194,8 @@ def test_nvfp4_entry_points_validate_before_launching():
     assert ffn(good, off=None) == M.MOE_ERR_INVALID_ARG   # E > 1 needs offsets
     assert ffn(good, R=-1) == M.MOE_ERR_INVALID_ARG
     assert ffn(good, R=0) == M.MOE_OK
+
+
+def test_workspace_status_rejects_a_null_workspace_without_a_device_call():
+    assert M.lib().moe_workspace_status(None) == M.MOE_ERR_INVALID_ARG
+    assert M.lib().moe_set_wait_test(0) == M.MOE_OK

@@ -108,6 +108,7 @@ def run_layer_fp8(x_bits, wr_bits, bias, routed_dev, shared_dev, k):
     b = None if bias is None else HP.to_dev(bias)
     M.moe_layer_forward_fp8_shared(HP.to_dev(x_bits), HP.to_dev(wr_bits), b, routed_dev,
                                    shared_dev, k, out, ids, wt, ws)
+    HP.assert_waits_ok(ws)
     names = _launch_names()
     return _np(out), _np(ids), _np(wt), names
 
@@ -228,6 +229,7 @@ def test_layer_fp8_shared_one_token_deterministic_and_garbage_workspace():
         M.moe_layer_forward_fp8_shared(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, None,
                                        None, ws)
         assert _launch_names() == ["gateup_fused_kernel", "down_stream_kernel"]
+        HP.assert_waits_ok(ws)
         outs.append(_np(out))
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))

@@ -96,6 +96,7 @@ def run_layer(x_bits, wr_bits, bias, routed_np, shared_np, k):
     ws = M.workspace(T, rd.H, rd.I, rd.E, k, HP.dev())
     b = None if bias is None else HP.to_dev(bias)
     M.moe_layer_forward_nvfp4(HP.to_dev(x_bits), HP.to_dev(wr_bits), b, rd, sd, k, out, ids, wt, ws)
+    HP.assert_waits_ok(ws)
     return _np(out), _np(ids), _np(wt), _names()
 
 
@@ -199,6 +200,7 @@ def test_one_token_fused_deterministic_and_garbage_workspace():
         out = torch.empty((w.T, w.H), dtype=torch.float32, device=HP.dev())
         M.moe_layer_forward_nvfp4(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, None, None, ws)
         assert _names() == FUSED
+        HP.assert_waits_ok(ws)
         outs.append(_np(out))
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint8), outs[0].view(np.uint8))

@@ -149,6 +149,7 @@ def run_ffn(x_bits, bank_np, offsets, row_token, R):
     T = x.shape[0]
     ws = M.workspace(T, bank.H, bank.I, bank.E, max(1, -(-R // T)), HP.dev())
     M.moe_expert_ffn_mxfp4(x, bank, off, rt, R, y, ws)
+    HP.assert_waits_ok(ws)
     return _np(y)[:R]
 
 
@@ -253,6 +254,7 @@ def run_layer(x_bits, wr_bits, bias, routed_dev, shared_dev, k):
     wt = torch.empty((T, k), dtype=torch.float32, device=HP.dev())
     ws = M.workspace(T, routed_dev.H, routed_dev.I, routed_dev.E, k, HP.dev())
     M.moe_layer_forward(x, wr, b, routed_dev, shared_dev, k, out, ids, wt, ws)
+    HP.assert_waits_ok(ws)
     return _np(out), _np(ids), _np(wt)
 
 
@@ -438,6 +440,7 @@ def test_layer_one_token_shapes_share_a_garbage_workspace():
             M.moe_layer_forward(HP.to_dev(d["x"]), HP.to_dev(d["w_router"]), None, rd, sd, w.k,
                                 out, ids, wt, ws)
             assert _launches() == ONE_TOKEN_PATH
+            HP.assert_waits_ok(ws)
             ref = O.layer(d["x"], d["w_router"], None, d["routed"], d["shared"], w.k)
             alt = HP.check_routing(ref, _np(ids), _np(wt), w.k)
             err = HP.rel_l2(_np(out), HP.reference_rows(ref, d["routed"], d["shared"],
@@ -517,6 +520,7 @@ def test_layer_token_counts_share_one_workspace():
         ids = torch.empty((T, w.k), dtype=torch.int32, device=HP.dev())
         wt = torch.empty((T, w.k), dtype=torch.float32, device=HP.dev())
         M.moe_layer_forward(HP.to_dev(x_bits), wr, None, rd, sd, w.k, out, ids, wt, ws)
+        HP.assert_waits_ok(ws)
         ref = O.layer(x_bits, d["w_router"], None, d["routed"], d["shared"], w.k)
         alt = HP.check_routing(ref, _np(ids), _np(wt), w.k)
         err = HP.rel_l2(_np(out), HP.reference_rows(ref, d["routed"], d["shared"],
@@ -536,6 +540,7 @@ def test_layer_with_garbage_workspace():
     ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device=HP.dev(), generator=g))
     out = torch.empty((w.T, w.H), dtype=torch.float32, device=HP.dev())
     M.moe_layer_forward(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, ws=ws)
+    HP.assert_waits_ok(ws)
     ref = O.layer(x, wr, None, routed, shared, w.k)
     assert HP.rel_l2(_np(out), ref["out"]) < 1e-5
 
