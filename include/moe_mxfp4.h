@@ -289,6 +289,33 @@ int moe_layer_forward(const void* x_bf16, const void* w_router_bf16,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops and harnesses that forbid hipMalloc. Same
+ * arguments, results, bit patterns and errors as moe_layer_forward, except
+ * that there is no workspace argument: the scratch is a 16 MiB array of
+ * device memory that the library holds on each GPU it runs on, from its
+ * load until the process ends. This call never allocates or frees memory.
+ *
+ *  - A call whose workspace need (as for moe_layer_forward) exceeds 16 MiB
+ *    returns MOE_ERR_WORKSPACE and enqueues nothing. At the real layer shape
+ *    (H 5120, I 2304, 384 experts, top-6, a shared expert) every call of up
+ *    to 16 tokens fits: decode and verification blocks.
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last
+ *    call's contents; nothing in it needs clearing between calls. Calls that
+ *    overlap on one GPU (other streams, other host threads) race on it and
+ *    must be serialised by the caller.
+ *  - A bounded in-kernel wait that gives up shows in the outputs as with
+ *    moe_layer_forward (NaN out, ids -1); moe_workspace_status cannot read
+ *    this array.
+ *  - The first call on a device looks up the array's address on that device
+ *    (MOE_ERR_HIP if the lookup fails).
+ */
+int moe_layer_forward_noalloc(const void* x_bf16, const void* w_router_bf16,
+                              const float* logit_bias, const moe_mxfp4_bank* routed,
+                              const moe_mxfp4_bank* shared, int T, int k, float* out,
+                              int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream);
+
+/*
  * One FP8 expert over T rows (the shared expert or a dense SwiGLU FFN in the
  * checkpoint's fp8 format): y[t] = W_down (silu(W_gate x_t) * (W_up x_t)),
  * weights dequantised exactly (E4M3 times a power of two), products summed

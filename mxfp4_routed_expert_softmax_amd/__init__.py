@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     moe_layer_forward,
     moe_layer_forward_fp8_shared,
     moe_layer_forward_mxfp8_act,
+    moe_layer_forward_noalloc,
     moe_layer_forward_nvfp4,
     moe_permute,
     moe_quantize_mxfp8,

@@ -90,6 +90,8 @@ _SIGS = {
                                 _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward_mxfp8_act": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank),
                                           _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (_I, [_P, _P, _P, ctypes.POINTER(Bank), ctypes.POINTER(Bank),
+                                        _I, _I, _P, _P, _P, _P]),
     "moe_quantize_mxfp8": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_expert_ffn_fp8": (_I, [_P, ctypes.POINTER(Fp8Bank), _I, _P, _P, _SZ, _P]),
     "moe_expert_ffn_nvfp4": (_I, [_P, ctypes.POINTER(NvBank), _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -366,6 +368,24 @@ def moe_layer_forward(x, w_router, logit_bias, routed: BankTensors, shared: Bank
                       k, out, topk_ids_out=None, topk_w_out=None, ws=None, stream=None):
     _layer("moe_layer_forward", x, w_router, logit_bias, routed, shared, k, out, topk_ids_out,
            topk_w_out, ws, stream)
+
+
+def moe_layer_forward_noalloc(x, w_router, logit_bias, routed: BankTensors,
+                              shared: BankTensors | None, k, out, topk_ids_out=None,
+                              topk_w_out=None, stream=None):
+    """moe_layer_forward on the library's own fixed per-GPU scratch (no
+    workspace argument; the call allocates nothing)."""
+    import torch
+    _need(x, "x", _bf16_types(), 2)
+    _need(w_router, "w_router", _bf16_types(), 2)
+    _need(out, "out", (torch.float32,), 2)
+    if logit_bias is not None:
+        _need(logit_bias, "logit_bias", (torch.float32,))
+    st = lib().moe_layer_forward_noalloc(
+        _ptr(x), _ptr(w_router), _ptr(logit_bias), ctypes.byref(routed.struct),
+        None if shared is None else ctypes.byref(shared.struct), x.shape[0], k, _ptr(out),
+        _ptr(topk_ids_out), _ptr(topk_w_out), _stream(stream, x))
+    _check("moe_layer_forward_noalloc", st)
 
 
 def moe_layer_forward_mxfp8_act(x, w_router, logit_bias, routed: BankTensors,

@@ -1,8 +1,18 @@
 // extern "C" entry points: argument validation, workspace layout and launch
 // order. Everything is validated before the first launch, so an error
 // return means nothing was enqueued. The host never synchronises.
+#include <mutex>
+
 #include "moe_mxfp4.h"
 #include "moe_internal.h"
+
+// Scratch of moe_layer_forward_noalloc: device memory the library holds on
+// each GPU it runs on, from the module's load until the process ends. In
+// host code `scratch` names a host-side stand-in, not a device address:
+// only the per-device address from hipGetSymbolAddress (noalloc_scratch
+// below) is ever passed to a kernel.
+constexpr size_t kNoallocScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -172,6 +182,27 @@ LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
   L.y_sh = c.take<float>((size_t)T * H);
   L.bytes = c.off;
   return L;
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; MOE_ERR_HIP if the lookup
+// fails, MOE_ERR_UNSUPPORTED beyond kMaxDevices devices.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 // Launch log of the last entry-point call on this host thread.
@@ -666,6 +697,20 @@ int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
     launch_expert_ffn(p, stream);
   launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
   return launch_status();
+}
+
+int moe_layer_forward_noalloc(const void* x_bf16, const void* w_router_bf16,
+                              const float* logit_bias, const moe_mxfp4_bank* routed,
+                              const moe_mxfp4_bank* shared, int T, int k, float* out,
+                              int32_t* topk_ids_out, float* topk_w_out, hipStream_t stream) {
+  void* ws = nullptr;
+  const int st = noalloc_scratch(&ws);
+  if (st != MOE_OK) {
+    begin_call();
+    return st;
+  }
+  return layer_forward(x_bf16, w_router_bf16, logit_bias, routed, shared, T, k, out, topk_ids_out,
+                       topk_w_out, ws, kNoallocScratchBytes, stream, false);
 }
 
 int moe_layer_forward_mxfp8_act(const void* x_bf16, const void* w_router_bf16,

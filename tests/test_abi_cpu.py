@@ -22,7 +22,8 @@ def test_library_exports_every_header_function():
                           "moe_quantize_mxfp8", "moe_layer_forward_mxfp8_act",
                           "moe_expert_ffn_fp8", "moe_layer_forward_fp8_shared",
                           "moe_expert_ffn_nvfp4", "moe_layer_forward_nvfp4",
-                          "moe_workspace_status", "moe_set_wait_test"}
+                          "moe_workspace_status", "moe_set_wait_test",
+                          "moe_layer_forward_noalloc"}
     lib = M.lib()
     for n in names:
         assert hasattr(lib, n), n
