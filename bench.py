@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline-loop", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="default decode run only: skip the 16k-token prefill sub-record")
     ap.add_argument("--verify-sweep", action="store_true",
                     help="instead of one workload: verification blocks of 2..8 correlated "
                          "tokens at the decode shape; per block size, time, the union of "
@@ -77,6 +79,45 @@ def parse():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def host_info():
+    """The host the CPU baseline runs on: CPU model, numpy's BLAS and the
+    cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name')} {b.get('version', '')}".strip()
+    except Exception:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        rt = [f"{i.get('internal_api')} ({i.get('num_threads')} threads)" for i in threadpool_info()
+              if i.get("user_api") == "blas"]
+        if rt:
+            blas = f"{blas}; runtime {', '.join(rt)}"
+    except Exception:
+        pass
+    return dict(cpu_model=model, blas=blas, affinity_cores=len(os.sched_getaffinity(0)))
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
 
 
 def main() -> int:
@@ -211,6 +252,16 @@ def main() -> int:
                                                           / cnt.sum()), 3))
         log(f"[bench] expert load: {load}")
 
+    # distinct routed experts of each token batch (the routing is the same
+    # for every bank copy)
+    U = []
+    for p in range(P):
+        M.moe_router_topk(x_pool[p], wrs[0], bias, w.k, ids, wts, None, ws)
+        U.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+    layer_roof = layer_roofline(w, U, W, K, P, ms_step, args)
+    log(f"[bench] layer roofline: {layer_roof}")
+
     # ---- roofline: the dominant kernel, timed with HIP events --------------
     # A second loop makes the same calls as the timed one with the library's
     # timing hook set: every kernel launch then carries a start and a stop
@@ -220,8 +271,8 @@ def main() -> int:
     # flops (MFMA-bound kernels) per launch.
     roof = None
     if not args.no_roofline_loop:
-        roof = kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bias,
-                               ids, wts, ws, P, C, W, K, stream, shared8=args.fp8_shared)
+        roof = kernel_roofline(args, w, M, lib, torch, np, step, U, P, W, K,
+                               shared8=args.fp8_shared)
     # ---- CPU baseline: the fp64 oracle on the host -------------------------
     cpu = None
     mx_err = None
@@ -253,11 +304,7 @@ def main() -> int:
         if args.nvfp4:
             from oracle import nvfp4 as NVO
             layer_fn = NVO.layer_nvfp4
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            cores = len(os.sched_getaffinity(0))
+        cores = cpu_threads()
         wr_np = S.gen_router(w, 0)
         n_tok, t_cpu, calls = 0, 0.0, 0
         Tcpu = w.T if w.T <= 16 else 1
@@ -271,7 +318,8 @@ def main() -> int:
         cpu = dict(value=round(n_tok / t_cpu, 3), unit="tokens/s", cores=int(cores),
                    kind="oracle",
                    sample=f"{calls} layer calls of {Tcpu} token(s) of this workload "
-                          f"({n_tok} tokens, {t_cpu:.1f} s, fp64 numpy on the host)")
+                          f"({n_tok} tokens, {t_cpu:.1f} s, fp64 numpy on the host)",
+                   **host_info())
         log(f"[bench] oracle: {cpu['value']} tokens/s on {cores} threads")
 
     line = {
@@ -298,8 +346,13 @@ def main() -> int:
                    "shared_expert_format": "fp8 e4m3, 32x32 ue8m0 blocks" if args.fp8_shared
                    else "nvfp4" if args.nvfp4 else "mxfp4"},
         "roofline": roof,
+        "layer_roofline": layer_roof,
         "cpu_baseline": cpu,
     }
+    if (w.name == "decode" and not (args.nvfp4 or args.fp8_shared or args.mxfp8_act)
+            and not args.no_prefill):
+        del x_pool, ws
+        line["prefill16k"] = prefill_record(args, M, S, np, torch, banks[0], routed_np, shared_np)
     if mx_err is not None:
         line["mxfp8_act_error"] = mx_err
     if load is not None:
@@ -307,6 +360,85 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     return 0
 
+
+
+def prefill_record(args, M, S, np, torch, bank, routed_np, shared_np):
+    """The prefill half of the metric beside the decode line: 16384 tokens of
+    the 16k-token workload (its seeded tokens and uniform bf16 router) through
+    the same layer, whose experts are the decode run's bank copy 0 (the same
+    shape and recipe; the expert values do not change the work). Layer time,
+    the event-timed grouped GEMMs against the 16-bit MFMA peak, the layer's
+    roofline, and the fp64 oracle on a bounded sample of tokens, which also
+    gives the GPU's error on those tokens."""
+    from oracle import moe as O
+    w = S.get("prefill16k")
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x_np = S.gen_tokens(w, 0)
+    wr_np = S.gen_router(w, 0)
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    wr = torch.from_numpy(wr_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    ws = M.workspace(w.T, w.H, w.I, w.E, w.k, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill16k: inputs resident in {time.time() - t0:.1f}s")
+
+    def call(i):
+        M.moe_layer_forward(x, wr, None, bank["routed"], bank["shared"], w.k, out, ids, wts, ws)
+
+    Wp, Kp = 2, 5
+    for i in range(Wp):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(Kp):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / Kp
+    U = int(torch.unique(ids).numel())
+    kern = sweep_kernel_times(M, torch, np, call, Kp)
+    gemms = {}
+    for name in ("gemm_gateup_kernel", "gemm_down_kernel"):
+        if name in kern:
+            fl = kernel_work(name, w, U)[1][0]
+            tf = fl / (kern[name] * 1e-6) / 1e12
+            gemms[name] = dict(us=kern[name], tflop=round(fl / 1e12, 3), tflops=round(tf, 1),
+                               mfma_frac=round(tf / MFMA_16BIT_PEAK_TFLOPS, 4))
+    layer = layer_roofline(w, [U], 0, 1, 1, ms, args)
+    rec = dict(workload="prefill16k", tokens=w.T, steps=Kp, warmup=Wp, ms_per_step=round(ms, 4),
+               tokens_per_s=round(w.T / (ms / 1e3), 1), active_experts=U,
+               bank="the decode run's bank copy 0 (same shape and recipe)",
+               layer_roofline=layer, gemm=gemms, kernels_us=kern)
+    log(f"[bench] prefill16k: {ms:.3f} ms/step, {rec['tokens_per_s']:,.0f} tokens/s; {gemms}")
+    if not args.no_cpu_baseline:
+        ids_np = ids.cpu().numpy()
+        got = out.cpu().numpy()
+        budget, t_cpu, toks, errs = 10.0, 0.0, [], []
+        rng = np.random.default_rng(7)
+        for t in rng.permutation(w.T):
+            if t_cpu >= budget or len(toks) >= 64:
+                break
+            ta = time.perf_counter()
+            r = O.layer(x_np[t:t + 1], wr_np, None, routed_np, shared_np, w.k)
+            t_cpu += time.perf_counter() - ta
+            toks.append(int(t))
+            if r["margin"][0] > 1e-4 and set(r["ids"][0].tolist()) == set(ids_np[t].tolist()):
+                errs.append((got[t], r["out"][0]))
+        rel = (float(np.linalg.norm(np.stack([a - b for a, b in errs]))
+                     / np.linalg.norm(np.stack([b for _, b in errs]))) if errs else None)
+        rec["cpu_baseline"] = dict(
+            value=round(len(toks) / t_cpu, 3), unit="tokens/s", cores=int(cpu_threads()),
+            kind="oracle",
+            sample=f"{len(toks)} single-token oracle calls on tokens drawn from the 16384 "
+                   f"({t_cpu:.1f} s, fp64 numpy on the host)", **host_info())
+        rec["rel_l2_vs_oracle_on_sample"] = None if rel is None else round(rel, 7)
+        log(f"[bench] prefill16k oracle: {rec['cpu_baseline']['value']} tokens/s; "
+            f"GPU rel-L2 on {len(errs)} sampled tokens {rel}")
+    return rec
 
 
 def sweep_kernel_times(M, torch, np, call, n):
@@ -526,8 +658,51 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
     return None, None
 
 
-def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bias, ids, wts,
-                    ws, P, C, W, K, stream, shared8=False):
+def expert_bytes(w, fmt):
+    """Weight bytes of one expert (gate, up and down) in a bank format."""
+    n = 3 * w.H * w.I
+    if fmt == "nvfp4":
+        return n // 2 + n // 16 + 12
+    if fmt == "fp8":
+        return n + 3 * (w.H // 32) * (w.I // 32)
+    return n // 2 + n // 32
+
+
+def layer_roofline(w, U, W, K, P, ms_step, args):
+    """The whole layer call against its roofline. Few tokens: HBM-bound,
+    on the selected experts' weight bytes (the union of the routed experts
+    the call touched, plus the shared expert) per call; this is the decode
+    model of bandwidth over routed expert bytes per token. Many tokens: the
+    layer's flops (router + routed and shared experts, 2 per multiply-add)
+    against the MFMA peak, with the HBM fraction of the touched experts'
+    weights beside it."""
+    import numpy as np
+    routed_fmt = "nvfp4" if args.nvfp4 else "mxfp4"
+    shared_fmt = "fp8" if args.fp8_shared else routed_fmt
+    u = float(np.mean([U[(W + i) % P] for i in range(K)]))
+    by = u * expert_bytes(w, routed_fmt) + expert_bytes(w, shared_fmt)
+    t = ms_step / 1e3
+    hbm = by / t / 1e9
+    if w.T <= 16:
+        return dict(bound="hbm", basis="selected experts' weight bytes (routed union + shared) "
+                    "per layer call / ms_per_step", experts=round(u + 1, 2), bytes=int(by),
+                    achieved=round(hbm, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(hbm / HBM_PEAK_GBS, 4))
+    fl = w.T * (2.0 * w.E * w.H + (w.k + 1) * 6.0 * w.H * w.I)
+    mpeak = MFMA_FP8_PEAK_TFLOPS if args.mxfp8_act else MFMA_16BIT_PEAK_TFLOPS
+    tf = fl / t / 1e12
+    bound = "mfma" if fl / (mpeak * 1e12) >= by / (HBM_PEAK_GBS * 1e9) else "hbm"
+    return dict(bound=bound, basis="layer flops (router + routed and shared experts) and the "
+                "touched experts' weight bytes per layer call / ms_per_step",
+                flops=fl, bytes=int(by),
+                achieved=round(tf, 1) if bound == "mfma" else round(hbm, 1),
+                peak=mpeak if bound == "mfma" else HBM_PEAK_GBS,
+                unit="TFLOP/s" if bound == "mfma" else "GB/s",
+                frac=round((tf / mpeak) if bound == "mfma" else (hbm / HBM_PEAK_GBS), 4),
+                mfma_frac=round(tf / mpeak, 4), hbm_frac=round(hbm / HBM_PEAK_GBS, 4))
+
+
+def kernel_roofline(args, w, M, lib, torch, np, step, U, P, W, K, shared8=False):
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch already loaded
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -541,13 +716,6 @@ def kernel_roofline(args, w, M, lib, torch, np, step, step_args, x_pool, wrs, bi
         if hip.hipEventCreate(ctypes.byref(e)) != 0:
             raise RuntimeError("hipEventCreate failed")
         return e.value
-
-    # distinct routed experts per token batch (same routing for every bank copy)
-    U = []
-    for p in range(P):
-        M.moe_router_topk(x_pool[p], wrs[0], bias, w.k, ids, wts, None, ws)
-        U.append(int(torch.unique(ids).numel()))
-    torch.cuda.synchronize()
 
     step(0)
     torch.cuda.synchronize()
