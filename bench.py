@@ -653,7 +653,7 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
                         + rows * H * 4)
     if name == "quant_mxfp8_kernel":
         return "hbm", T * H * 2 + T * H * 33 // 32
-    if name == "router_mfma_kernel":
+    if name in ("router_mfma_kernel", "router_mfma_lds_kernel"):
         return "mfma", T * 2.0 * w.E * H
     return None, None
 

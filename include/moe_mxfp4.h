@@ -251,6 +251,13 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E,
  *                  or written out of bounds (the affected rows are garbage)
  *   R              number of rows (== expert_offsets[E])
  *   y_rows         [R][H] fp32 out
+ * Precision: up to 128 rows, h = silu(g) * u stays in fp32. Above that the
+ * rows run on the bf16 / fp16 matrix cores (grouped GEMM), which round h
+ * once to fp16 for the down product (about 2e-4 relative error): an |h| of
+ * 65520 or more becomes +-inf there, and every output of that row comes out
+ * NaN or inf, never finite and wrong. Such magnitudes are far outside the
+ * layer's activations (|h| stays below about 10^3 for bf16 N(0,1) tokens and
+ * the configs' scales).
  */
 int moe_expert_ffn_mxfp4(const void* x_bf16, const moe_mxfp4_bank* bank,
                          const int32_t* expert_offsets, const int32_t* row_token,
@@ -281,6 +288,9 @@ int moe_combine(const float* y_rows, const int32_t* inv_row, const float* topk_w
  *   shared         one-expert bank added with weight 1, or NULL
  *   out            [T][H] fp32
  *   topk_ids_out   [T][k] int32 or NULL; topk_w_out [T][k] fp32 or NULL
+ * Up to 16 tokens every step keeps fp32 (the persistent few-token kernels);
+ * more tokens run the grouped GEMM, with h in fp16 as described for
+ * moe_expert_ffn_mxfp4 (an out-of-range h gives non-finite rows).
  */
 int moe_layer_forward(const void* x_bf16, const void* w_router_bf16,
                       const float* logit_bias, const moe_mxfp4_bank* routed,

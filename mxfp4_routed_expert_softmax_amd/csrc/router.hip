@@ -196,7 +196,7 @@ void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bi
                           int T, int H, int E, float* logits, hipStream_t s) {
   if (T > kRouterGemvMaxT && H % kRtBK == 0 && (size_t)T * H * 2 < (1ull << 32) &&
       (size_t)E * H * 2 < (1ull << 32)) {
-    launch("router_mfma_kernel", router_mfma_lds_kernel, dim3((T + 127) / 128, (E + 127) / 128),
+    launch("router_mfma_lds_kernel", router_mfma_lds_kernel, dim3((T + 127) / 128, (E + 127) / 128),
            dim3(256), 0, s, x, wr, bias, T, H, E, logits);
     return;
   }

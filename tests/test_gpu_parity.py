@@ -263,6 +263,7 @@ def _layer_parity(w, x_bits, wr, bias, routed, shared, tokens=None):
     out, ids, wt = run_layer(x_bits, wr, bias, HP.bank_to_dev(routed),
                              None if shared is None else HP.bank_to_dev(shared), w.k)
     tok = ref["tokens"]
+    assert np.isfinite(out).all()          # every row, compared or not
     alt = HP.check_routing(ref, ids, wt, w.k)
     ref_out = HP.reference_rows(ref, routed, shared, tok, alt)
     err = HP.rel_l2(out[tok], ref_out)
@@ -626,3 +627,98 @@ def test_gemm_layer_all_tokens():
     assert err < HP.GEMM_TOL
     err = _layer_parity(w, x, wr, None, routed, None)
     assert err < HP.GEMM_TOL
+
+
+
+def test_gemm_h_beyond_fp16_range_gives_non_finite_rows_not_wrong_ones():
+    # The grouped GEMM carries h = silu(g) * u in fp16. A token scaled up by
+    # 2^8 drives |h| past the fp16 maximum: its rows must come out non-finite
+    # (never finite and wrong), while a token scaled by 2^3 (|h| still in
+    # range) and every other row stay within the GEMM tolerance.
+    w = GEMM_MID
+    x = S.gen_tokens(w, 4).copy()
+    big, mid = 17, 42
+    xf = O.bf16_to_f64(x)
+    xf[big] *= 2.0 ** 8
+    xf[mid] *= 2.0 ** 3
+    x = S.f64_to_bf16_bits(xf)              # exact: powers of two
+    bank = S.gen_bank(w, 4)
+    r = O.route(x, S.gen_router(w, 4), S.gen_zipf_bias(w, 4), w.k)
+    off, rt = r["offsets"], r["row_token"]
+    y = run_ffn(x, bank, off, rt, w.R)
+    ref = O.expert_rows(r["x"], bank, off, rt)
+    hmax = np.zeros(w.R)
+    for e in range(w.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size:
+            wg, wu, _ = O.expert_weights(bank, e)
+            X = r["x"][rt[rows]]
+            hmax[rows] = np.abs(O.silu(X @ wg.T) * (X @ wu.T)).max(axis=1)
+    over = hmax >= 65520.0                  # rounds to inf in fp16
+    assert over[rt == big].all() and not over[rt != big].any(), hmax[rt == big]
+    assert hmax[rt == mid].max() > 1000.0   # large, but inside the range
+    assert not np.isfinite(y[over]).any()
+    ok = ~over
+    assert np.isfinite(y[ok]).all()
+    assert HP.rel_l2(y[ok], ref[ok]) < HP.GEMM_TOL
+    assert _row_errors(y[ok], ref[ok]).max() < 4 * HP.GEMM_TOL
+
+
+# ---------------------------------------------------------------------------
+# Fallback kernels for shapes the tiled kernels do not take
+# ---------------------------------------------------------------------------
+
+def test_router_unstaged_mfma_kernel_for_hidden_not_multiple_of_64():
+    # T > 16 takes the MFMA router; with H % 64 != 0 its unstaged form
+    w = S.Workload("rt_h96", 106, T=40, H=96, E=48, k=4, I=64, exp_lo=-6, exp_hi=-3,
+                   router_std=0.2)
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    ref = O.route(x, wr, None, w.k)
+    lg, ids, wt = run_router(w, x, wr, None)
+    assert _launches()[0] == "router_mfma_kernel"
+    assert np.abs(lg - ref["logits"]).max() / np.abs(ref["logits"]).max() < 1e-5
+    HP.check_routing(ref, ids, wt, w.k)
+
+
+def test_router_staged_mfma_kernel_is_named_apart():
+    w = S.get("prefill2k_zipf")
+    x, wr = S.gen_tokens(w, 0)[:64], S.gen_router(w, 0)
+    ref = O.route(x, wr, None, w.k)
+    lg, ids, wt = run_router(w, x, wr, None)
+    assert _launches()[0] == "router_mfma_lds_kernel"
+    HP.check_routing(ref, ids, wt, w.k)
+
+
+def test_layer_gemv_fallback_for_shapes_the_gemm_does_not_tile():
+    # 40 tokens with H % 256 != 0 and I % 128 != 0: the bucketed GEMVs (fp32 h)
+    # and the unstaged router
+    w = S.Workload("gemv_fb", 107, T=40, H=288, E=8, k=4, I=160, exp_lo=-6, exp_hi=-3)
+    d = S.gen_inputs(w, 0)
+    err = _layer_parity(w, d["x"], d["w_router"], None, d["routed"], d["shared"])
+    names = _launches()
+    assert "gateup_gemv_kernel" in names and "down_gemv_kernel" in names, names
+    assert "router_mfma_kernel" in names, names
+    assert err < HP.FP32_TOL
+
+
+def test_layer_one_token_chain_for_hidden_not_multiple_of_128():
+    # one token with H % 128 != 0: the three-launch chain instead of the fused
+    # launches
+    w = S.Workload("one_h96", 108, T=1, H=96, E=16, k=2, I=64, exp_lo=-6, exp_hi=-3)
+    d = S.gen_inputs(w, 0)
+    err = _layer_parity(w, d["x"], d["w_router"], None, d["routed"], d["shared"])
+    assert _launches() == ["route_kernel", "gateup_kernel", "down_kernel"]
+    assert err < HP.FP32_TOL
+
+
+def test_ffn_few_rows_real_decode_shape_through_its_table_kernel():
+    # moe_expert_ffn_mxfp4 with the six rows of one decode token at the real
+    # shape: the few-row path (its slot-table kernel, then gate/up and down)
+    w = S.get("decode")
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    r = O.route(x, wr, None, w.k)
+    bank = S.gen_bank(w, 0, experts=sorted(set(r["ids"][0].tolist())))
+    y = run_ffn(x, bank, r["offsets"], r["row_token"], w.k)
+    assert _launches() == ["ffn_table_kernel", "gateup_kernel", "down_kernel"]
+    ref = O.expert_rows(r["x"], bank, r["offsets"], r["row_token"])
+    assert HP.rel_l2(y, ref) < HP.FP32_TOL
