@@ -55,7 +55,8 @@ def _run_ffn(x_bits, bank, offsets, row_token, R):
     rt = None if row_token is None else HP.to_dev(row_token.astype(np.int32))
     M.moe_expert_ffn_mxfp4(HP.to_dev(x_bits), bd, off, rt, R, y, ws)
     torch.cuda.synchronize()
-    assert "gemm_gateup_kernel" in _launches() and "gemm_down_kernel" in _launches()
+    names = _launches()
+    assert "gemm_gateup_kernel" in names and "gemm_down_kernel" in names, names
     return y.cpu().numpy().astype(np.float64)
 
 
