@@ -561,9 +561,9 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
     if name == "gateup_fused_kernel" and shared8:
         # one token with the FP8 shared expert streamed in the same launch:
         # the MXFP4 routed work plus the FP8 expert (1 byte per weight, 1 per
-        # 32 x 32 block), its h row written and read back and its y row
+        # 32 x 32 block), its h and y rows written and read back
         _, b = kernel_work(name, w, U, False)
-        return "hbm", b + 3 * H * I + 3 * (H // 32) * (I // 32) + T * I * 8 + T * H * 4
+        return "hbm", b + 3 * H * I + 3 * (H // 32) * (I // 32) + T * I * 8 + T * H * 8
     if name == "fp8_gateup_gemv_kernel":
         # the FP8 shared expert's gate/up: 1 byte per weight, 1 per 32 x 32 block
         return "hbm", 2 * I * H + 2 * (I // 32) * (H // 32) + T * H * 2 + T * I * 4
@@ -583,18 +583,13 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
     if name == "down_gemv_kernel":
         return "hbm", (U + (1 if shared else 0)) * dn_expert + (R + (T if shared else 0)) * (I * 4 + H * 4)
     if name == "gateup_fused_kernel":
-        # one token: router rows, routing, shared + routed gate/up, and the
-        # shared expert's down rows (its h read back, its y row written)
-        b = w.E * H * 2 + T * H * 2 + T * w.E * 4 + (U + (1 if shared else 0)) * gu_expert \
-            + (R + (T if shared else 0)) * I * 4
-        if shared:
-            b += dn_expert + T * I * 4 + T * H * 4
-        return "hbm", b
-    if name == "down_stream_kernel":
-        # one token: the routed experts' down rows, then the combine (which
-        # reads the shared expert's y row)
-        return "hbm", U * dn_expert + R * I * 4 + R * H * 4 + (T * H * 4 if shared else 0) \
-            + T * H * 4 + T * w.k * 8
+        # the whole one-token layer: router rows, routing, gate/up and down of
+        # the routed experts and the shared one, each h row and y row written
+        # and read back once, the output row and the k ids and weights
+        rows = R + (T if shared else 0)
+        return "hbm", w.E * H * 2 + T * H * 2 + T * w.E * 4 \
+            + (U + (1 if shared else 0)) * (gu_expert + dn_expert) \
+            + rows * (I * 8 + H * 8) + T * H * 4 + T * w.k * 8
     if name == "route_block_kernel":
         # block of tokens: router rows, the routing, the shared expert's
         # gate/up for every token of the block

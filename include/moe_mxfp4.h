@@ -165,9 +165,14 @@ int moe_set_kernel_events(hipEvent_t* events, int n);
  * kernels whose workgroups hand data to one another inside a launch and wait
  * for it with a bounded number of polls. If one of those waits gives up
  * (which a correct run never does), the call still finishes with every
- * access in bounds, and its last launch writes NaN to every element of
- * `out`, -1 to `topk_ids_out` and NaN to `topk_w_out`, so the failure shows
- * in the outputs themselves. This call reads the result recorded in the
+ * access in bounds, and the failure shows in the outputs themselves:
+ *   - one token (a single launch): every output column group whose inputs
+ *     passed through that wait is NaN (all of `out` if the routing's wait
+ *     gave up), and if the routing's wait gave up, `topk_ids_out` is -1 and
+ *     `topk_w_out` NaN;
+ *   - 2..16 tokens: the call's last launch writes NaN to every element of
+ *     `out`, -1 to `topk_ids_out` and NaN to `topk_w_out`.
+ * This call reads the result recorded in the
  * first 16 bytes of `ws` with a blocking device-to-host copy: synchronise
  * the call's stream first, and pass the same workspace before reusing it.
  * Returns MOE_OK (every wait completed, or the last call made with `ws` had

@@ -67,6 +67,9 @@ constexpr int kDnRows = 32;     // down: 8 lanes per row, 8 rows per wave
 constexpr int kDnU = 9;         // down chunks per lane per batch (K = 2304 in one)
 constexpr int kReplicas = 16;        // copies of the one-token routing table
 constexpr int kReplicaWords = 512;   // 4 KB apart, so readers spread over channels
+// Words of a replica: [0, k) the chosen ids, [kRepWeights, + 2k) the
+// routing weights' low and high halves.
+constexpr int kRepWeights = 64;
 constexpr int kRouterV = 16;    // router: 16-byte vectors per lane (H <= 8192)
 constexpr long kSpinLimit = 1L << 20;  // polls (with s_sleep) before giving up
 // A tagged word: the call's 48-bit tag above a 16-bit payload. A reader
@@ -79,8 +82,11 @@ constexpr uint32_t kWaitRouterFlags = 1;  // chain routing: router flags
 constexpr uint32_t kWaitLogits = 2;       // routing: tagged logits
 constexpr uint32_t kWaitTable = 3;        // one-token gate/up: routing table copy
 constexpr uint32_t kWaitShared = 4;       // one-token shared down: shared gate/up flags
-// Result word of a few-token call: this magic above the wait code (0 = OK).
-constexpr uint32_t kResultMagic = 0x57414954u;
+constexpr uint32_t kWaitGateup = 5;       // one-token routed down: the slot's gate/up items
+// Result word of a few-token call: this magic above the call's 48-bit tag.
+// The call's status is the code of the status word when that word carries
+// the same tag, else OK.
+constexpr uint64_t kResultMagic = 0x5741u;
 
 constexpr int kLdsGu = kMT * kGuLanes * kGuU * 64;  // bf16 x chunks
 constexpr int kLdsDn = kMT * 8 * kDnU * 128;        // fp32 h chunks
@@ -186,8 +192,10 @@ struct DecodeArgs {
   long wait_limit;     // polls before the routing's first wait gives up
                        // (every other wait: kSpinLimit)
   uint64_t* wstat;     // [0] status word: tag << 16 | the code of a wait that
-                       // gave up; [1] result word (kResultMagic << 32 | code)
-  int32_t* cnt_dn;     // [dn_items] routed down items finished per column
+                       // gave up; [1] result word (kResultMagic << 48 | tag)
+  int32_t* cnt_dn;     // [dn_items] down items finished per output column group
+  uint64_t* hw;        // one token: [rows][I] routed h values as value words
+  uint64_t* yw;        // one token: [rows][H] y values as value words
   int max_slots;       // routed slots
   int rows;            // rows of h and y (routed rows, then T shared rows)
   int nb_router, gu_items, dn_items;
@@ -218,12 +226,31 @@ __device__ __forceinline__ uint64_t tag_word(uint64_t tag, uint32_t payload) {
 }
 
 // A bounded wait gave up: record it for the call's last launch.
+// The store completes before the wave goes on, so any signal the wave gives
+// afterwards (a flag, a count, a tagged word) is seen after it.
 __device__ __forceinline__ void report_timeout(const DecodeArgs& a, uint32_t code) {
   cst(a.wstat, tag_word(a.tag, code));
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
-// In the call's last launch (every wait of the call ran in earlier
-// launches): the code of a wait that gave up during this call, or 0.
+// A value word of the one-token launch: the low 32 bits of the call's tag
+// above an fp32 value. Like a tagged word, it shows by itself whether it
+// holds this call's value (foreign bytes pass with a chance of 2^-32 per
+// word), so its reader needs no flag and its writer no wait.
+__device__ __forceinline__ uint64_t value_word(const DecodeArgs& a, float v) {
+  return (a.tag << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ bool is_mine(const DecodeArgs& a, uint64_t w) {
+  return (uint32_t)(w >> 32) == (uint32_t)a.tag;
+}
+
+__device__ __forceinline__ uint64_t result_word(const DecodeArgs& a) {
+  return (kResultMagic << 48) | (a.tag & 0xffffffffffffull);
+}
+
+// The code of a wait of this call that gave up, or 0. Read where every wait
+// the reader's results depend on has been passed (in a later launch, or
+// after a count that those waits precede).
 __device__ __forceinline__ uint32_t call_wait_code(const DecodeArgs& a) {
   const uint64_t v = cld(a.wstat);
   return (v >> kTagShift) == a.tag ? (uint32_t)(v & 0xffffu) : 0u;
@@ -243,7 +270,7 @@ __device__ void finish_call(const DecodeArgs& a, uint32_t code, int b, int nb) {
         if (a.w_out) a.w_out[i] = __builtin_nanf("");
       }
   }
-  if (b == 0 && threadIdx.x == 0) a.wstat[1] = ((uint64_t)kResultMagic << 32) | code;
+  if (b == 0 && threadIdx.x == 0) a.wstat[1] = result_word(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -397,7 +424,7 @@ __device__ void topk_rows_f64(const float (&lv)[NR][NK], int E, int k, int* cons
 }
 
 template <int NK, int HALVES>
-__device__ void poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, uint32_t code,
+__device__ bool poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, uint32_t code,
                             const uint64_t* src, int n, uint32_t* out);
 
 // One token's logits, lane l holding experts l, l + 64, ...: polled as
@@ -770,11 +797,12 @@ __device__ void combine_column(const DecodeArgs& a, int c, bool failed) {
 // and K = I <= 2304 for down, one batch per row; larger shapes take the
 // one-shot kernels.)
 // ---------------------------------------------------------------------------
-constexpr int kStreamBlocks = 768;  // persistent workgroups per streaming kernel
 // The one-token gate/up stream gives each workgroup the same number of items,
 // two (one pass of its two-buffer loop) wherever at most this many
 // workgroups then cover the routed items.
 constexpr int kGuStreamMax = 896;
+// Down items (32-row groups) per workgroup of the one-token launch (1 or 2).
+constexpr int kDnPerWg = 2;
 
 // sg / su: the words holding the lane's scale bytes (byte lane % 4 of each).
 struct GuRegs {
@@ -842,7 +870,7 @@ __device__ __forceinline__ void gu_compute(const DecodeArgs& a, const int* tab, 
     }
   }
   const float g = group_sum<kGuLanes>(ag), u = group_sum<kGuLanes>(au);
-  if (j == 0 && n < a.I) a.h[(size_t)row * a.I + n] = silu_mul(g, u);
+  if (j == 0 && n < a.I) cst(a.hw + (size_t)row * a.I + n, value_word(a, silu_mul(g, u)));
 }
 
 // Router rows for one token with x staged in LDS: a wave per expert row,
@@ -878,9 +906,10 @@ __device__ void router_rows_one(const DecodeArgs& a, int b, uint4* s_x) {
 // word carries the tag `expect`; each value is HALVES tagged words, its
 // 16-bit pieces at src + h n (h = 0 the low piece). Returns the values
 // through `out` (NK per lane). Bounded: a timeout records `code` in the
-// status word and returns what was read, which every consumer clamps.
+// status word and returns false with what was read, which every consumer
+// clamps.
 template <int NK, int HALVES>
-__device__ void poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, uint32_t code,
+__device__ bool poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, uint32_t code,
                             const uint64_t* src, int n, uint32_t* out) {
   const int lane = lane_id();
   for (long it = 0;; ++it) {
@@ -897,25 +926,32 @@ __device__ void poll_tagged(const DecodeArgs& a, uint64_t expect, long limit, ui
       }
       out[i] = val;
     }
-    if (__all(ok)) return;
+    if (__all(ok)) return true;
     if (it >= limit) {
       if (lane == 0) report_timeout(a, code);
-      return;
+      return false;
     }
     __builtin_amdgcn_s_sleep(1);
   }
 }
 
+// Replica r of the one-token routing words.
+__device__ __forceinline__ uint64_t* replica(const DecodeArgs& a, int r) {
+  return a.tagged + 2 * a.E + (size_t)r * kReplicaWords;
+}
+
 // The one-token routing workgroup (wave 0): waits for the tagged logits,
-// takes the top-k (descending logit, ties to the lower id) with weights
-// renormalised over the k, writes the layer outputs and the table the down
-// launch reads, and publishes the chosen ids as tagged words in kReplicas
-// copies for the gate/up workgroups of this launch.
+// takes the top-k (descending logit, ties to the lower id) and publishes
+// the chosen ids as tagged words in kReplicas copies, then the weights
+// renormalised over the k as tagged words, for the workgroups of this
+// launch; writes the ids and weights out (-1 and NaN if its wait gave up)
+// and the call's result word.
 template <int NK>
 __device__ void route_token_tagged(const DecodeArgs& a) {
-  const int lane = lane_id(), k = a.k, ms = a.max_slots;
+  const int lane = lane_id(), k = a.k;
   uint32_t raw[NK];
-  poll_tagged<NK, 2>(a, a.wait_tag, a.wait_limit, kWaitLogits, a.tagged, a.E, raw);
+  if (lane == 0) a.wstat[1] = result_word(a);
+  const bool ok = poll_tagged<NK, 2>(a, a.wait_tag, a.wait_limit, kWaitLogits, a.tagged, a.E, raw);
   // k rounds of: each lane's best remaining key, the wave's best of those
   // (fp64 max on the keys' bits), and that key taken out
   double key[NK];
@@ -945,57 +981,58 @@ __device__ void route_token_tagged(const DecodeArgs& a) {
     if (j == 0) top = val;
   }
   // the gate/up workgroups wait on the ids alone: publish them before the
-  // weights and the down launch's table are worked out
-  if (lane < k) {
-    uint64_t* rep0 = a.tagged + 2 * a.E;
-    for (int r = 0; r < kReplicas; ++r)
-      cst(rep0 + (size_t)r * kReplicaWords + lane, tag_word(a.tag, (uint32_t)my_id));
-  }
-  // weights and slots from the k chosen lanes, read lane by lane (cheaper
-  // than shuffles through LDS); the sum runs over j = 0..k-1 in order
+  // weights are worked out
+  if (lane < k)
+    for (int r = 0; r < kReplicas; ++r) cst(replica(a, r) + lane, tag_word(a.tag, (uint32_t)my_id));
+  // weights from the k chosen lanes, read lane by lane (cheaper than
+  // shuffles through LDS); the sum runs over j = 0..k-1 in order
   const float z = lane < k ? expf(my_val - top) : 0.0f;
   float zsum = 0.0f;
-  int slot = 0;
-  for (int q = 0; q < k; ++q) {
+  for (int q = 0; q < k; ++q)
     zsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), q));
-    slot += __builtin_amdgcn_readlane(my_id, q) < my_id;
-  }
   const float wj = z / zsum;
   if (lane < k) {
-    a.tab[1 + slot] = my_id;
-    a.tab[1 + ms + slot] = slot;
-    a.tab[1 + 2 * ms + slot] = 1;
-    a.row_token[slot] = 0;
-    a.inv_row[lane] = slot;
-    a.route_w[lane] = wj;
-    if (a.ids_out) a.ids_out[lane] = my_id;
-    if (a.w_out) a.w_out[lane] = wj;
+    const uint32_t wb = __float_as_uint(wj);
+    for (int r = 0; r < kReplicas; ++r) {
+      uint64_t* ww = replica(a, r) + kRepWeights;
+      cst(ww + lane, tag_word(a.tag, wb));
+      cst(ww + k + lane, tag_word(a.tag, wb >> 16));
+    }
+    if (a.ids_out) a.ids_out[lane] = ok ? my_id : -1;
+    if (a.w_out) a.w_out[lane] = ok ? wj : __builtin_nanf("");
   }
-  if (lane == 0) a.tab[0] = k;
-  for (int i = lane; i < a.dn_items; i += kWave) a.cnt_dn[i] = 0;
 }
 
-// A gate/up workgroup's copy of the routing: polls replica `r` and builds
-// the slot table in LDS (slot = rank of the expert id among the k, so slots
-// ascend by expert id; one row per slot, row = slot).
-__device__ void load_routing_tagged(const DecodeArgs& a, int r, int* s_tab) {
-  const int k = a.k, ms = a.max_slots;
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    uint32_t v[1];
-    poll_tagged<1, 1>(a, a.tag, kSpinLimit, kWaitTable,
-                      a.tagged + 2 * a.E + (size_t)r * kReplicaWords, k, v);
-    const int my_id = lane < k ? min(max((int)v[0], 0), a.E - 1) : 0x7fffffff;
-    int slot = 0;
-    for (int q = 0; q < k; ++q) slot += __builtin_amdgcn_readlane(my_id, q) < my_id;
-    if (lane < k) {
-      s_tab[1 + slot] = my_id;
-      s_tab[1 + ms + slot] = slot;
-      s_tab[1 + 2 * ms + slot] = 1;
-    }
-    if (lane == 0) s_tab[0] = k;
+// A workgroup's copy of the routing, taken by one wave: polls replica `r`
+// and builds the slot table in LDS (slot = rank of the expert id among the
+// k, so slots ascend by expert id; one row per slot, row = slot), and
+// (s_inv not null) the slot of each choice j.
+__device__ void routing_copy(const DecodeArgs& a, int r, int* s_tab, int* s_inv) {
+  const int k = a.k, ms = a.max_slots, lane = lane_id();
+  uint32_t v[1];
+  poll_tagged<1, 1>(a, a.tag, kSpinLimit, kWaitTable, replica(a, r), k, v);
+  const int my_id = lane < k ? min(max((int)v[0], 0), a.E - 1) : 0x7fffffff;
+  int slot = 0;
+  for (int q = 0; q < k; ++q) slot += __builtin_amdgcn_readlane(my_id, q) < my_id;
+  if (lane < k) {
+    s_tab[1 + slot] = my_id;
+    s_tab[1 + ms + slot] = slot;
+    s_tab[1 + 2 * ms + slot] = 1;
+    if (s_inv) s_inv[lane] = slot;
   }
+  if (lane == 0) s_tab[0] = k;
+}
+
+__device__ void load_routing_tagged(const DecodeArgs& a, int r, int* s_tab) {
+  if (threadIdx.x < kWave) routing_copy(a, r, s_tab, nullptr);
   __syncthreads();
+}
+
+// The k routing weights (one wave), from replica r's tagged words.
+__device__ void routing_weights(const DecodeArgs& a, int r, float* s_w) {
+  uint32_t v[1];
+  poll_tagged<1, 2>(a, a.tag, kSpinLimit, kWaitTable, replica(a, r) + kRepWeights, a.k, v);
+  if (lane_id() < a.k) s_w[lane_id()] = __uint_as_float(v[0]);
 }
 
 // sc: the words holding the lane's scale bytes (byte (lane % 8) % 4 of each).
@@ -1104,7 +1141,7 @@ __device__ __forceinline__ void dn_compute(const DecodeArgs& a, const int* tab, 
     }
   }
   const float v = group_sum<8>(acc);
-  if (j == 0 && n < a.H) cst(a.y + (size_t)row * a.H + n, v);
+  if (j == 0 && n < a.H) cst(a.yw + (size_t)row * a.H + n, value_word(a, v));
 }
 
 // ---------------------------------------------------------------------------
@@ -1150,7 +1187,8 @@ __device__ __forceinline__ void gu_issue_nv(const DecodeArgs& a, const uint8_t* 
   }
 }
 
-template <bool kCoherent>
+// kWord: h as value words (routed); otherwise coherent fp32 (shared)
+template <bool kWord>
 __device__ __forceinline__ void gu_compute_nv(const DecodeArgs& a, int rb, int row, float mg,
                                               float mu, const GuRegs& r, const uint4* s_x) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -1181,11 +1219,10 @@ __device__ __forceinline__ void gu_compute_nv(const DecodeArgs& a, int rb, int r
   }
   const float g = group_sum<kGuLanes>(ag) * mg, u = group_sum<kGuLanes>(au) * mu;
   if (j == 0 && n < a.I) {
-    float* p = a.h + (size_t)row * a.I + n;
-    if (kCoherent)
-      cst(p, silu_mul(g, u));
+    if (kWord)
+      cst(a.hw + (size_t)row * a.I + n, value_word(a, silu_mul(g, u)));
     else
-      *p = silu_mul(g, u);
+      cst(a.h + (size_t)row * a.I + n, silu_mul(g, u));
   }
 }
 
@@ -1202,8 +1239,8 @@ __device__ __forceinline__ void gu_compute_nv_routed(const DecodeArgs& a, const 
   const int s = it / a.gu_items, rb = it - s * a.gu_items;
   const int e = min(max(tab[1 + s], 0), a.routed.E - 1);
   const int row = min(max(tab[1 + a.max_slots + s], 0), a.rows - 1);
-  gu_compute_nv<false>(a, rb, row, nv_matrix_scale(a.routed, e, 0), nv_matrix_scale(a.routed, e, 1),
-                       r, s_x);
+  gu_compute_nv<true>(a, rb, row, nv_matrix_scale(a.routed, e, 0), nv_matrix_scale(a.routed, e, 1),
+                      r, s_x);
 }
 
 // down: item it of the routed slots (it < nr) or of the shared expert
@@ -1282,61 +1319,110 @@ __device__ __forceinline__ void dn_compute_nv(const DecodeArgs& a, const int* ta
     }
   }
   const float v = group_sum<8>(acc) * d.md;
-  if (j == 0 && n < a.H) cst(a.y + (size_t)d.row * a.H + n, v);
+  if (j == 0 && n < a.H) cst(a.yw + (size_t)d.row * a.H + n, value_word(a, v));
 }
 
-// Combine of output columns [32c, 32c + 32) of the one token: the shared
-// row, then the k routed rows in order j = 0..k-1, one fp32 fma each. Rows
-// and weights come from LDS; the y rows were written by other workgroups of
-// this launch (coherent loads, all issued together).
-__device__ void combine_column_one(const DecodeArgs& a, int c, const int* s_inv,
-                                   const float* s_w, bool failed) {
-  const int n = c * kDnRows + (int)threadIdx.x;
-  if (threadIdx.x >= kDnRows || n >= a.H) return;
-  float v = a.y_shared_ext ? a.y_shared_ext[n]
-            : a.has_shared ? cld(a.y + (size_t)a.R * a.H + n) : 0.0f;
+// The slot's h row from its value words (all threads): reads until every
+// word carries the call's tag. Bounded like poll_tagged.
+__device__ void poll_h_words(const DecodeArgs& a, int row, DnRegs& r) {
+  const int nv = a.I >> 2;
+  const uint64_t* src = a.hw + (size_t)row * a.I;
+  for (long it = 0;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = min((int)threadIdx.x + i * kThreads, nv - 1);
+      uint64_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = cld(src + 4 * f + q);
+        ok &= is_mine(a, w[q]);
+      }
+      r.h[i] = f32x4_t{__uint_as_float((uint32_t)w[0]), __uint_as_float((uint32_t)w[1]),
+                       __uint_as_float((uint32_t)w[2]), __uint_as_float((uint32_t)w[3])};
+    }
+    if (__syncthreads_and(ok)) return;
+    if (it >= kSpinLimit) {
+      if (threadIdx.x == 0) report_timeout(a, kWaitGateup);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Output column groups c0 and (live1) c0 + 1 of the one token, by wave 0
+// (lanes 0..31 and 32..63), each if all its parts have their y words: the
+// shared row, then the k routed rows in order j, one fp32 fma each. Called
+// by each part's writer once its own words have landed, so the writer
+// whose words land last finds them all (another may too, and writes the
+// same values). failed: a wait of the call gave up; the group is NaN.
+__device__ void try_combine(const DecodeArgs& a, int c0, bool live1, const int* s_inv,
+                            const float* s_w, bool failed) {
+  const int lane = lane_id();
+  const int n = (lane < 32 ? c0 : c0 + 1) * kDnRows + (lane & 31);
+  const bool valid = (lane < 32 || live1) && n < a.H;
+  const int nn = valid ? n : 0;
+  bool ok = true;
+  float v = 0.0f;
+  if (a.y_shared_ext) {
+    v = a.y_shared_ext[nn];
+  } else if (a.has_shared) {
+    const uint64_t w = cld(a.yw + (size_t)a.R * a.H + nn);
+    ok &= is_mine(a, w);
+    v = __uint_as_float((uint32_t)w);
+  }
   for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
-    float y[8];
+    uint64_t y[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int r = min(max(s_inv[min(j0 + u, a.k - 1)], 0), a.R - 1);
-      y[u] = cld(a.y + (size_t)r * a.H + n);
+      y[u] = cld(a.yw + (size_t)r * a.H + nn);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (j0 + u < a.k) v = fmaf(s_w[j0 + u], y[u], v);
+      if (j0 + u < a.k) {
+        ok &= is_mine(a, y[u]);
+        v = fmaf(s_w[j0 + u], __uint_as_float((uint32_t)y[u]), v);
+      }
   }
-  a.out[n] = failed ? __builtin_nanf("") : v;
+  const uint64_t bad = __ballot(valid && !ok);
+  const bool done = lane < 32 ? (uint32_t)bad == 0u : (uint32_t)(bad >> 32) == 0u;
+  if (valid && done) a.out[n] = failed ? __builtin_nanf("") : v;
 }
 
-// Decode gate/up, one launch: [router rows | the routing workgroup |
-// shared expert gate/up items | G routed workgroups]. The routed workgroups
-// stage the token, poll a replica of the routing table and then stream the
-// items b, b + G, b + 2G, ... of the selected experts (items slot-major, 8
-// rows each) with two register buffers, so the weights of the next item are
-// in flight while the current one is computed.
 // Completion flags of the shared expert's gate/up items in the one-token
 // launch: one tagged word per item, after the routing copies.
 __device__ __forceinline__ uint64_t* shared_flags(const DecodeArgs& a) {
   return a.tagged + 2 * a.E + (size_t)kReplicas * kReplicaWords;
 }
 
-// The shared expert's down item c (32 output rows) inside the one-token
-// gate/up launch. These workgroups come last in the grid, so they start as
-// the routed gate/up workers leave and use the bandwidth of that tail: by
-// then the shared gate/up items are long done (their flags are checked
-// all the same) and the shared h row is read coherently with the weights.
-// The next launch is left with only the routed experts' down rows.
-__device__ void shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
-  if (threadIdx.x < kWave) {
+// LDS of a down workgroup of the one-token launch: the slot table, the slot
+// and weight of each choice j (for the combine), then the staged h row.
+struct DownLds {
+  int* tab;
+  int* inv;
+  float* w;
+  f32x4_t* h;
+  __device__ DownLds(const DecodeArgs& a, char* lds)
+      : tab(reinterpret_cast<int*>(lds)),
+        inv(tab + 1 + 3 * a.max_slots),
+        w(reinterpret_cast<float*>(inv + a.k)),
+        h(reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int))) {}
+};
+
+// The waits of a shared down workgroup, a wave each: the routing copy and
+// the routing weights (for the combine) and the shared gate/up flags.
+__device__ void shared_down_waits(const DecodeArgs& a, int n_sh, const DownLds& L) {
+  const int wave = threadIdx.x >> 6;
+  if (wave == 0) {
     uint32_t v[6];
     poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
+  } else if (wave == 1) {
+    routing_copy(a, blockIdx.x % kReplicas, L.tab, L.inv);
+  } else if (wave == 2) {
+    routing_weights(a, blockIdx.x % kReplicas, L.w);
   }
   __syncthreads();
-  DnRegs A;
-  dn_issue(a, nullptr, 0, c, A, true, false);
-  dn_issue_h<true>(a, min(a.R, a.rows - 1), A);
-  dn_compute(a, nullptr, 0, c, A, reinterpret_cast<f32x4_t*>(lds));
 }
 
 // ---------------------------------------------------------------------------
@@ -1407,7 +1493,7 @@ __device__ void fp8_shared_gu_item(const DecodeArgs& a, int item, uint4* s_x) {
 // Down item c: 32 output rows of the shared y row, 8 lanes per row. The
 // weights are requested before the wait for the gate/up flags; h is read
 // coherently once they are all up.
-__device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
+__device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, const DownLds& L) {
   const int H = a.H, I = a.I;
   const int q = threadIdx.x & 7;
   const int n = c * kDnRows + (threadIdx.x >> 3);
@@ -1424,12 +1510,8 @@ __device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, char*
     wd[u] = bload16(rd, nr * I + cc * 16);
     sd[u] = bload8(rs, (nr >> 5) * sb + (cc >> 1));
   }
-  if (threadIdx.x < kWave) {
-    uint32_t v[6];
-    poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
-  }
-  __syncthreads();
-  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds);
+  shared_down_waits(a, n_sh, L);
+  f32x4_t* s_h = L.h;
   const uint64_t* hrow = reinterpret_cast<const uint64_t*>(a.h + (size_t)a.R * I);
   for (int f = threadIdx.x; f < (I >> 2); f += kThreads) {
     const uint64_t lo = cld(hrow + 2 * f), hi = cld(hrow + 2 * f + 1);
@@ -1457,7 +1539,7 @@ __device__ void fp8_shared_down_item(const DecodeArgs& a, int c, int n_sh, char*
     }
   }
   acc = group_sum<8>(acc);
-  if (ok && q == 0) cst(a.y + (size_t)a.R * H + n, acc);
+  if (ok && q == 0) cst(a.yw + (size_t)a.R * H + n, value_word(a, acc));
 }
 
 // NVFP4 shared expert, one token: gate/up item (h write-through) and down
@@ -1469,26 +1551,98 @@ __device__ void nv_shared_gu_item(const DecodeArgs& a, int item, uint4* s_x) {
       a.H >> 3, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
       [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
   __syncthreads();
-  gu_compute_nv<true>(a, item, min(a.R, a.rows - 1), nv_matrix_scale(a.shared, 0, 0),
+  gu_compute_nv<false>(a, item, min(a.R, a.rows - 1), nv_matrix_scale(a.shared, 0, 0),
                       nv_matrix_scale(a.shared, 0, 1), r, s_x);
 }
 
-__device__ void nv_shared_down_item(const DecodeArgs& a, int c, int n_sh, char* lds) {
-  DnRegs A;
-  dn_issue_nv(a, nullptr, 0, c, A, true, false);
-  if (threadIdx.x < kWave) {
-    uint32_t v[6];
-    poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
+// Down items c0 and c0 + 1 (live1: the second exists) of one slot, or of
+// the shared expert (slot < 0), in one workgroup of the one-token launch:
+// both items' weights are in flight before the wait for the slot's h row
+// (its value words, or the shared gate/up flags and then the shared row),
+// which is read once. A routed pair takes the routing copy first (it names
+// the expert); a shared pair requests its weights at once.
+template <bool NV>
+__device__ void down_pair(const DecodeArgs& a, int slot, int c0, bool live1, int n_sh,
+                          const DownLds& L) {
+  const int r = blockIdx.x % kReplicas;
+  const int nr = a.max_slots * a.dn_items;
+  const int wave = threadIdx.x >> 6;
+  const int it = slot < 0 ? nr + c0 : slot * a.dn_items + c0;
+  DnRegs A, B;
+  auto issue = [&](int i, DnRegs& R, bool live) {
+    if constexpr (NV)
+      dn_issue_nv(a, L.tab, nr, i, R, live, false);
+    else
+      dn_issue(a, L.tab, nr, i, R, live, false);
+  };
+  if (slot < 0) {
+    issue(it, A, true);
+    issue(live1 ? it + 1 : it, B, live1);
+    if (wave == 0) {
+      uint32_t v[6];
+      poll_tagged<6, 1>(a, a.tag, kSpinLimit, kWaitShared, shared_flags(a), n_sh, v);
+    } else if (wave == 1) {
+      routing_copy(a, r, L.tab, L.inv);
+    } else if (wave == 2) {
+      routing_weights(a, r, L.w);
+    }
+    __syncthreads();
+  } else {
+    if (wave == 0)
+      routing_copy(a, r, L.tab, L.inv);
+    else if (wave == 1)
+      routing_weights(a, r, L.w);
+    __syncthreads();
+    issue(it, A, true);
+    issue(live1 ? it + 1 : it, B, live1);
   }
-  __syncthreads();
-  dn_issue_h<true>(a, min(a.R, a.rows - 1), A);
-  dn_compute_nv(a, nullptr, 0, c, A, reinterpret_cast<f32x4_t*>(lds));
+  if (slot < 0)
+    dn_issue_h<true>(a, min(a.R, a.rows - 1), A);
+  else
+    poll_h_words(a, min(max(L.tab[1 + a.max_slots + slot], 0), a.rows - 1), A);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) B.h[i] = A.h[i];
+  auto compute = [&](int i, const DnRegs& R) {
+    if constexpr (NV)
+      dn_compute_nv(a, L.tab, nr, i, R, L.h);
+    else
+      dn_compute(a, L.tab, nr, i, R, L.h);
+  };
+  compute(it, A);
+  if (live1) compute(it + 1, B);
 }
 
+// After a workgroup's down items (column groups c0, and c0 + 1 if live1):
+// once their y words have landed, combine whichever of the groups has all
+// its parts. Every wait whose data reach a group comes before that group's
+// last part is written, so its combine sees any of them that gave up in
+// the status word and writes NaN.
+__device__ void finish_parts(const DecodeArgs& a, int c0, bool live1, const DownLds& L) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < kWave) try_combine(a, c0, live1, L.inv, L.w, call_wait_code(a) != 0);
+}
+
+// The whole one-token layer in one launch, workgroups in dispatch order:
+// [router rows | the routing workgroup | shared gate/up items | G routed
+// gate/up workgroups | shared down items | routed down items].
+// * The routed gate/up workgroups stage the token, poll a replica of the
+//   routing table and then stream the items b, b + G, ... of the selected
+//   experts (slot-major, 8 rows each) with two register buffers, so the
+//   weights of the next item are in flight while the current one is
+//   computed. Each item counts itself for its slot once its h rows have
+//   landed.
+// * The down items (32 output rows each) come last, so they are dispatched
+//   as gate/up workgroups retire: each requests its weights at once and then
+//   waits for its h row (the slot's count, or the shared flags), and the
+//   last of a column group's items combines it.
+// A workgroup waits only on workgroups before it in dispatch order, which
+// were dispatched before it and never wait on it.
 // NV: NVFP4 banks (routed and shared); otherwise MXFP4 (shared possibly FP8).
 template <bool NV>
 __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
-                                                                int n_sd, int G) {
+                                                                int n_sd, int G, int per,
+                                                                int dpw) {
   extern __shared__ __align__(16) char lds[];
   const int b0 = blockIdx.x;
   if (b0 < a.nb_router) {
@@ -1519,12 +1673,21 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
     return;
   }
   if (b0 >= a.nb_router + 1 + n_shared + G) {
-    if constexpr (NV)
-      nv_shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
-    else if (a.shared_fp8)
-      fp8_shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
-    else
-      shared_down_item(a, b0 - (a.nb_router + 1 + n_shared + G), n_shared, lds);
+    // down workgroups: dpw (1 or 2) column groups each (one for the FP8
+    // shared expert), the shared expert's first, then slot by slot
+    const int d = b0 - (a.nb_router + 1 + n_shared + G);
+    const DownLds L(a, lds);
+    const int per_slot = (a.dn_items + dpw - 1) / dpw;
+    if (d < n_sd && !NV && a.shared_fp8) {
+      fp8_shared_down_item(a, d, n_shared, L);
+      finish_parts(a, d, false, L);
+      return;
+    }
+    const int slot = d < n_sd ? -1 : (d - n_sd) / per_slot;
+    const int c0 = dpw * (d < n_sd ? d : (d - n_sd) - slot * per_slot);
+    const bool live1 = dpw == 2 && c0 + 1 < a.dn_items;
+    down_pair<NV>(a, slot, c0, live1, n_shared, L);
+    finish_parts(a, c0, live1, L);
     return;
   }
   const int b = b0 - a.nb_router - 1 - n_shared;
@@ -1535,11 +1698,14 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
       [&](int idx, uint4 v) { s_x[(idx & 3) * (kGuLanes * kGuU) + (idx >> 2)] = v; });
   load_routing_tagged(a, b % kReplicas, tab);
   const int n = tab[0] * a.gu_items;
-  // Fixed trip over pairs of items with no early exit (an exit between the
-  // halves would let the compiler merge them and move the buffers to
-  // scratch). Issues past this workgroup's last item are padding: their
-  // weight loads read nothing (empty resources) and are not used.
-  const int mine = b < n ? (n - b + G - 1) / G : 0;
+  // Items first .. first + mine - 1, contiguous, so the slots complete in
+  // the order their workgroups are dispatched. Fixed trip over pairs of
+  // items with no early exit (an exit between the halves would let the
+  // compiler merge them and move the buffers to scratch). Issues past this
+  // workgroup's last item are padding: their weight loads read nothing
+  // (empty resources) and are not used.
+  const int first = b * per;
+  const int mine = max(0, min(per, n - first));
   GuRegs A, B;
   auto issue = [&](int it, GuRegs& r, bool live) {
     if constexpr (NV)
@@ -1553,77 +1719,15 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
     else
       gu_compute(a, tab, it, r, s_x);
   };
-  issue(b < n ? b : 0, A, b < n);
+  issue(mine > 0 ? first : 0, A, mine > 0);
   for (int kk = 0; kk < mine; kk += 2) {
-    const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
-    issue(i1 < n ? i1 : i0, B, i1 < n);
+    const int i0 = first + kk;
+    const bool l1 = kk + 1 < mine, l2 = kk + 2 < mine;
+    issue(l1 ? i0 + 1 : i0, B, l1);
     compute(i0, A);
-    issue(i2 < n ? i2 : i0, A, i2 < n);
-    if (i1 < n) compute(i1, B);
+    issue(l2 ? i0 + 2 : i0, A, l2);
+    if (l1) compute(i0 + 1, B);
   }
-}
-
-// One token, down projection: routed (slot, 32-row group) items, then the
-// shared expert's, streamed by persistent workgroups with two register
-// buffers. After its last item a workgroup drains its y stores and bumps
-// the counters of all the columns it wrote at once; the workgroup that
-// completes a column (every routed slot and the shared expert) combines it.
-template <bool NV>
-__global__ __launch_bounds__(kThreads) void down_stream_kernel(DecodeArgs a, int G) {
-  extern __shared__ __align__(16) char lds[];
-  __shared__ int s_last[32];
-  int* tab = reinterpret_cast<int*>(lds);
-  int* s_inv = tab + 1 + 3 * a.max_slots;
-  float* s_w = reinterpret_cast<float*>(s_inv + a.k);
-  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds + 1024 * sizeof(int));
-  for (int i = threadIdx.x; i < 1 + 3 * a.max_slots; i += kThreads) tab[i] = a.tab[i];
-  for (int i = threadIdx.x; i < a.k; i += kThreads) {
-    s_inv[i] = a.inv_row[i];
-    s_w[i] = a.route_w[i];
-  }
-  // every wait of the call ran in launch 1
-  const uint32_t code = call_wait_code(a);
-  finish_call(a, code, blockIdx.x, gridDim.x);
-  __syncthreads();
-  const int ns = min(max(tab[0], 0), a.max_slots);
-  const int nr = ns * a.dn_items;
-  const int n = nr;       // the shared expert's rows were done in the gate/up launch
-  const int parts = ns;   // routed contributions per column
-  const int b = blockIdx.x;
-  if (b >= n) return;
-  const int mine = (n - b + G - 1) / G;  // <= 32 (the grid is at least n / 32)
-  DnRegs A, B;
-  auto issue = [&](int it, DnRegs& r, bool live) {
-    if constexpr (NV)
-      dn_issue_nv(a, tab, nr, it, r, live);
-    else
-      dn_issue(a, tab, nr, it, r, live);
-  };
-  auto compute = [&](int it, const DnRegs& r) {
-    if constexpr (NV)
-      dn_compute_nv(a, tab, nr, it, r, s_h);
-    else
-      dn_compute(a, tab, nr, it, r, s_h);
-  };
-  issue(b, A, true);
-  for (int k = 0; k < mine; k += 2) {
-    const int i0 = b + k * G, i1 = i0 + G, i2 = i1 + G;
-    issue(i1 < n ? i1 : i0, B, i1 < n);
-    compute(i0, A);
-    issue(i2 < n ? i2 : i0, A, i2 < n);
-    if (i1 < n) compute(i1, B);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if ((int)threadIdx.x < min(mine, 32)) {
-    const int c = (b + (int)threadIdx.x * G) % a.dn_items;  // nr is a multiple of dn_items
-    s_last[threadIdx.x] =
-        __hip_atomic_fetch_add(a.cnt_dn + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        parts - 1;
-  }
-  __syncthreads();
-  for (int t = 0; t < min(mine, 32); ++t)
-    if (s_last[t]) combine_column_one(a, (b + t * G) % a.dn_items, s_inv, s_w, code != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -2203,7 +2307,7 @@ constexpr long kForcedSpinLimit = 256;
 struct DecodeLayout {
   int max_slots, rows, gu_items, dn_items, nb_router;
   size_t off_wstat, off_flags, off_cnt, off_tab, off_rt, off_inv, off_logits, off_w, off_h, off_y,
-      off_tagged, bytes;
+      off_tagged, off_hw, off_yw, bytes;
 };
 
 size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -2242,6 +2346,12 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   o += al(sizeof(float) * (size_t)L.rows * I);
   L.off_y = o;
   o += al(ffn ? 0 : sizeof(float) * (size_t)L.rows * H);
+  // one token: h and y as value words
+  const bool one = T == 1 && !ffn;
+  L.off_hw = o;
+  o += al(one ? sizeof(uint64_t) * (size_t)L.rows * I : 0);
+  L.off_yw = o;
+  o += al(one ? sizeof(uint64_t) * (size_t)L.rows * H : 0);
   L.bytes = o;
   return L;
 }
@@ -2256,8 +2366,9 @@ void set_force_wait_timeout(int on) { g_force_timeout = on; }
 int read_decode_status(const void* ws) {
   uint64_t v[2] = {0, 0};
   if (hipMemcpy(v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -1;
-  if ((uint32_t)(v[1] >> 32) != kResultMagic) return 0;  // no few-token call recorded
-  return (int)(uint32_t)v[1];
+  if ((v[1] >> 48) != kResultMagic) return 0;  // no few-token call recorded
+  const uint64_t tag = v[1] & 0xffffffffffffull;
+  return (v[0] >> kTagShift) == tag ? (int)(v[0] & 0xffffu) : 0;
 }
 
 template <int MT>
@@ -2308,8 +2419,7 @@ static bool stream_path(const DecodeLaunch& d, const DecodeLayout& L) {
   return d.T == 1 && !ffn && (d.H >> 5) <= kGuLanes * kGuU && d.H % 128 == 0 &&
          d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU && d.I <= 3 * 4 * kThreads &&
          d.H * 2 + 4 * (1 + 3 * L.max_slots) <= kLdsBytes &&
-         1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave && d.E <= 16 * kWave &&
-         (L.max_slots + 1) * L.dn_items <= 32 * kStreamBlocks;
+         1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave && d.E <= 16 * kWave;
 }
 
 bool decode_fuses_nvfp4(const DecodeLaunch& d) {
@@ -2357,6 +2467,8 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.flags = reinterpret_cast<uint64_t*>(w + L.off_flags);
   a.tagged = reinterpret_cast<uint64_t*>(w + L.off_tagged);
   a.cnt_dn = reinterpret_cast<int32_t*>(w + L.off_cnt);
+  a.hw = reinterpret_cast<uint64_t*>(w + L.off_hw);
+  a.yw = reinterpret_cast<uint64_t*>(w + L.off_yw);
   a.wstat = reinterpret_cast<uint64_t*>(w + L.off_wstat);
   a.tab = reinterpret_cast<int32_t*>(w + L.off_tab);
   a.row_token = reinterpret_cast<int32_t*>(w + L.off_rt);
@@ -2385,17 +2497,17 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   const bool stream = stream_path(d, L);
   if (stream) {
     const int n_sh = shared ? L.gu_items : 0;
-    const int n_sd = shared ? L.dn_items : 0;
+    int n_sd = shared ? L.dn_items : 0;
     const int per = max(2, (routed_gu + kGuStreamMax - 1) / kGuStreamMax);
     const int gg = (routed_gu + per - 1) / per;
     const bool nv = d.routed.codec == kCodecNvfp4;
+    // down workgroups: kDnPerWg 32-row groups each (FP8 shared expert: one)
+    const int per_slot = (L.dn_items + kDnPerWg - 1) / kDnPerWg;
+    const int nd = L.max_slots * per_slot;
+    if (shared && !d.shared_fp8) n_sd = per_slot;
     launch("gateup_fused_kernel", nv ? gateup_fused_kernel<true> : gateup_fused_kernel<false>,
-           dim3(L.nb_router + 1 + n_sh + gg + n_sd), dim3(kThreads), kLdsBytes, s, a, n_sh, n_sd,
-           gg);
-    const int nd = L.max_slots * L.dn_items;
-    const int gd = nd < kStreamBlocks ? nd : kStreamBlocks;
-    launch("down_stream_kernel", nv ? down_stream_kernel<true> : down_stream_kernel<false>,
-           dim3(gd), dim3(kThreads), kLdsBytes, s, a, gd);
+           dim3(L.nb_router + 1 + n_sh + gg + n_sd + nd), dim3(kThreads), kLdsBytes, s, a, n_sh,
+           n_sd, gg, per, kDnPerWg);
     return;
   }
   // A block of 2..5 or 8 tokens: router + routing, then the streaming

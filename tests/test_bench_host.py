@@ -11,6 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
+import synthetic as S  # noqa: E402
 
 
 def test_committed_traffic_record_matches_the_committed_kernel():
@@ -18,8 +19,11 @@ def test_committed_traffic_record_matches_the_committed_kernel():
     # record left behind by a later change would report no traffic at all
     t = bench.recorded_traffic("gateup_fused_kernel", "decode")
     assert isinstance(t, int)
-    # within 2 % of the launch's algorithmic bytes (98.04 MB): no re-reads
-    assert abs(t / 98.04e6 - 1.0) < 0.02
+    # within 2 % of the launch's algorithmic bytes (the whole one-token
+    # layer with 6 routed experts, 135.98 MB): no re-reads of weights
+    _, algo = bench.kernel_work("gateup_fused_kernel", S.get("decode"), 6)
+    assert abs(algo / 135.98e6 - 1.0) < 1e-4
+    assert abs(t / algo - 1.0) < 0.02
 
 
 def _fake_tree(tmp_path, src_text, recorded_sha):

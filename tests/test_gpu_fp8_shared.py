@@ -162,7 +162,7 @@ def test_layer_fp8_shared_real_shape_few_tokens(name, T, path):
     routed = _selected_bank(wT, x, wr, None)
     err, names = _fp8_layer_parity(wT, x, wr, None, routed, S.gen_fp8_bank(w, 0))
     if T == 1:
-        assert names == ["gateup_fused_kernel", "down_stream_kernel"]
+        assert names == ["gateup_fused_kernel"]
     else:
         assert names[:2] == ["fp8_gateup_gemv_kernel", "fp8_down_gemv_kernel"]
     assert path in names
@@ -182,7 +182,7 @@ ONE_TOKEN_FP8 = [
 def test_layer_fp8_shared_one_token_fused(w):
     x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
     err, names = _fp8_layer_parity(w, x, wr, None, S.gen_bank(w, 0), S.gen_fp8_bank(w, 0))
-    assert names == ["gateup_fused_kernel", "down_stream_kernel"]
+    assert names == ["gateup_fused_kernel"]
     assert err < 1e-4
 
 
@@ -192,7 +192,7 @@ def test_layer_fp8_shared_one_token_every_code():
     x, wr = S.gen_tokens(w, 1), S.gen_router(w, 1)
     err, names = _fp8_layer_parity(w, x, wr, None, S.gen_bank(w, 1),
                                    S.gen_fp8_bank(w, 1, all_codes=True))
-    assert names == ["gateup_fused_kernel", "down_stream_kernel"]
+    assert names == ["gateup_fused_kernel"]
     assert err < 1e-4
 
 
@@ -228,7 +228,7 @@ def test_layer_fp8_shared_one_token_deterministic_and_garbage_workspace():
         out = torch.empty((w.T, w.H), dtype=torch.float32, device=HP.dev())
         M.moe_layer_forward_fp8_shared(HP.to_dev(x), HP.to_dev(wr), None, rd, sd, w.k, out, None,
                                        None, ws)
-        assert _launch_names() == ["gateup_fused_kernel", "down_stream_kernel"]
+        assert _launch_names() == ["gateup_fused_kernel"]
         HP.assert_waits_ok(ws)
         outs.append(_np(out))
     for o in outs[1:]:

@@ -133,7 +133,7 @@ def _selected(w, x, wr):
     return sorted(sel)
 
 
-FUSED = ["gateup_fused_kernel", "down_stream_kernel"]
+FUSED = ["gateup_fused_kernel"]
 
 
 @pytest.mark.parametrize("name", ["decode", "spec5"])

@@ -347,7 +347,7 @@ def _launches():
 
 
 # kernels of the one-token path
-ONE_TOKEN_PATH = ["gateup_fused_kernel", "down_stream_kernel"]
+ONE_TOKEN_PATH = ["gateup_fused_kernel"]
 
 
 @pytest.mark.parametrize("variant", ["shared", "no_shared_with_bias"])

@@ -43,7 +43,7 @@ def _names():
 # verification block, and the three-launch chain (6 tokens)
 PATHS = [
     ("one_token", S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
-     ["gateup_fused_kernel", "down_stream_kernel"]),
+     ["gateup_fused_kernel"]),
     ("block", S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
      ["route_block_kernel", "gateup_block_kernel", "down_block_kernel", "combine_block_kernel"]),
     ("chain", S.Workload("chain6", 105, T=6, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
