@@ -605,7 +605,7 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
         if shared:
             b += dn_expert + T * I * 4 + T * H * 4
         return "hbm", b
-    if name == "down_block_kernel":
+    if name in ("down_block_kernel", "down_block_mfma_kernel"):
         # down of the U routed experts, h rows read, y rows written
         return "hbm", U * dn_expert + R * I * 4 + R * H * 4
     if name == "combine_block_kernel":

@@ -2169,6 +2169,219 @@ __global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block down on the matrix cores (blocks of at most 5 tokens). For one slot,
+// y[t][n] = sum_k W[n][k] h_t[k] over the slot's m <= 5 tokens is a dense
+// contraction of 64 weight rows (an item, 16 per wave) with m token rows.
+// Each fp32 h value is split exactly into three bf16 parts, h = hi + mid +
+// lo (each part holds the next 8 significant bits; bf16 has fp32's
+// exponent range), and the 16 rows of the MFMA's A operand are the (token,
+// part) pairs 3 t + p, read from LDS; the B operand is the weight rows'
+// codes converted exactly to bf16 with their E8M0 scales. One
+// v_mfma_f32_16x16x32_bf16 per 32 K values then serves every token and
+// part, each product of bf16 parts is exact and every sum is fp32, so the
+// result matches the fp32 GEMV to within fp32 rounding. The three parts of
+// a token are added at the end of the item. Compared with the fp32 GEMV,
+// where every 8 weight rows of a wave read the same h values from LDS, the
+// LDS reads per weight row drop by about 4x at the block's average of two
+// tokens per slot.
+// K order: lane group g (lanes 16 g .. 16 g + 15) of a wave takes K range
+// [128 S + 32 g, + 32) of super-step S, one E8M0 block: 16 bytes of codes
+// of its weight row, used by MFMA steps s = 0..3 for K values 8 s .. 8 s + 7
+// of that range, and A is read in the same order.
+// ---------------------------------------------------------------------------
+constexpr int kMfRows = 64;   // weight rows per item (16 per wave)
+constexpr int kMfSup = 18;    // super-steps of 128 K (I <= 2304)
+// bytes per staged row of bf16 h parts, padded so that the 16 rows a
+// fragment read touches fall in distinct LDS banks
+constexpr int kMfRowBytes = kMfSup * 256 + 16;
+constexpr int kMfLds = 16 * kMfRowBytes + 4 * 256 * 4;  // rows + a 16 x 16 tile per wave
+
+// One item's weights for a lane: 23 vector loads, so that two buffers stay
+// under the 63 loads a wave can have in flight.
+constexpr int kMfScl = (kMfSup * 4 + 15) / 16;  // 16-byte loads of a row's scales
+struct MfW {
+  uint4 c[kMfSup];     // codes of K range [128 S + 32 g, + 32)
+  uint4 sc[kMfScl];    // the row's scale bytes: block b at byte b % 16 of sc[b / 16]
+};
+
+// Item `it` of the routed slots: slot it / per, 64-row group it % per.
+struct MfItem {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int rg, row0, m;
+};
+__device__ __forceinline__ MfItem mf_item(const DecodeArgs& a, const LaneTable& tab, int it,
+                                          int per) {
+  const int sl = it / per, rg = it - sl * per;
+  const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + sl], 0), a.routed.E - 1));
+  const int row0 = min(max(tab[1 + a.max_slots + sl], 0), a.R);
+  const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, 5));
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  return MfItem{a.routed.d_codes + (size_t)e * a.H * crow,
+                a.routed.d_scales + (size_t)e * a.H * srow, rg, row0, m};
+}
+
+__device__ __forceinline__ void mf_issue(const DecodeArgs& a, const MfItem& d, MfW& r, bool live) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4;
+  const int row = min(d.rg * kMfRows + wave * 16 + (lane & 15), a.H - 1);
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  const __amdgpu_buffer_rsrc_t rc = matrix_rsrc(uniform_ptr(d.codes), live ? a.H * crow : 0u);
+  const __amdgpu_buffer_rsrc_t rs = matrix_rsrc(uniform_ptr(d.scales), live ? a.H * srow : 0u);
+  const int nsup = a.I >> 7;
+#pragma unroll
+  for (int S = 0; S < kMfSup; ++S) {
+    // super-steps past the row's K read nothing (an offset past the resource
+    // returns zeros)
+    r.c[S] = bload16(rc, S < nsup ? row * crow + S * 64 + g * 16 : 0x7ffffff0);
+  }
+  // the row's I / 32 scale bytes (the last load may run into the next row,
+  // or past the resource, which returns zeros; those bytes are not used)
+#pragma unroll
+  for (int j = 0; j < kMfScl; ++j)
+    r.sc[j] = bload16(rs, 16 * j < (int)srow ? row * srow + 16 * j : 0x7ffffff0);
+}
+
+// The slot's m h rows (fp32, written by the previous launch) into LDS as
+// bf16 parts: row 3 t + p of s_a holds part p of token t. Every load of a
+// thread is issued before the first is used (one wait, not one a round).
+constexpr int kMfStageU = (5 * (kMfSup * 128 / 8) + kThreads - 1) / kThreads;  // rounds
+__device__ __forceinline__ void mf_stage_h(const DecodeArgs& a, int row0, int m, char* s_a,
+                                           int rs) {
+  const int n8 = a.I >> 3;  // 8 values per thread and round
+  f32x4_t v0[kMfStageU], v1[kMfStageU];
+#pragma unroll
+  for (int u = 0; u < kMfStageU; ++u) {
+    const int q = max(min((int)threadIdx.x + u * kThreads, m * n8 - 1), 0);
+    const int t = q / n8, k = (q - t * n8) * 8;
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.h + (size_t)(row0 + t) * a.I + k);
+    v0[u] = src[0];
+    v1[u] = src[1];
+  }
+#pragma unroll
+  for (int u = 0; u < kMfStageU; ++u) {
+    const int q = (int)threadIdx.x + u * kThreads;
+    if (q >= m * n8) break;
+    const int t = q / n8, k = (q - t * n8) * 8;
+    const float v[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
+    uint32_t part[3][4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      float x0 = v[i], x1 = v[i + 1];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        // round to bf16 (nearest even); the remainder is exact in fp32
+        const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
+        const uint32_t r0 = (b0 + 0x7fffu + ((b0 >> 16) & 1u)) & 0xffff0000u;
+        const uint32_t r1 = (b1 + 0x7fffu + ((b1 >> 16) & 1u)) & 0xffff0000u;
+        part[p][i >> 1] = (r0 >> 16) | (r1 & 0xffff0000u);
+        x0 -= __uint_as_float(r0);
+        x1 -= __uint_as_float(r1);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      *reinterpret_cast<uint4*>(s_a + (3 * t + p) * rs + k * 2) =
+          make_uint4(part[p][0], part[p][1], part[p][2], part[p][3]);
+  }
+}
+
+// One item: 16 weight rows per wave against the staged (token, part) rows,
+// then y[row0 + t] for the item's rows, t < m.
+__device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d, const MfW& r,
+                                           const char* s_a, int rs, float* s_c) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, ar = lane & 15;
+  const int nsup = a.I >> 7;
+  const bool arow = ar < 3 * d.m;
+  const char* arow_p = s_a + ar * rs + g * 64;
+  // two accumulators (steps 0, 2 and 1, 3 of each super-step), and the
+  // super-step's four A fragments read together: the MFMAs do not wait on
+  // one another, nor each on its own LDS read
+  f32x4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
+#pragma unroll
+  for (int S = 0; S < kMfSup; ++S) {
+    if (S < nsup) {
+      uint4 av[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        av[q] = arow ? *reinterpret_cast<const uint4*>(arow_p + S * 256 + q * 16)
+                     : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 sv = r.sc[S >> 2];
+      const uint32_t sw = (S & 3) == 0 ? sv.x : (S & 3) == 1 ? sv.y : (S & 3) == 2 ? sv.z : sv.w;
+      const float sc = e8m0_to_f32(__builtin_amdgcn_ubfe(sw, 8u * g, 8));
+      const uint32_t w[4] = {r.c[S].x, r.c[S].y, r.c[S].z, r.c[S].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0);
+        const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1);
+        const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2);
+        const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3);
+        const bf16x8_t b = bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+        if (q & 1)
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[q]), b, c1,
+                                                        0, 0, 0);
+        else
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[q]), b, c0,
+                                                        0, 0, 0);
+      }
+    }
+  }
+  const f32x4_t c = c0 + c1;
+  // lane holds C[(t, p) = 4 g + i][weight row ar]; add the three parts of
+  // each token (hi, then mid, then lo) through this wave's 16 x 16 LDS tile
+  float* cw = s_c + wave * 256;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cw[(4 * g + i) * 16 + ar] = c[i];
+  __builtin_amdgcn_wave_barrier();
+  const int n = d.rg * kMfRows + wave * 16 + ar;
+  for (int t = g; t < d.m; t += 4) {
+    const float v = (cw[(3 * t) * 16 + ar] + cw[(3 * t + 1) * 16 + ar]) + cw[(3 * t + 2) * 16 + ar];
+    if (n < a.H) a.y[(size_t)(d.row0 + t) * a.H + n] = v;
+  }
+}
+
+// Block down for blocks of at most 5 tokens: routed (slot, 64-row group)
+// items slot-major, workgroup b taking the contiguous stretch
+// [n b / G, n (b + 1) / G) with two register buffers for the weights; the
+// slot's h parts are staged when an item's slot differs from the staged one.
+__global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs a, int G) {
+  __shared__ __align__(16) char lds[kMfLds];
+  constexpr int rs = kMfRowBytes;
+  char* s_a = lds;
+  float* s_c = reinterpret_cast<float*>(lds + 16 * rs);
+  LaneTable tab;
+  tab.load(a.tab, 1 + 3 * a.max_slots);
+  const int ns = min(max(tab[0], 0), a.max_slots);
+  const int per = (a.H + kMfRows - 1) / kMfRows;
+  const int n = ns * per;
+  const int b = blockIdx.x;
+  const int lo = (int)((long)n * b / G), hi = (int)((long)n * (b + 1) / G);
+  if (lo >= hi) return;
+  int staged = -1;
+  auto restage = [&](int it) {
+    const MfItem d = mf_item(a, tab, it, per);
+    __syncthreads();  // every wave is done with the staged rows
+    mf_stage_h(a, d.row0, d.m, s_a, rs);
+    __syncthreads();
+    staged = it / per;
+  };
+  MfW A, B;
+  mf_issue(a, mf_item(a, tab, lo, per), A, true);
+  restage(lo);
+  for (int i0 = lo; i0 < hi; i0 += 2) {
+    const int i1 = i0 + 1, i2 = i0 + 2;
+    mf_issue(a, mf_item(a, tab, i1 < hi ? i1 : i0, per), B, i1 < hi);
+    mf_compute(a, mf_item(a, tab, i0, per), A, s_a, rs, s_c);
+    if (i1 < hi && i1 / per != staged) restage(i1);
+    mf_issue(a, mf_item(a, tab, i2 < hi ? i2 : i0, per), A, i2 < hi);
+    if (i1 < hi) {
+      mf_compute(a, mf_item(a, tab, i1, per), B, s_a, rs, s_c);
+      if (i2 < hi && i2 / per != staged) restage(i2);
+    }
+  }
+}
+
 // Block gate/up: G persistent workgroups stage the T token rows and the
 // slot table, then stream the routed items with two register buffers. The
 // last n_sd workgroups of the grid each take one 32-row group of the shared
@@ -2216,9 +2429,11 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
 // Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
 // token in fixed order (shared row, then j = 0..k-1).
 __global__ __launch_bounds__(kThreads) void combine_block_kernel(DecodeArgs a) {
-  const uint32_t code = call_wait_code(a);  // every wait of the call ran in launch 1
-  finish_call(a, code, blockIdx.x, gridDim.x);
+  // every wait of the call ran in the earlier launches; the status read is
+  // in flight with the combine's loads, which do not wait on it
+  const uint32_t code = call_wait_code(a);
   combine_column(a, blockIdx.x, code != 0);
+  finish_call(a, code, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -2384,11 +2599,25 @@ void launch_chain(const DecodeArgs& a, const DecodeLayout& L, bool ffn, bool sha
                      a, ffn ? 0 : 1);
 }
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Persistent grids no larger than the workgroups the CUs hold at once:
 // three a CU by registers, fewer where the LDS a workgroup needs allows less.
 int resident_grid(uint32_t lds_bytes) {
   const int by_lds = lds_bytes ? (int)(163840u / lds_bytes) : 3;
-  return 256 * (by_lds < 3 ? (by_lds < 1 ? 1 : by_lds) : 3);
+  return cu_count() * (by_lds < 3 ? (by_lds < 1 ? 1 : by_lds) : 3);
 }
 
 template <int TB>
@@ -2406,10 +2635,19 @@ void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch
   const int n_sd = shared ? L.dn_items : 0;
   launch("gateup_block_kernel", gateup_block_kernel<TB>, dim3(gg + n_sd), dim3(kThreads), lds_gu,
          s, a, gg);
-  const uint32_t lds_dn = (uint32_t)(d.T * 8 * kDnU * 8 * 16);
-  const int nd = L.max_slots * L.dn_items, rd = resident_grid(lds_dn);
-  const int gd = nd < rd ? nd : rd;
-  launch("down_block_kernel", down_block_kernel<TB>, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
+  if constexpr (TB <= 5) {
+    // on the matrix cores: 16 staged rows of bf16 h parts and a 16 x 16
+    // fp32 tile per wave (76 KB of LDS); two workgroups a CU
+    const int nd = L.max_slots * ((d.H + kMfRows - 1) / kMfRows), rd = 2 * cu_count();
+    const int gd = nd < rd ? nd : rd;
+    launch("down_block_mfma_kernel", down_block_mfma_kernel, dim3(gd), dim3(kThreads), 0, s, a,
+           gd);
+  } else {
+    const uint32_t lds_dn = (uint32_t)(d.T * 8 * kDnU * 8 * 16);
+    const int nd = L.max_slots * L.dn_items, rd = resident_grid(lds_dn);
+    const int gd = nd < rd ? nd : rd;
+    launch("down_block_kernel", down_block_kernel<TB>, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
+  }
   launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
 }
 

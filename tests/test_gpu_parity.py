@@ -374,9 +374,11 @@ BLOCKS = [
     S.Workload("blk_eight_wide", 101, T=8, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
 ]
 
-# kernels of the block path
-BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_kernel",
-              "combine_block_kernel"]
+# kernels of the block path: blocks of up to 5 tokens take the down rows on
+# the matrix cores, blocks of 8 the fp32 GEMV
+def block_path(T):
+    down = "down_block_mfma_kernel" if T <= 5 else "down_block_kernel"
+    return ["route_block_kernel", "gateup_block_kernel", down, "combine_block_kernel"]
 
 
 @pytest.mark.parametrize("variant", ["shared", "no_shared_with_bias"])
@@ -387,7 +389,7 @@ def test_layer_block_path(w, variant):
     if variant == "no_shared_with_bias":
         bias, shared = np.linspace(-0.5, 0.5, w.E).astype(np.float32), None
     err = _layer_parity(w, d["x"], d["w_router"], bias, d["routed"], shared)
-    assert _launches() == BLOCK_PATH
+    assert _launches() == block_path(w.T)
     assert err < HP.FP32_TOL
 
 
@@ -402,7 +404,7 @@ def test_layer_block_of_eight_real_shape():
     shared = S.gen_bank(w, 0, shared=True)
     print(f"verify8 union of routed experts: {len(sel)} of {w.T * w.k}")
     err = _layer_parity(w, x, wr, None, routed, shared)
-    assert _launches() == BLOCK_PATH
+    assert _launches() == block_path(w.T)
     assert err < HP.FP32_TOL
 
 
@@ -416,7 +418,7 @@ def test_layer_block_path_correlated_tokens_share_experts():
     union = set(r["ids"].reshape(-1).tolist())
     assert len(union) < w.T * w.k  # experts are shared between tokens
     err = _layer_parity(w, d["x"], d["w_router"], None, d["routed"], d["shared"])
-    assert _launches() == BLOCK_PATH
+    assert _launches() == block_path(w.T)
     assert err < HP.FP32_TOL
 
 
