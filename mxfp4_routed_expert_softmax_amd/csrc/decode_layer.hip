@@ -2109,66 +2109,6 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
   }
 }
 
-// Block down: routed (slot, 32-row group) items slot-major; workgroup b
-// takes the contiguous stretch
-// [n b / G, n (b + 1) / G) with two register buffers for the weights. The
-// combine is a launch of its own: combining in the last workgroup to finish
-// a column group put the combine's coherent loads on the tail of this one.
-template <int TB>
-__global__ __launch_bounds__(kThreads, 3) void down_block_kernel(DecodeArgs a, int G) {
-  extern __shared__ __align__(16) char lds[];
-  // LDS holds only the staged h rows; the slot table rides across the lanes
-  f32x4_t* s_h = reinterpret_cast<f32x4_t*>(lds);
-  LaneTable tab;
-  tab.load(a.tab, 1 + 3 * a.max_slots);
-  const int ns = min(max(tab[0], 0), a.max_slots);
-  const int nr = ns * a.dn_items;
-  const int n = nr;  // the shared expert's rows were done in the gate/up launch
-  const int b = blockIdx.x;
-  const int lo = (int)((long)n * b / G), hi = (int)((long)n * (b + 1) / G);
-  if (lo >= hi) return;
-  // item it: routed items first, so the shared groups follow at offset nr
-  auto item = [&](int it) {
-    return it < nr ? blk_item<TB>(a, tab, 0, it, a.dn_items, false)
-                   : blk_item<TB>(a, tab, a.dn_items, it - nr, a.dn_items, false);
-  };
-  auto slot_of = [&](int it) { return it < nr ? it / a.dn_items : ns; };
-  // The slot's h rows are copied into LDS when an item's slot differs from
-  // the one staged (once or twice per workgroup: its items are a contiguous
-  // stretch), each copy issued between the item's weights and the next
-  // item's, so waiting for it never waits for the next item's weights.
-  const uint32_t s_h_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  auto restage = [&](int it, int& staged) {
-    __syncthreads();  // every wave is done reading the staged rows
-    dn_copy_h(a, item(it), s_h_lds);
-    staged = slot_of(it);
-  };
-  int staged = -1;
-  DnW A, B;
-  dn_issue_blk(a, item(lo), A, true);
-  restage(lo, staged);
-  bool fresh = true;
-  for (int i0 = lo; i0 < hi; i0 += 2) {
-    const int i1 = i0 + 1, i2 = i0 + 2;
-    dn_issue_blk(a, item(i1 < hi ? i1 : i0), B, i1 < hi);
-    dn_compute_blk<TB>(a, item(i0), fresh, A, s_h);
-    fresh = false;
-    if (i1 < hi && slot_of(i1) != staged) {
-      restage(i1, staged);
-      fresh = true;
-    }
-    dn_issue_blk(a, item(i2 < hi ? i2 : i0), A, i2 < hi);
-    if (i1 < hi) {
-      dn_compute_blk<TB>(a, item(i1), fresh, B, s_h);
-      fresh = false;
-      if (i2 < hi && slot_of(i2) != staged) {
-        restage(i2, staged);
-        fresh = true;
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Block down on the matrix cores (blocks of at most 5 tokens). For one slot,
 // y[t][n] = sum_k W[n][k] h_t[k] over the slot's m <= 5 tokens is a dense
@@ -2216,7 +2156,7 @@ __device__ __forceinline__ MfItem mf_item(const DecodeArgs& a, const LaneTable& 
   const int sl = it / per, rg = it - sl * per;
   const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + sl], 0), a.routed.E - 1));
   const int row0 = min(max(tab[1 + a.max_slots + sl], 0), a.R);
-  const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, 5));
+  const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, 8));
   const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
   return MfItem{a.routed.d_codes + (size_t)e * a.H * crow,
                 a.routed.d_scales + (size_t)e * a.H * srow, rg, row0, m};
@@ -2243,28 +2183,22 @@ __device__ __forceinline__ void mf_issue(const DecodeArgs& a, const MfItem& d, M
     r.sc[j] = bload16(rs, 16 * j < (int)srow ? row * srow + 16 * j : 0x7ffffff0);
 }
 
+// Parts of each h value a slot of m tokens carries: three bf16 (exact) up
+// to 5 tokens, so that the (token, part) rows fit one 16-row tile; two (16
+// significant bits, relative error at most 2^-17) for 6 to 8 tokens.
+__device__ __forceinline__ int mf_parts(int m) { return m <= 5 ? 3 : 2; }
+
 // The slot's m h rows (fp32, written by the previous launch) into LDS as
-// bf16 parts: row 3 t + p of s_a holds part p of token t. Every load of a
-// thread is issued before the first is used (one wait, not one a round).
-constexpr int kMfStageU = (5 * (kMfSup * 128 / 8) + kThreads - 1) / kThreads;  // rounds
+// bf16 parts: row P t + p of s_a holds part p of token t (P = mf_parts(m)).
 __device__ __forceinline__ void mf_stage_h(const DecodeArgs& a, int row0, int m, char* s_a,
                                            int rs) {
   const int n8 = a.I >> 3;  // 8 values per thread and round
-  f32x4_t v0[kMfStageU], v1[kMfStageU];
-#pragma unroll
-  for (int u = 0; u < kMfStageU; ++u) {
-    const int q = max(min((int)threadIdx.x + u * kThreads, m * n8 - 1), 0);
+  const int P = mf_parts(m);
+  for (int q = threadIdx.x; q < m * n8; q += kThreads) {
     const int t = q / n8, k = (q - t * n8) * 8;
     const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.h + (size_t)(row0 + t) * a.I + k);
-    v0[u] = src[0];
-    v1[u] = src[1];
-  }
-#pragma unroll
-  for (int u = 0; u < kMfStageU; ++u) {
-    const int q = (int)threadIdx.x + u * kThreads;
-    if (q >= m * n8) break;
-    const int t = q / n8, k = (q - t * n8) * 8;
-    const float v[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
+    const f32x4_t v0 = src[0], v1 = src[1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t part[3][4];
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -2282,8 +2216,9 @@ __device__ __forceinline__ void mf_stage_h(const DecodeArgs& a, int row0, int m,
     }
 #pragma unroll
     for (int p = 0; p < 3; ++p)
-      *reinterpret_cast<uint4*>(s_a + (3 * t + p) * rs + k * 2) =
-          make_uint4(part[p][0], part[p][1], part[p][2], part[p][3]);
+      if (p < P)
+        *reinterpret_cast<uint4*>(s_a + (P * t + p) * rs + k * 2) =
+            make_uint4(part[p][0], part[p][1], part[p][2], part[p][3]);
   }
 }
 
@@ -2293,7 +2228,8 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
                                            const char* s_a, int rs, float* s_c) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, ar = lane & 15;
   const int nsup = a.I >> 7;
-  const bool arow = ar < 3 * d.m;
+  const int P = mf_parts(d.m);
+  const bool arow = ar < P * d.m;
   const char* arow_p = s_a + ar * rs + g * 64;
   // two accumulators (steps 0, 2 and 1, 3 of each super-step), and the
   // super-step's four A fragments read together: the MFMAs do not wait on
@@ -2336,7 +2272,8 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
   __builtin_amdgcn_wave_barrier();
   const int n = d.rg * kMfRows + wave * 16 + ar;
   for (int t = g; t < d.m; t += 4) {
-    const float v = (cw[(3 * t) * 16 + ar] + cw[(3 * t + 1) * 16 + ar]) + cw[(3 * t + 2) * 16 + ar];
+    float v = cw[(P * t) * 16 + ar] + cw[(P * t + 1) * 16 + ar];
+    if (P == 3) v += cw[(P * t + 2) * 16 + ar];
     if (n < a.H) a.y[(size_t)(d.row0 + t) * a.H + n] = v;
   }
 }
@@ -2635,18 +2572,13 @@ void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch
   const int n_sd = shared ? L.dn_items : 0;
   launch("gateup_block_kernel", gateup_block_kernel<TB>, dim3(gg + n_sd), dim3(kThreads), lds_gu,
          s, a, gg);
-  if constexpr (TB <= 5) {
+  {
     // on the matrix cores: 16 staged rows of bf16 h parts and a 16 x 16
     // fp32 tile per wave (76 KB of LDS); two workgroups a CU
     const int nd = L.max_slots * ((d.H + kMfRows - 1) / kMfRows), rd = 2 * cu_count();
     const int gd = nd < rd ? nd : rd;
     launch("down_block_mfma_kernel", down_block_mfma_kernel, dim3(gd), dim3(kThreads), 0, s, a,
            gd);
-  } else {
-    const uint32_t lds_dn = (uint32_t)(d.T * 8 * kDnU * 8 * 16);
-    const int nd = L.max_slots * L.dn_items, rd = resident_grid(lds_dn);
-    const int gd = nd < rd ? nd : rd;
-    launch("down_block_kernel", down_block_kernel<TB>, dim3(gd), dim3(kThreads), lds_dn, s, a, gd);
   }
   launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
 }
@@ -2748,12 +2680,9 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
            n_sd, gg, per, kDnPerWg);
     return;
   }
-  // A block of 2..5 or 8 tokens: router + routing, then the streaming
-  // gate/up and down launches over the union of the block's experts. At 6
-  // and 7 tokens the instantiation for 8 measured no faster than the chain
-  // below at the real shape (164.5 and 184.0 us against 165.2 and 166.3 us),
-  // so those take the chain.
-  const bool block = d.T >= 2 && d.T <= kBlockT && d.T != 6 && d.T != 7 && !ffn &&
+  // A block of 2..8 tokens: router + routing, then the streaming gate/up
+  // and down launches over the union of the block's experts.
+  const bool block = d.T >= 2 && d.T <= kBlockT && !ffn &&
                      (d.H >> 5) <= kGuLanes * kGuU &&
                      d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU &&
                      d.E <= 16 * kWave && 1 + 3 * L.max_slots <= LaneTable::kMax &&

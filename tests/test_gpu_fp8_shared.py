@@ -149,7 +149,8 @@ def _selected_bank(w, x, wr, bias):
 @pytest.mark.parametrize("name,T,path", [
     ("decode", 1, "gateup_fused_kernel"),
     ("spec5", 5, "gateup_block_kernel"),
-    ("spec5", 6, "gateup_kernel"),
+    ("spec5", 6, "gateup_block_kernel"),
+    ("spec5", 9, "gateup_kernel"),
 ])
 def test_layer_fp8_shared_real_shape_few_tokens(name, T, path):
     # one token streams the FP8 expert inside the fused launches; more tokens

@@ -40,14 +40,14 @@ def _names():
 
 
 # one workload per few-token path: one token (fused launches), a
-# verification block, and the three-launch chain (6 tokens)
+# verification block, and the three-launch chain (9 tokens)
 PATHS = [
     ("one_token", S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
      ["gateup_fused_kernel"]),
     ("block", S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
      ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
       "combine_block_kernel"]),
-    ("chain", S.Workload("chain6", 105, T=6, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    ("chain", S.Workload("chain9", 105, T=9, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
      ["route_kernel", "gateup_kernel", "down_kernel"]),
 ]
 
