@@ -596,6 +596,9 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
         b = w.E * H * 2 + T * H * 2 + T * w.E * 4
         if shared:
             b += gu_expert + T * I * 4
+        if shared8:
+            # the FP8 shared expert's gate/up: 1 byte per weight, 1 per block
+            b += 2 * I * H + 2 * (I // 32) * (H // 32) + T * I * 4
         return "hbm", b
     if name == "gateup_block_kernel":
         # gate/up of the U routed experts, each read once for all the block's
@@ -604,12 +607,14 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
         b = U * gu_expert + T * H * 2 + R * I * 4
         if shared:
             b += dn_expert + T * I * 4 + T * H * 4
+        if shared8:
+            b += H * I + (H // 32) * (I // 32) + T * I * 4 + T * H * 4
         return "hbm", b
     if name in ("down_block_kernel", "down_block_mfma_kernel"):
         # down of the U routed experts, h rows read, y rows written
         return "hbm", U * dn_expert + R * I * 4 + R * H * 4
     if name == "combine_block_kernel":
-        rows = R + (T if shared else 0)
+        rows = R + (T if shared or shared8 else 0)
         return "hbm", rows * H * 4 + T * H * 4 + T * w.k * 8
     if name in ("gateup_stream_kernel", "gateup_kernel"):
         # routed gate/up of the U experts (+ the shared expert's down rows)

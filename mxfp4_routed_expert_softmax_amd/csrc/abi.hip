@@ -90,8 +90,9 @@ size_t fp8_ffn_ws(int T, int H, int I) {
 
 // Workspace of the few-token layer with an FP8 shared expert: the decode
 // path's (no MXFP4 shared expert), then y_sh [T][H], then the FP8 scratch.
-// (One token may instead stream the FP8 expert inside the fused launches,
-// which needs the decode layout with a shared expert.)
+// (One token and blocks of 2..8 tokens may instead stream the FP8 expert
+// inside the few-token launches, which needs the decode layout with a shared
+// expert.)
 size_t few_fp8_ws(int T, int H, int I, int E, int k) {
   const size_t sep = align_up(decode_ws_bytes(T, H, I, E, k, T * k, false, false)) +
                      align_up((size_t)T * H * sizeof(float)) + fp8_ffn_ws(T, H, I);
@@ -470,8 +471,8 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
     d.ids_out = topk_ids_out;
     d.w_out = topk_w_out;
     if (shared8) {
-      // one token: the FP8 expert streams inside the fused launches, like
-      // the MXFP4 shared expert
+      // one token, and blocks of 2..8 tokens: the FP8 expert streams inside
+      // the few-token launches, like the MXFP4 shared expert
       DecodeLaunch f = d;
       f.has_shared = true;
       f.shared_fp8 = true;

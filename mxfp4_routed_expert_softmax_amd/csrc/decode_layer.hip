@@ -1964,9 +1964,146 @@ __device__ __forceinline__ void gateup_block_items(const DecodeArgs& a, const Ta
   }
 }
 
+// FP8 shared expert in the block launches: the columns and rows of the
+// one-token FP8 items, each 16-byte weight chunk converted once and used for
+// every token of the block. Gate/up item `item` (the route launch): 8
+// columns of the block's shared h rows R .. R + T - 1, 32 lanes per column;
+// the weights are requested before the token rows are staged (row t at
+// s_x + t * H / 8, when `stage`).
+template <int TB>
+__device__ void fp8_shared_gu_blk(const DecodeArgs& a, int item, uint4* s_x, bool stage) {
+  const int H = a.H, I = a.I, T = min(a.T, TB);
+  const int lane = lane_id(), wave = threadIdx.x >> 6, j = lane & 31;
+  const int n = item * kGuRows + wave * 2 + (lane >> 5);
+  const bool ok = n < I;
+  const int nr = ok ? n : I - 1;
+  const int nch = H >> 4, sb = H >> 5, nv = H >> 3;
+  const __amdgpu_buffer_rsrc_t rg = matrix_rsrc(a.sh8_gu_w, (uint32_t)I * H);
+  const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(a.sh8_gu_w + (size_t)I * H, (uint32_t)I * H);
+  const __amdgpu_buffer_rsrc_t rs = matrix_rsrc(a.sh8_gu_s, (uint32_t)(2 * (I >> 5) * sb));
+  uint4 wg[kF8GuU], wu[kF8GuU];
+  uint32_t sg[kF8GuU], su[kF8GuU];
+#pragma unroll
+  for (int u = 0; u < kF8GuU; ++u) {
+    const int c = j + 32 * u;
+    wg[u] = bload16(rg, nr * H + c * 16);
+    wu[u] = bload16(ru, nr * H + c * 16);
+    sg[u] = bload8(rs, (nr >> 5) * sb + (c >> 1));
+    su[u] = bload8(rs, ((I + nr) >> 5) * sb + (c >> 1));
+  }
+  if (stage) {
+    stage_rows<uint4>(
+        T * nv, [&](int idx) { return reinterpret_cast<const uint4*>(a.x)[idx]; },
+        [&](int idx, uint4 v) { s_x[idx] = v; });
+    __syncthreads();
+  }
+  float ag[TB], au[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) ag[t] = au[t] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kF8GuU; ++u) {
+    const int c = j + 32 * u;
+    if (c < nch) {
+      const float fg = e8m0_to_f32(sg[u]), fu = e8m0_to_f32(su[u]);
+      const uint32_t gw[4] = {wg[u].x, wg[u].y, wg[u].z, wg[u].w};
+      const uint32_t uw[4] = {wu[u].x, wu[u].y, wu[u].z, wu[u].w};
+      bf16x2_t g2[8], u2[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g2[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw[i], fg, false);
+        g2[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw[i], fg, true);
+        u2[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(uw[i], fu, false);
+        u2[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(uw[i], fu, true);
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        if (t < T) {
+          const uint4 x0 = s_x[t * nv + 2 * c], x1 = s_x[t * nv + 2 * c + 1];
+          const uint32_t xx[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            ag[t] = __builtin_amdgcn_fdot2_f32_bf16(g2[p], as_bf16x2(xx[p]), ag[t], false);
+            au[t] = __builtin_amdgcn_fdot2_f32_bf16(u2[p], as_bf16x2(xx[p]), au[t], false);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    if (t < T) {
+      const float g = group_sum<32>(ag[t]), u = group_sum<32>(au[t]);
+      if (ok && j == 0) a.h[(size_t)(a.R + t) * I + n] = silu_mul(g, u);
+    }
+  }
+}
+
+// Down item c (the gate/up launch's tail): 32 rows of the block's shared y
+// rows, 8 lanes per row, from the h rows the route launch wrote (staged in
+// LDS, row t at s_h + t * I / 4, after the weights are requested).
+template <int TB>
+__device__ void fp8_shared_down_blk(const DecodeArgs& a, int c, f32x4_t* s_h) {
+  const int H = a.H, I = a.I, T = min(a.T, TB);
+  const int q = threadIdx.x & 7;
+  const int n = c * kDnRows + (threadIdx.x >> 3);
+  const bool ok = n < H;
+  const int nr = ok ? n : H - 1;
+  const int nch = I >> 4, sb = I >> 5, nv = I >> 2;
+  const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(a.sh8_d_w, (uint32_t)H * I);
+  const __amdgpu_buffer_rsrc_t rs = matrix_rsrc(a.sh8_d_s, (uint32_t)((H >> 5) * sb));
+  uint4 wd[kF8DnU];
+  uint32_t sd[kF8DnU];
+#pragma unroll
+  for (int u = 0; u < kF8DnU; ++u) {
+    const int cc = q + 8 * u;
+    wd[u] = bload16(rd, nr * I + cc * 16);
+    sd[u] = bload8(rs, (nr >> 5) * sb + (cc >> 1));
+  }
+  const f32x4_t* hrows = reinterpret_cast<const f32x4_t*>(a.h + (size_t)a.R * I);
+  for (int f = threadIdx.x; f < T * nv; f += kThreads) s_h[f] = hrows[f];
+  __syncthreads();
+  float acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kF8DnU; ++u) {
+    const int cc = q + 8 * u;
+    if (cc < nch) {
+      const float f = e8m0_to_f32(sd[u]);
+      const uint32_t ww[4] = {wd[u].x, wd[u].y, wd[u].z, wd[u].w};
+      f32x2_t p[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ww[i], f, false);
+        p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ww[i], f, true);
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        if (t < T) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4_t h4 = s_h[t * nv + 4 * cc + i];
+            acc[t] = fmaf(p[2 * i].x, h4.x, acc[t]);
+            acc[t] = fmaf(p[2 * i].y, h4.y, acc[t]);
+            acc[t] = fmaf(p[2 * i + 1].x, h4.z, acc[t]);
+            acc[t] = fmaf(p[2 * i + 1].y, h4.w, acc[t]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    if (t < T) {
+      const float v = group_sum<8>(acc[t]);
+      if (ok && q == 0) cst(a.y + (size_t)(a.R + t) * H + n, v);
+    }
+  }
+}
+
 // Block launch 1: [router rows | the routing workgroup | n_sw workgroups
-// streaming the shared expert's gate/up items, which need no routing and
-// use the bandwidth the router and the routing leave idle].
+// streaming the shared expert's gate/up items (MXFP4 or FP8), which need no
+// routing and use the bandwidth the router and the routing leave idle].
 template <int TB>
 __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int n_sw) {
   extern __shared__ __align__(16) char lds[];
@@ -1975,6 +2112,10 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int
     router_rows_blk(a, b, reinterpret_cast<uint4*>(lds));
   } else if (b == a.nb_router) {
     routing<true>(a, lds);
+  } else if (a.shared_fp8) {
+    bool stage = true;
+    for (int it = b - a.nb_router - 1; it < a.gu_items; it += n_sw, stage = false)
+      fp8_shared_gu_blk<TB>(a, it, reinterpret_cast<uint4*>(lds), stage);
   } else {
     uint4* s_x = reinterpret_cast<uint4*>(lds);
     stage_block_rows(a, s_x);
@@ -2322,12 +2463,16 @@ __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs
 // Block gate/up: G persistent workgroups stage the T token rows and the
 // slot table, then stream the routed items with two register buffers. The
 // last n_sd workgroups of the grid each take one 32-row group of the shared
-// expert's down rows (its h rows came from the previous launch); dispatched
-// last, they run in the tail of the routed stream.
+// expert's down rows (MXFP4 or FP8; its h rows came from the previous
+// launch); dispatched last, they run in the tail of the routed stream.
 template <int TB>
 __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
   if ((int)blockIdx.x >= G) {
+    if (a.shared_fp8) {
+      fp8_shared_down_blk<TB>(a, (int)blockIdx.x - G, reinterpret_cast<f32x4_t*>(lds));
+      return;
+    }
     const int* none = nullptr;
     const BlkItem d = blk_item<TB>(a, none, a.dn_items, (int)blockIdx.x - G, a.dn_items, false);
     DnW A;
@@ -2592,6 +2737,14 @@ static bool stream_path(const DecodeLaunch& d, const DecodeLayout& L) {
          1 + 3 * L.max_slots + 2 * d.k <= 1024 && d.k <= kWave && d.E <= 16 * kWave;
 }
 
+// A block of 2..8 tokens takes this call.
+static bool block_path(const DecodeLaunch& d, const DecodeLayout& L) {
+  return d.T >= 2 && d.T <= kBlockT && d.ffn_mode == 0 && (d.H >> 5) <= kGuLanes * kGuU &&
+         d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU && d.E <= 16 * kWave &&
+         1 + 3 * L.max_slots <= LaneTable::kMax && d.R <= LaneTable::kMax &&
+         d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
+}
+
 bool decode_fuses_nvfp4(const DecodeLaunch& d) {
   if (d.ffn_mode != 0 || d.T != 1) return false;
   const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, false, d.has_shared);
@@ -2599,10 +2752,11 @@ bool decode_fuses_nvfp4(const DecodeLaunch& d) {
 }
 
 bool decode_fuses_fp8_shared(const DecodeLaunch& d) {
-  if (d.ffn_mode != 0 || d.T != 1) return false;
+  if (d.ffn_mode != 0) return false;
   const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, false, true);
   // the FP8 items hold K = H in 32 x kF8GuU chunks and K = I in 8 x kF8DnU
-  return stream_path(d, L) && (d.H >> 4) <= 32 * kF8GuU && (d.I >> 4) <= 8 * kF8DnU;
+  if ((d.H >> 4) > 32 * kF8GuU || (d.I >> 4) > 8 * kF8DnU) return false;
+  return d.T == 1 ? stream_path(d, L) : block_path(d, L);
 }
 
 void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
@@ -2682,12 +2836,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   }
   // A block of 2..8 tokens: router + routing, then the streaming gate/up
   // and down launches over the union of the block's experts.
-  const bool block = d.T >= 2 && d.T <= kBlockT && !ffn &&
-                     (d.H >> 5) <= kGuLanes * kGuU &&
-                     d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU &&
-                     d.E <= 16 * kWave && 1 + 3 * L.max_slots <= LaneTable::kMax &&
-                     d.R <= LaneTable::kMax && d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
-  if (block) {
+  if (block_path(d, L)) {
     if (d.T <= 5)
       launch_block<5>(a, L, d, shared, s);
     else

@@ -146,15 +146,23 @@ def _selected_bank(w, x, wr, bias):
     return S.gen_bank(w, 0, experts=sorted(sel))
 
 
+BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
+              "combine_block_kernel"]
+
+
 @pytest.mark.parametrize("name,T,path", [
     ("decode", 1, "gateup_fused_kernel"),
+    ("spec5", 2, "gateup_block_kernel"),
     ("spec5", 5, "gateup_block_kernel"),
     ("spec5", 6, "gateup_block_kernel"),
+    ("spec5", 8, "gateup_block_kernel"),
     ("spec5", 9, "gateup_kernel"),
 ])
 def test_layer_fp8_shared_real_shape_few_tokens(name, T, path):
-    # one token streams the FP8 expert inside the fused launches; more tokens
-    # run it first, in its own two launches
+    # one token streams the FP8 expert inside the fused launch and a block of
+    # 2..8 tokens inside the block launches (gate/up in the route launch,
+    # down in the gate/up launch's tail); more tokens run it first, in its
+    # own two launches
     w = S.get(name)
     x = S.gen_tokens(w, 0, T=T) if T != w.T else S.gen_tokens(w, 0)
     wr = S.gen_router(w, 0)
@@ -164,9 +172,31 @@ def test_layer_fp8_shared_real_shape_few_tokens(name, T, path):
     err, names = _fp8_layer_parity(wT, x, wr, None, routed, S.gen_fp8_bank(w, 0))
     if T == 1:
         assert names == ["gateup_fused_kernel"]
+    elif T <= 8:
+        assert names == BLOCK_PATH
     else:
         assert names[:2] == ["fp8_gateup_gemv_kernel", "fp8_down_gemv_kernel"]
     assert path in names
+    assert err < 1e-4
+
+
+# blocks of tokens through the block launches at shapes where the item
+# counts, the tokens per block and the routed rows per slot differ from the
+# real shape's (block of 3: the 5-token build; 7: the 8-token build; every
+# finite E4M3 byte in the last)
+BLOCK_FP8 = [
+    (S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3), False),
+    (S.Workload("blk_small7", 97, T=7, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3), False),
+    (S.Workload("blk_wide4", 98, T=4, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3), True),
+]
+
+
+@pytest.mark.parametrize("w,every", BLOCK_FP8, ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_fp8_shared_block_launches(w, every):
+    x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
+    err, names = _fp8_layer_parity(w, x, wr, None, S.gen_bank(w, 0),
+                                   S.gen_fp8_bank(w, 0, all_codes=every))
+    assert names == BLOCK_PATH
     assert err < 1e-4
 
 
