@@ -637,8 +637,9 @@ int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
   if (!aligned16(x_bf16) || !aligned16(w_router_bf16) || !aligned16(out))
     return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
-  if (T == 1) {
-    // one token: the fused launches, with NVFP4 items
+  if (T <= kDecodeMaxT) {
+    // one token: the fused launch; a block of 2..8 tokens: the block
+    // launches; both with NVFP4 items
     DecodeLaunch d{};
     d.ffn_mode = 0;
     d.x = static_cast<const uint16_t*>(x_bf16);

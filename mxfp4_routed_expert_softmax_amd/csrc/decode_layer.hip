@@ -1759,6 +1759,7 @@ struct BlkItem {
   int row0;   // first h / y row of the slot
   int m;      // the slot's rows (tokens)
   bool shared;
+  int e;      // routed expert (NVFP4 matrix scales); -1: the shared expert
 };
 
 // A small table held across the lanes of a wave: entry i sits in lane
@@ -1779,30 +1780,34 @@ struct LaneTable {
   }
 };
 
-template <int TB, class Tab>
+template <int TB, bool NV, class Tab>
 __device__ __forceinline__ BlkItem blk_item(const DecodeArgs& a, const Tab& tab, int n_sh, int it,
                                             int per, bool gu) {
-  const uint32_t crow = (uint32_t)(gu ? a.H : a.I) >> 1, srow = (uint32_t)(gu ? a.H : a.I) >> 5;
+  const uint32_t crow = (uint32_t)(gu ? a.H : a.I) >> 1;
+  const uint32_t srow = (uint32_t)(gu ? a.H : a.I) >> (NV ? 4 : 5);
   const size_t mat = gu ? 2 * (size_t)a.I : (size_t)a.H;
   const uint8_t* c0 = gu ? a.routed.gu_codes : a.routed.d_codes;
   const uint8_t* s0 = gu ? a.routed.gu_scales : a.routed.d_scales;
   if (it < n_sh)
     return BlkItem{gu ? a.shared.gu_codes : a.shared.d_codes,
-                   gu ? a.shared.gu_scales : a.shared.d_scales, it, a.R, min(a.T, TB), true};
+                   gu ? a.shared.gu_scales : a.shared.d_scales, it, a.R, min(a.T, TB), true, -1};
   const int q = it - n_sh, sl = q / per, rb = q - sl * per;
   const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + sl], 0), a.routed.E - 1));
   const int row0 = min(max(tab[1 + a.max_slots + sl], 0), a.R);
   const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, TB));
-  return BlkItem{c0 + (size_t)e * mat * crow, s0 + (size_t)e * mat * srow, rb, row0, m, false};
+  return BlkItem{c0 + (size_t)e * mat * crow, s0 + (size_t)e * mat * srow, rb, row0, m, false, e};
 }
 
+// NV: an NVFP4 bank, whose 32-code chunk j + 32 u has its two scale bytes
+// in half j % 2 of the word at 4 (j / 2) + 64 u of the row's H / 16.
+template <bool NV>
 __device__ __forceinline__ void gu_issue_blk(const DecodeArgs& a, const BlkItem& d, GuRegs& r,
                                              bool live) {
   live = __builtin_amdgcn_readfirstlane((int)live) != 0;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & (kGuLanes - 1);
   const int nr = min(d.rb * kGuRows + wave * (kWave / kGuLanes) + lane / kGuLanes, a.I - 1);
-  const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> 5;
+  const uint32_t crow = (uint32_t)a.H >> 1, srow = (uint32_t)a.H >> (NV ? 4 : 5);
   const uint8_t* gbase = uniform_ptr(d.codes);
   const uint8_t* sbase = uniform_ptr(d.scales);
   const uint32_t cb = live ? a.I * crow : 0u, sb = live ? a.I * srow : 0u;
@@ -1810,13 +1815,14 @@ __device__ __forceinline__ void gu_issue_blk(const DecodeArgs& a, const BlkItem&
   const __amdgpu_buffer_rsrc_t ru = matrix_rsrc(gbase + (size_t)a.I * crow, cb);
   const __amdgpu_buffer_rsrc_t rgs = matrix_rsrc(sbase, sb);
   const __amdgpu_buffer_rsrc_t rus = matrix_rsrc(sbase + (size_t)a.I * srow, sb);
-  const int co = nr * crow + j * 16, so = nr * srow + (j & ~3);
+  const int co = nr * crow + j * 16, so = nr * srow + (NV ? 4 * (j >> 1) : (j & ~3));
+  constexpr int su_step = NV ? 2 * kGuLanes : kGuLanes;
 #pragma unroll
   for (int u = 0; u < kGuU; ++u) {
     r.g[u] = bload16(rg, co + u * kGuLanes * 16);
     r.u[u] = bload16(ru, co + u * kGuLanes * 16);
-    r.sg[u] = bload32(rgs, so + u * kGuLanes);
-    r.su[u] = bload32(rus, so + u * kGuLanes);
+    r.sg[u] = bload32(rgs, so + u * su_step);
+    r.su[u] = bload32(rus, so + u * su_step);
   }
 }
 
@@ -1825,7 +1831,7 @@ __device__ __forceinline__ void gu_issue_blk(const DecodeArgs& a, const BlkItem&
 // comes from the staged block at s_x + t * kXRow. Unrolled over the block
 // (no loop-carried store, so the waits for this item's weights do not also
 // wait for the next item's).
-template <int TB, class Tab>
+template <int TB, bool NV, class Tab>
 __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkItem& d,
                                                const Tab& s_rt, const GuRegs& r,
                                                const uint4* s_x) {
@@ -1847,8 +1853,15 @@ __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkIte
   for (int u = 0; u < kGuU; ++u) {
     const int c = kGuLanes * u + j;
     if (c < kc) {
-      const float fg = e8m0_to_f32(__builtin_amdgcn_ubfe(r.sg[u], sh, 8));
-      const float fu = e8m0_to_f32(__builtin_amdgcn_ubfe(r.su[u], sh, 8));
+      // MXFP4: one scale per chunk; NVFP4: one per 16-code half (.x, .y)
+      f32x2_t fg, fu;
+      if constexpr (NV) {
+        fg = nv_scale_pair(r.sg[u], 16u * (j & 1));
+        fu = nv_scale_pair(r.su[u], 16u * (j & 1));
+      } else {
+        fg.x = fg.y = e8m0_to_f32(__builtin_amdgcn_ubfe(r.sg[u], sh, 8));
+        fu.x = fu.y = e8m0_to_f32(__builtin_amdgcn_ubfe(r.su[u], sh, 8));
+      }
       const uint32_t gw[4] = {r.g[u].x, r.g[u].y, r.g[u].z, r.g[u].w};
       const uint32_t uw[4] = {r.u[u].x, r.u[u].y, r.u[u].z, r.u[u].w};
       bf16x2_t wg[16], wu[16];
@@ -1867,27 +1880,43 @@ __device__ __forceinline__ void gu_compute_blk(const DecodeArgs& a, const BlkIte
       for (int i = 0; i < TB; ++i) {
         if (i < d.m) {
           const uint4* xv = xt[i] + c;
-          float pg = 0.0f, pu = 0.0f;
+          float pg[2] = {0.0f, 0.0f}, pu[2] = {0.0f, 0.0f};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint4 xq = xv[q * P];
             const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+            const int hf = NV ? q >> 1 : 0;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-              pg = __builtin_amdgcn_fdot2_f32_bf16(wg[4 * q + p], as_bf16x2(xw[p]), pg, false);
-              pu = __builtin_amdgcn_fdot2_f32_bf16(wu[4 * q + p], as_bf16x2(xw[p]), pu, false);
+              pg[hf] = __builtin_amdgcn_fdot2_f32_bf16(wg[4 * q + p], as_bf16x2(xw[p]), pg[hf], false);
+              pu[hf] = __builtin_amdgcn_fdot2_f32_bf16(wu[4 * q + p], as_bf16x2(xw[p]), pu[hf], false);
             }
           }
-          ag[i] = fmaf(pg, fg, ag[i]);
-          au[i] = fmaf(pu, fu, au[i]);
+          if constexpr (NV) {
+            ag[i] = fmaf(pg[1], fg.y, fmaf(pg[0], fg.x, ag[i]));
+            au[i] = fmaf(pu[1], fu.y, fmaf(pu[0], fu.x, au[i]));
+          } else {
+            ag[i] = fmaf(pg[0], fg.x, ag[i]);
+            au[i] = fmaf(pu[0], fu.x, au[i]);
+          }
         }
       }
     }
   }
+  float mg = 1.0f, mu = 1.0f;  // NVFP4 matrix scales, applied to the row sums
+  if constexpr (NV) {
+    const BankView& bv = d.e < 0 ? a.shared : a.routed;
+    mg = nv_matrix_scale(bv, max(d.e, 0), 0);
+    mu = nv_matrix_scale(bv, max(d.e, 0), 1);
+  }
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     if (i < d.m) {
-      const float g = group_sum<kGuLanes>(ag[i]), u = group_sum<kGuLanes>(au[i]);
+      float g = group_sum<kGuLanes>(ag[i]), u = group_sum<kGuLanes>(au[i]);
+      if constexpr (NV) {
+        g *= mg;
+        u *= mu;
+      }
       if (j == 0 && n < a.I) a.h[(size_t)(d.row0 + i) * a.I + n] = silu_mul(g, u);
     }
   }
@@ -1947,20 +1976,21 @@ __device__ __forceinline__ void stage_block_rows(const DecodeArgs& a, uint4* s_x
 
 // Streams gate/up items b, b + G, ... < n (item numbering of blk_item with
 // n_sh shared items first) with two register buffers.
-template <int TB, class Tab>
+template <int TB, bool NV, class Tab>
 __device__ __forceinline__ void gateup_block_items(const DecodeArgs& a, const Tab& s_tab,
                                                    const Tab& s_rt, const uint4* s_x, int n_sh,
                                                    int n, int b, int G) {
   // fixed trip over pairs of items; padding issues read nothing
   const int mine = b < n ? (n - b + G - 1) / G : 0;
   GuRegs A, B;
-  gu_issue_blk(a, blk_item<TB>(a, s_tab, n_sh, b < n ? b : 0, a.gu_items, true), A, b < n);
+  auto item = [&](int it) { return blk_item<TB, NV>(a, s_tab, n_sh, it, a.gu_items, true); };
+  gu_issue_blk<NV>(a, item(b < n ? b : 0), A, b < n);
   for (int kk = 0; kk < mine; kk += 2) {
     const int i0 = b + kk * G, i1 = i0 + G, i2 = i1 + G;
-    gu_issue_blk(a, blk_item<TB>(a, s_tab, n_sh, i1 < n ? i1 : i0, a.gu_items, true), B, i1 < n);
-    gu_compute_blk<TB>(a, blk_item<TB>(a, s_tab, n_sh, i0, a.gu_items, true), s_rt, A, s_x);
-    gu_issue_blk(a, blk_item<TB>(a, s_tab, n_sh, i2 < n ? i2 : i0, a.gu_items, true), A, i2 < n);
-    if (i1 < n) gu_compute_blk<TB>(a, blk_item<TB>(a, s_tab, n_sh, i1, a.gu_items, true), s_rt, B, s_x);
+    gu_issue_blk<NV>(a, item(i1 < n ? i1 : i0), B, i1 < n);
+    gu_compute_blk<TB, NV>(a, item(i0), s_rt, A, s_x);
+    gu_issue_blk<NV>(a, item(i2 < n ? i2 : i0), A, i2 < n);
+    if (i1 < n) gu_compute_blk<TB, NV>(a, item(i1), s_rt, B, s_x);
   }
 }
 
@@ -2104,7 +2134,7 @@ __device__ void fp8_shared_down_blk(const DecodeArgs& a, int c, f32x4_t* s_h) {
 // Block launch 1: [router rows | the routing workgroup | n_sw workgroups
 // streaming the shared expert's gate/up items (MXFP4 or FP8), which need no
 // routing and use the bandwidth the router and the routing leave idle].
-template <int TB>
+template <int TB, bool NV>
 __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int n_sw) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x;
@@ -2121,8 +2151,8 @@ __global__ __launch_bounds__(kThreads) void route_block_kernel(DecodeArgs a, int
     stage_block_rows(a, s_x);
     __syncthreads();
     const int* none = nullptr;
-    gateup_block_items<TB>(a, none, none, s_x, a.gu_items, a.gu_items, b - a.nb_router - 1,
-                           n_sw);
+    gateup_block_items<TB, NV>(a, none, none, s_x, a.gu_items, a.gu_items, b - a.nb_router - 1,
+                               n_sw);
   }
 }
 
@@ -2131,20 +2161,23 @@ struct DnW {
   uint32_t sc[kDnU];
 };
 
+// NV: chunk j + 8 u's two scale bytes are half j % 2 of the word at
+// 4 (j / 2) + 16 u of the row's I / 16.
+template <bool NV>
 __device__ __forceinline__ void dn_issue_blk(const DecodeArgs& a, const BlkItem& d, DnW& r,
                                              bool live) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int j = lane & 7;
   const int nr = min(d.rb * kDnRows + wave * 8 + (lane >> 3), a.H - 1);
-  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> (NV ? 4 : 5);
   live = __builtin_amdgcn_readfirstlane((int)live) != 0;
   const __amdgpu_buffer_rsrc_t rd = matrix_rsrc(uniform_ptr(d.codes), live ? a.H * crow : 0u);
   const __amdgpu_buffer_rsrc_t rds = matrix_rsrc(uniform_ptr(d.scales), live ? a.H * srow : 0u);
-  const int co = nr * crow + j * 16, so = nr * srow + 4 * (j >> 2);
+  const int co = nr * crow + j * 16, so = nr * srow + (NV ? 4 * (j >> 1) : 4 * (j >> 2));
 #pragma unroll
   for (int u = 0; u < kDnU; ++u) {
     r.w[u] = bload16(rd, co + u * 8 * 16);
-    r.sc[u] = bload32(rds, so + u * 8);
+    r.sc[u] = bload32(rds, so + u * (NV ? 16 : 8));
   }
 }
 
@@ -2188,7 +2221,7 @@ __device__ __forceinline__ void dn_copy_h(const DecodeArgs& a, const BlkItem& d,
 // for the combine in this launch. `fresh`: the slot's h rows were just
 // copied (before the kDnIssueLoads loads of the next item's weights), so
 // wait for the copies and make them visible to every wave first.
-template <int TB>
+template <int TB, bool NV>
 __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkItem& d, bool fresh,
                                                const DnW& r, const f32x4_t* s_h) {
   if (fresh) {
@@ -2209,7 +2242,11 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
   for (int u = 0; u < kDnU; ++u) {
     const int ch = 8 * u + j;
     if (ch < kc) {
-      const float fd = e8m0_to_f32(__builtin_amdgcn_ubfe(r.sc[u], sh, 8));
+      f32x2_t fd;  // MXFP4: one scale per chunk; NVFP4: one per 16-code half
+      if constexpr (NV)
+        fd = nv_scale_pair(r.sc[u], 16u * (j & 1));
+      else
+        fd.x = fd.y = e8m0_to_f32(__builtin_amdgcn_ubfe(r.sc[u], sh, 8));
       const uint32_t ww[4] = {r.w[u].x, r.w[u].y, r.w[u].z, r.w[u].w};
       f32x2_t wf[16];
 #pragma unroll
@@ -2223,28 +2260,35 @@ __device__ __forceinline__ void dn_compute_blk(const DecodeArgs& a, const BlkIte
       for (int i = 0; i < TB; ++i) {
         if (i < d.m) {
           const f32x4_t* hv = s_h + i * kHRow + ch;
-          float pd = 0.0f;
+          float pd[2] = {0.0f, 0.0f};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4_t ha = hv[2 * q * P], hb = hv[(2 * q + 1) * P];
-            pd = fmaf(wf[4 * q + 0].x, ha.x, pd);
-            pd = fmaf(wf[4 * q + 0].y, ha.y, pd);
-            pd = fmaf(wf[4 * q + 1].x, ha.z, pd);
-            pd = fmaf(wf[4 * q + 1].y, ha.w, pd);
-            pd = fmaf(wf[4 * q + 2].x, hb.x, pd);
-            pd = fmaf(wf[4 * q + 2].y, hb.y, pd);
-            pd = fmaf(wf[4 * q + 3].x, hb.z, pd);
-            pd = fmaf(wf[4 * q + 3].y, hb.w, pd);
+            const int hf = NV ? q >> 1 : 0;
+            pd[hf] = fmaf(wf[4 * q + 0].x, ha.x, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 0].y, ha.y, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 1].x, ha.z, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 1].y, ha.w, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 2].x, hb.x, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 2].y, hb.y, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 3].x, hb.z, pd[hf]);
+            pd[hf] = fmaf(wf[4 * q + 3].y, hb.w, pd[hf]);
           }
-          acc[i] = fmaf(pd, fd, acc[i]);
+          if constexpr (NV)
+            acc[i] = fmaf(pd[1], fd.y, fmaf(pd[0], fd.x, acc[i]));
+          else
+            acc[i] = fmaf(pd[0], fd.x, acc[i]);
         }
       }
     }
   }
+  float md = 1.0f;
+  if constexpr (NV) md = nv_matrix_scale(d.e < 0 ? a.shared : a.routed, max(d.e, 0), 2);
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     if (i < d.m) {
-      const float v = group_sum<8>(acc[i]);
+      float v = group_sum<8>(acc[i]);
+      if constexpr (NV) v *= md;
       if (j == 0 && n < a.H) cst(a.y + (size_t)(d.row0 + i) * a.H + n, v);
     }
   }
@@ -2278,50 +2322,78 @@ constexpr int kMfSup = 18;    // super-steps of 128 K (I <= 2304)
 constexpr int kMfRowBytes = kMfSup * 256 + 16;
 constexpr int kMfLds = 16 * kMfRowBytes + 4 * 256 * 4;  // rows + a 16 x 16 tile per wave
 
-// One item's weights for a lane: 23 vector loads, so that two buffers stay
-// under the 63 loads a wave can have in flight.
+// One item's weights for a lane: 23 vector loads (NVFP4: 27), so that two
+// buffers stay under the 63 loads a wave can have in flight.
 constexpr int kMfScl = (kMfSup * 4 + 15) / 16;  // 16-byte loads of a row's scales
+template <bool NV>
 struct MfW {
-  uint4 c[kMfSup];     // codes of K range [128 S + 32 g, + 32)
-  uint4 sc[kMfScl];    // the row's scale bytes: block b at byte b % 16 of sc[b / 16]
+  uint4 c[kMfSup];  // codes of super-step S
+  uint4 sc[kMfScl];  // the row's scale bytes: block b at byte b % 16 of sc[b / 16]
+};
+template <>
+struct MfW<true> {
+  uint4 c[kMfSup];
+  uint32_t sc[kMfSup / 2];  // the lane group's scale bytes of super-steps 2 S', 2 S' + 1
 };
 
 // Item `it` of the routed slots: slot it / per, 64-row group it % per.
 struct MfItem {
   const uint8_t* codes;
   const uint8_t* scales;
-  int rg, row0, m;
+  int rg, row0, m, e;
 };
+template <bool NV>
 __device__ __forceinline__ MfItem mf_item(const DecodeArgs& a, const LaneTable& tab, int it,
                                           int per) {
   const int sl = it / per, rg = it - sl * per;
   const int e = __builtin_amdgcn_readfirstlane(min(max(tab[1 + sl], 0), a.routed.E - 1));
   const int row0 = min(max(tab[1 + a.max_slots + sl], 0), a.R);
   const int m = min(max(tab[1 + 2 * a.max_slots + sl], 0), min(a.R - row0, 8));
-  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> (NV ? 4 : 5);
   return MfItem{a.routed.d_codes + (size_t)e * a.H * crow,
-                a.routed.d_scales + (size_t)e * a.H * srow, rg, row0, m};
+                a.routed.d_scales + (size_t)e * a.H * srow, rg, row0, m, e};
 }
 
-__device__ __forceinline__ void mf_issue(const DecodeArgs& a, const MfItem& d, MfW& r, bool live) {
+// NVFP4 banks (one E4M3 scale per 16 codes, 36 words a row at I = 2304)
+// take another K order, so that a lane's scales of two super-steps are one
+// word: lane group g's 32 K values of super-step S = 2 S' + p are block
+// 8 S' + 2 g + p of 32, whose four scale bytes (p = 0, 1; MFMA steps 0-1 and
+// 2-3) are word 4 S' + g of the row. The code loads of S and S + 1 then
+// read one 128-byte span of each row. Needs an even number of super-steps
+// (I % 256 == 0).
+
+template <bool NV>
+__device__ __forceinline__ void mf_issue(const DecodeArgs& a, const MfItem& d, MfW<NV>& r,
+                                         bool live) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4;
   const int row = min(d.rg * kMfRows + wave * 16 + (lane & 15), a.H - 1);
-  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> 5;
+  const uint32_t crow = (uint32_t)a.I >> 1, srow = (uint32_t)a.I >> (NV ? 4 : 5);
   live = __builtin_amdgcn_readfirstlane((int)live) != 0;
   const __amdgpu_buffer_rsrc_t rc = matrix_rsrc(uniform_ptr(d.codes), live ? a.H * crow : 0u);
   const __amdgpu_buffer_rsrc_t rs = matrix_rsrc(uniform_ptr(d.scales), live ? a.H * srow : 0u);
   const int nsup = a.I >> 7;
+  if constexpr (NV) {
+    const int cg = row * crow + g * 32, sg = row * srow + g * 4;
 #pragma unroll
-  for (int S = 0; S < kMfSup; ++S) {
-    // super-steps past the row's K read nothing (an offset past the resource
-    // returns zeros)
-    r.c[S] = bload16(rc, S < nsup ? row * crow + S * 64 + g * 16 : 0x7ffffff0);
+    for (int S = 0; S < kMfSup; ++S)
+      r.c[S] = bload16(rc, S < nsup ? cg + (S >> 1) * 128 + (S & 1) * 16 : 0x7ffffff0);
+#pragma unroll
+    for (int j = 0; j < kMfSup / 2; ++j)
+      r.sc[j] = bload32(rs, 2 * j < nsup ? sg + 16 * j : 0x7ffffff0);
+  } else {
+#pragma unroll
+    for (int S = 0; S < kMfSup; ++S) {
+      // super-steps past the row's K read nothing (an offset past the
+      // resource returns zeros)
+      r.c[S] = bload16(rc, S < nsup ? row * crow + S * 64 + g * 16 : 0x7ffffff0);
+    }
+    // the row's I / 32 scale bytes (the last load may run into the next
+    // row, or past the resource, which returns zeros; those bytes are not
+    // used)
+#pragma unroll
+    for (int j = 0; j < kMfScl; ++j)
+      r.sc[j] = bload16(rs, 16 * j < (int)srow ? row * srow + 16 * j : 0x7ffffff0);
   }
-  // the row's I / 32 scale bytes (the last load may run into the next row,
-  // or past the resource, which returns zeros; those bytes are not used)
-#pragma unroll
-  for (int j = 0; j < kMfScl; ++j)
-    r.sc[j] = bload16(rs, 16 * j < (int)srow ? row * srow + 16 * j : 0x7ffffff0);
 }
 
 // Parts of each h value a slot of m tokens carries: three bf16 (exact) up
@@ -2365,13 +2437,17 @@ __device__ __forceinline__ void mf_stage_h(const DecodeArgs& a, int row0, int m,
 
 // One item: 16 weight rows per wave against the staged (token, part) rows,
 // then y[row0 + t] for the item's rows, t < m.
-__device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d, const MfW& r,
-                                           const char* s_a, int rs, float* s_c) {
+template <bool NV>
+__device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
+                                           const MfW<NV>& r, const char* s_a, int rs,
+                                           float* s_c) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, ar = lane & 15;
   const int nsup = a.I >> 7;
   const int P = mf_parts(d.m);
   const bool arow = ar < P * d.m;
-  const char* arow_p = s_a + ar * rs + g * 64;
+  // A: K of super-step S for lane group g at 128 S + 32 g (NVFP4, S = 2 S' + p:
+  // 256 S' + 64 g + 32 p)
+  const char* arow_p = s_a + ar * rs + (NV ? g * 128 : g * 64);
   // two accumulators (steps 0, 2 and 1, 3 of each super-step), and the
   // super-step's four A fragments read together: the MFMAs do not wait on
   // one another, nor each on its own LDS read
@@ -2382,19 +2458,38 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
       uint4 av[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        av[q] = arow ? *reinterpret_cast<const uint4*>(arow_p + S * 256 + q * 16)
+        av[q] = arow ? *reinterpret_cast<const uint4*>(
+                           arow_p + (NV ? (S >> 1) * 512 + (S & 1) * 64 : S * 256) + q * 16)
                      : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 sv = r.sc[S >> 2];
-      const uint32_t sw = (S & 3) == 0 ? sv.x : (S & 3) == 1 ? sv.y : (S & 3) == 2 ? sv.z : sv.w;
-      const float sc = e8m0_to_f32(__builtin_amdgcn_ubfe(sw, 8u * g, 8));
       const uint32_t w[4] = {r.c[S].x, r.c[S].y, r.c[S].z, r.c[S].w};
+      float sc = 0.0f;
+      f32x2_t sn = {0.0f, 0.0f};
+      if constexpr (NV) {
+        sn = nv_scale_pair(r.sc[S >> 1], 16u * (S & 1));
+      } else {
+        const uint4 sv = r.sc[S >> 2];
+        const uint32_t sw = (S & 3) == 0 ? sv.x : (S & 3) == 1 ? sv.y : (S & 3) == 2 ? sv.z : sv.w;
+        sc = e8m0_to_f32(__builtin_amdgcn_ubfe(sw, 8u * g, 8));
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0);
-        const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1);
-        const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2);
-        const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3);
-        const bf16x8_t b = bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+        bf16x8_t b;
+        if constexpr (NV) {
+          // the scaled conversion applies only a power of two: convert, then
+          // multiply by the E4M3 scale in fp32 (E2M1 x E4M3 is exact in bf16)
+          const float s2 = q < 2 ? sn.x : sn.y;
+          const f32x2_t f0 = fp4x2_to_f32<0>(w[q]), f1 = fp4x2_to_f32<1>(w[q]);
+          const f32x2_t f2 = fp4x2_to_f32<2>(w[q]), f3 = fp4x2_to_f32<3>(w[q]);
+          b = bf16x8_t{(__bf16)(f0.x * s2), (__bf16)(f0.y * s2), (__bf16)(f1.x * s2),
+                       (__bf16)(f1.y * s2), (__bf16)(f2.x * s2), (__bf16)(f2.y * s2),
+                       (__bf16)(f3.x * s2), (__bf16)(f3.y * s2)};
+        } else {
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1);
+          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2);
+          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3);
+          b = bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+        }
         if (q & 1)
           c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[q]), b, c1,
                                                         0, 0, 0);
@@ -2412,9 +2507,11 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
   for (int i = 0; i < 4; ++i) cw[(4 * g + i) * 16 + ar] = c[i];
   __builtin_amdgcn_wave_barrier();
   const int n = d.rg * kMfRows + wave * 16 + ar;
+  const float md = NV ? nv_matrix_scale(a.routed, d.e, 2) : 1.0f;
   for (int t = g; t < d.m; t += 4) {
     float v = cw[(P * t) * 16 + ar] + cw[(P * t + 1) * 16 + ar];
     if (P == 3) v += cw[(P * t + 2) * 16 + ar];
+    if (NV) v *= md;
     if (n < a.H) a.y[(size_t)(d.row0 + t) * a.H + n] = v;
   }
 }
@@ -2423,6 +2520,7 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
 // items slot-major, workgroup b taking the contiguous stretch
 // [n b / G, n (b + 1) / G) with two register buffers for the weights; the
 // slot's h parts are staged when an item's slot differs from the staged one.
+template <bool NV>
 __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs a, int G) {
   __shared__ __align__(16) char lds[kMfLds];
   constexpr int rs = kMfRowBytes;
@@ -2438,23 +2536,24 @@ __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs
   if (lo >= hi) return;
   int staged = -1;
   auto restage = [&](int it) {
-    const MfItem d = mf_item(a, tab, it, per);
+    const MfItem d = mf_item<NV>(a, tab, it, per);
     __syncthreads();  // every wave is done with the staged rows
     mf_stage_h(a, d.row0, d.m, s_a, rs);
     __syncthreads();
     staged = it / per;
   };
-  MfW A, B;
-  mf_issue(a, mf_item(a, tab, lo, per), A, true);
+  MfW<NV> A, B;
+  auto item = [&](int it) { return mf_item<NV>(a, tab, it, per); };
+  mf_issue<NV>(a, item(lo), A, true);
   restage(lo);
   for (int i0 = lo; i0 < hi; i0 += 2) {
     const int i1 = i0 + 1, i2 = i0 + 2;
-    mf_issue(a, mf_item(a, tab, i1 < hi ? i1 : i0, per), B, i1 < hi);
-    mf_compute(a, mf_item(a, tab, i0, per), A, s_a, rs, s_c);
+    mf_issue<NV>(a, item(i1 < hi ? i1 : i0), B, i1 < hi);
+    mf_compute<NV>(a, item(i0), A, s_a, rs, s_c);
     if (i1 < hi && i1 / per != staged) restage(i1);
-    mf_issue(a, mf_item(a, tab, i2 < hi ? i2 : i0, per), A, i2 < hi);
+    mf_issue<NV>(a, item(i2 < hi ? i2 : i0), A, i2 < hi);
     if (i1 < hi) {
-      mf_compute(a, mf_item(a, tab, i1, per), B, s_a, rs, s_c);
+      mf_compute<NV>(a, item(i1), B, s_a, rs, s_c);
       if (i2 < hi && i2 / per != staged) restage(i2);
     }
   }
@@ -2465,7 +2564,7 @@ __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs
 // last n_sd workgroups of the grid each take one 32-row group of the shared
 // expert's down rows (MXFP4 or FP8; its h rows came from the previous
 // launch); dispatched last, they run in the tail of the routed stream.
-template <int TB>
+template <int TB, bool NV>
 __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a, int G) {
   extern __shared__ __align__(16) char lds[];
   if ((int)blockIdx.x >= G) {
@@ -2474,13 +2573,14 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
       return;
     }
     const int* none = nullptr;
-    const BlkItem d = blk_item<TB>(a, none, a.dn_items, (int)blockIdx.x - G, a.dn_items, false);
+    const BlkItem d =
+        blk_item<TB, NV>(a, none, a.dn_items, (int)blockIdx.x - G, a.dn_items, false);
     DnW A;
-    dn_issue_blk(a, d, A, true);
+    dn_issue_blk<NV>(a, d, A, true);
     dn_copy_h(a, d, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the weights and the copies
     __syncthreads();
-    dn_compute_blk<TB>(a, d, false, A, reinterpret_cast<const f32x4_t*>(lds));
+    dn_compute_blk<TB, NV>(a, d, false, A, reinterpret_cast<const f32x4_t*>(lds));
     return;
   }
   uint4* s_x = reinterpret_cast<uint4*>(lds);
@@ -2495,7 +2595,7 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
     for (int i = threadIdx.x; i < a.R; i += kThreads) s_rt[i] = a.row_token[i];
     __syncthreads();
     const int ns = min(max(s_tab[0], 0), a.max_slots);
-    gateup_block_items<TB>(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
+    gateup_block_items<TB, NV>(a, s_tab, s_rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
   } else {
     // LDS holds only the T token rows (at most 80 KB: two workgroups a CU);
     // the slot table and row map ride in registers across each wave's lanes
@@ -2504,7 +2604,7 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
     rt.load(a.row_token, a.R);
     __syncthreads();
     const int ns = min(max(tab[0], 0), a.max_slots);
-    gateup_block_items<TB>(a, tab, rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
+    gateup_block_items<TB, NV>(a, tab, rt, s_x, 0, ns * a.gu_items, blockIdx.x, G);
   }
 }
 
@@ -2702,27 +2802,27 @@ int resident_grid(uint32_t lds_bytes) {
   return cu_count() * (by_lds < 3 ? (by_lds < 1 ? 1 : by_lds) : 3);
 }
 
-template <int TB>
+template <int TB, bool NV>
 void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch& d, bool shared,
                   hipStream_t s) {
   const uint32_t lds_x = (uint32_t)(d.T * kXRow * 16);
   const uint32_t lds_rt = lds_x > (uint32_t)kLdsBytes ? lds_x : (uint32_t)kLdsBytes;
   const int n_sw = shared ? (L.gu_items < 256 ? L.gu_items : 256) : 0;
-  launch("route_block_kernel", route_block_kernel<TB>, dim3(L.nb_router + 1 + n_sw),
+  launch("route_block_kernel", route_block_kernel<TB, NV>, dim3(L.nb_router + 1 + n_sw),
          dim3(kThreads), lds_rt, s, a, n_sw);
   const uint32_t lds_gu =
       lds_x + (TB <= 5 ? (uint32_t)(sizeof(int) * (1 + 3 * L.max_slots + d.R)) : 0u);
   const int ng = L.max_slots * L.gu_items, rg = resident_grid(lds_gu);
   const int gg = ng < rg ? ng : rg;
   const int n_sd = shared ? L.dn_items : 0;
-  launch("gateup_block_kernel", gateup_block_kernel<TB>, dim3(gg + n_sd), dim3(kThreads), lds_gu,
+  launch("gateup_block_kernel", gateup_block_kernel<TB, NV>, dim3(gg + n_sd), dim3(kThreads), lds_gu,
          s, a, gg);
   {
     // on the matrix cores: 16 staged rows of bf16 h parts and a 16 x 16
     // fp32 tile per wave (76 KB of LDS); two workgroups a CU
     const int nd = L.max_slots * ((d.H + kMfRows - 1) / kMfRows), rd = 2 * cu_count();
     const int gd = nd < rd ? nd : rd;
-    launch("down_block_mfma_kernel", down_block_mfma_kernel, dim3(gd), dim3(kThreads), 0, s, a,
+    launch("down_block_mfma_kernel", down_block_mfma_kernel<NV>, dim3(gd), dim3(kThreads), 0, s, a,
            gd);
   }
   launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
@@ -2742,13 +2842,14 @@ static bool block_path(const DecodeLaunch& d, const DecodeLayout& L) {
   return d.T >= 2 && d.T <= kBlockT && d.ffn_mode == 0 && (d.H >> 5) <= kGuLanes * kGuU &&
          d.H % 128 == 0 && d.I % 128 == 0 && (d.I >> 5) <= 8 * kDnU && d.E <= 16 * kWave &&
          1 + 3 * L.max_slots <= LaneTable::kMax && d.R <= LaneTable::kMax &&
-         d.T * (d.H >> 3) <= kBlockXLoads * kThreads;
+         d.T * (d.H >> 3) <= kBlockXLoads * kThreads &&
+         (d.routed.codec != kCodecNvfp4 || d.I % 256 == 0);  // NVFP4 down: word-aligned scales
 }
 
 bool decode_fuses_nvfp4(const DecodeLaunch& d) {
-  if (d.ffn_mode != 0 || d.T != 1) return false;
+  if (d.ffn_mode != 0) return false;
   const DecodeLayout L = layout(d.T, d.H, d.I, d.E, d.k, d.R, false, d.has_shared);
-  return stream_path(d, L);
+  return d.T == 1 ? stream_path(d, L) : block_path(d, L);
 }
 
 bool decode_fuses_fp8_shared(const DecodeLaunch& d) {
@@ -2837,10 +2938,11 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   // A block of 2..8 tokens: router + routing, then the streaming gate/up
   // and down launches over the union of the block's experts.
   if (block_path(d, L)) {
+    const bool nv = d.routed.codec == kCodecNvfp4;
     if (d.T <= 5)
-      launch_block<5>(a, L, d, shared, s);
+      (nv ? launch_block<5, true> : launch_block<5, false>)(a, L, d, shared, s);
     else
-      launch_block<8>(a, L, d, shared, s);
+      (nv ? launch_block<8, true> : launch_block<8, false>)(a, L, d, shared, s);
     return;
   }
   if (one)

@@ -134,17 +134,54 @@ def _selected(w, x, wr):
 
 
 FUSED = ["gateup_fused_kernel"]
+BLOCK = ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
+         "combine_block_kernel"]
 
 
-@pytest.mark.parametrize("name", ["decode", "spec5"])
-def test_layer_real_shape_few_tokens(name):
-    # one token takes the fused launches with NVFP4 items; more tokens the
-    # separate ones
+@pytest.mark.parametrize("name,T", [("decode", 1), ("spec5", 2), ("spec5", 5), ("spec5", 8),
+                                    ("spec5", 9)])
+def test_layer_real_shape_few_tokens(name, T):
+    # one token takes the fused launch with NVFP4 items, a block of 2..8
+    # tokens the block launches (down on the matrix cores), more tokens the
+    # three-launch chain
     w = S.get(name)
+    x = S.gen_tokens(w, 0, T=T) if T != w.T else S.gen_tokens(w, 0)
+    wT = S.Workload(w.name, w.cfg_id, T=T, H=w.H, E=w.E, k=w.k, I=w.I, exp_lo=w.exp_lo,
+                    exp_hi=w.exp_hi)
+    wr = S.gen_router(w, 0)
+    routed = S.gen_nvfp4_bank(w, 0, experts=_selected(wT, x, wr))
+    assert _parity(wT, x, wr, None, routed, S.gen_nvfp4_bank(w, 0, shared=True)) < 1e-4
+    names = _names()
+    if T == 1:
+        assert names == FUSED
+    elif T <= 8:
+        assert names == BLOCK
+    else:
+        assert "gateup_block_kernel" not in names
+
+
+# blocks of tokens at shapes where the item counts, the tokens per block
+# (the 5- and the 8-token builds) and the rows per slot differ from the real
+# shape's; I = 384 is not a multiple of 256 and leaves the block launches
+BLOCK_NV = [
+    S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_small7", 97, T=7, H=512, E=32, k=2, I=256, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_wide8", 98, T=8, H=2048, E=128, k=8, I=768, exp_lo=-6, exp_hi=-3),
+    S.Workload("blk_i384", 99, T=4, H=512, E=32, k=4, I=384, exp_lo=-6, exp_hi=-3),
+]
+
+
+@pytest.mark.parametrize("w", BLOCK_NV, ids=lambda w: w.name)
+@pytest.mark.parametrize("shared", [True, False], ids=["shared", "no_shared"])
+def test_layer_block_launches(w, shared):
     x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
-    routed = S.gen_nvfp4_bank(w, 0, experts=_selected(w, x, wr))
-    assert _parity(w, x, wr, None, routed, S.gen_nvfp4_bank(w, 0, shared=True)) < 1e-4
-    assert (_names() == FUSED) == (w.T == 1)
+    sh = S.gen_nvfp4_bank(w, 0, shared=True) if shared else None
+    bias = None if shared else np.linspace(-1, 1, w.E).astype(np.float32)
+    assert _parity(w, x, wr, bias, S.gen_nvfp4_bank(w, 0), sh) < 1e-4
+    if w.I % 256 == 0:
+        assert _names() == BLOCK
+    else:
+        assert "down_block_mfma_kernel" not in _names()
 
 
 ONE_TOKEN_NV = [
