@@ -364,62 +364,42 @@ __device__ __forceinline__ uint64_t wave_max_key_f64(uint64_t k) {
 // keys (one v_max_f64 per exchange); lane l holds experts l, l + 64, ...
 // (E <= 64 NK). Weights: softmax over the k chosen logits, summed over
 // j = 0..k-1 in order.
-template <int NK, int NR>
-__device__ void topk_rows_f64(const float (&lv)[NR][NK], int E, int k, int* const* ids,
-                              float* const* w) {
-  // NR rows at once (independent exchanges interleave, so two rows cost
-  // little more than one)
+template <int NK>
+__device__ void topk_row_f64(const float (&lv)[NK], int E, int k, int* ids, float* w) {
   const int lane = lane_id();
-  double key[NR][NK];
+  double key[NK];
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = lane + kWave * i;
-      key[r][i] = __longlong_as_double(e < E ? (long long)topk_key_f64(lv[r][i], e) : 0);
-    }
-  float my_val[NR], top[NR];
-  int my_id[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    my_val[r] = top[r] = 0.0f;
-    my_id[r] = 0;
+  for (int i = 0; i < NK; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = __longlong_as_double(e < E ? (long long)topk_key_f64(lv[i], e) : 0);
   }
+  float my_val = 0.0f, top = 0.0f;
+  int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t win[NR];
+    double best = key[0];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      double best = key[r][0];
+    for (int i = 1; i < NK; ++i) best = fmax(best, key[i]);
+    const uint64_t win = wave_max_key_f64((uint64_t)__double_as_longlong(best));
+    const uint32_t id = 0x7fffffffu - (uint32_t)(win & 0x7fffffffu);
+    uint32_t bits = (uint32_t)(win >> 31);
+    bits = (bits & 0x80000000u) ? (bits & 0x7fffffffu) : ~bits;
+    const float val = __uint_as_float(bits);
 #pragma unroll
-      for (int i = 1; i < NK; ++i) best = fmax(best, key[r][i]);
-      win[r] = wave_max_key_f64((uint64_t)__double_as_longlong(best));
+    for (int i = 0; i < NK; ++i)
+      if ((uint64_t)__double_as_longlong(key[i]) == win) key[i] = 0.0;
+    if (lane == j) {
+      my_val = val;
+      my_id = (int)min(id, (uint32_t)(E - 1));
     }
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint32_t id = 0x7fffffffu - (uint32_t)(win[r] & 0x7fffffffu);
-      uint32_t bits = (uint32_t)(win[r] >> 31);
-      bits = (bits & 0x80000000u) ? (bits & 0x7fffffffu) : ~bits;
-      const float val = __uint_as_float(bits);
-#pragma unroll
-      for (int i = 0; i < NK; ++i)
-        if ((uint64_t)__double_as_longlong(key[r][i]) == win[r]) key[r][i] = 0.0;
-      if (lane == j) {
-        my_val[r] = val;
-        my_id[r] = (int)min(id, (uint32_t)(E - 1));
-      }
-      if (j == 0) top[r] = val;
-    }
+    if (j == 0) top = val;
   }
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float z = lane < k ? expf(my_val[r] - top[r]) : 0.0f;
-    float zsum = 0.0f;
-    for (int q = 0; q < k; ++q)
-      zsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), q));
-    if (lane < k) {
-      ids[r][lane] = my_id[r];
-      w[r][lane] = z / zsum;
-    }
+  const float z = lane < k ? expf(my_val - top) : 0.0f;
+  float zsum = 0.0f;
+  for (int q = 0; q < k; ++q)
+    zsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z), q));
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = z / zsum;
   }
 }
 
@@ -448,26 +428,14 @@ __device__ __forceinline__ void row_logits(const DecodeArgs& a, int t, float (&l
   }
 }
 
+// Wave w takes tokens w, w + 4, ... one after the other (two tokens' rounds
+// interleaved in one wave measured slower than the same rounds in turn).
 template <int NK, bool TAGGED>
 __device__ void topk_block_rows(const DecodeArgs& a, int* s_ids, float* s_w) {
-  // wave w: token w, and token w + 4 alongside it when there is one
-  const int w = threadIdx.x >> 6;
-  for (int t = w; t < a.T; t += 2 * (kThreads / kWave)) {
-    const int t2 = t + kThreads / kWave;
-    if (t2 < a.T) {
-      float lv[2][NK];
-      row_logits<NK, TAGGED>(a, t, lv[0]);
-      row_logits<NK, TAGGED>(a, t2, lv[1]);
-      int* ids[2] = {s_ids + t * a.k, s_ids + t2 * a.k};
-      float* ws[2] = {s_w + t * a.k, s_w + t2 * a.k};
-      topk_rows_f64<NK, 2>(lv, a.E, a.k, ids, ws);
-    } else {
-      float lv[1][NK];
-      row_logits<NK, TAGGED>(a, t, lv[0]);
-      int* ids[1] = {s_ids + t * a.k};
-      float* ws[1] = {s_w + t * a.k};
-      topk_rows_f64<NK, 1>(lv, a.E, a.k, ids, ws);
-    }
+  for (int t = threadIdx.x >> 6; t < a.T; t += kThreads / kWave) {
+    float lv[NK];
+    row_logits<NK, TAGGED>(a, t, lv);
+    topk_row_f64<NK>(lv, a.E, a.k, s_ids + t * a.k, s_w + t * a.k);
   }
 }
 
@@ -2807,7 +2775,7 @@ void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch
                   hipStream_t s) {
   const uint32_t lds_x = (uint32_t)(d.T * kXRow * 16);
   const uint32_t lds_rt = lds_x > (uint32_t)kLdsBytes ? lds_x : (uint32_t)kLdsBytes;
-  const int n_sw = shared ? (L.gu_items < 256 ? L.gu_items : 256) : 0;
+  const int n_sw = shared ? L.gu_items : 0;  // one item each (at most 288 at I <= 2304)
   launch("route_block_kernel", route_block_kernel<TB, NV>, dim3(L.nb_router + 1 + n_sw),
          dim3(kThreads), lds_rt, s, a, n_sw);
   const uint32_t lds_gu =
