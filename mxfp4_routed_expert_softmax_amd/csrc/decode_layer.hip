@@ -180,6 +180,7 @@ struct DecodeArgs {
   int32_t* tab;        // [1 + 3 * max_slots]: n_slots, expert[], row0[], m[]
   int32_t* row_token;  // [rows]
   int32_t* inv_row;    // [T][k]
+  int32_t* row_pair;   // [R] the choice t k + j each bucket row holds
   float* h;            // [rows][I]
   float* y;            // [rows][H]
   uint64_t* flags;     // [nb_router] router flags (tagged words)
@@ -429,7 +430,9 @@ __device__ __forceinline__ void row_logits(const DecodeArgs& a, int t, float (&l
 }
 
 // Wave w takes tokens w, w + 4, ... one after the other (two tokens' rounds
-// interleaved in one wave measured slower than the same rounds in turn).
+// interleaved in one wave measured slower than the same rounds in turn, and
+// polling both tokens' logits before either selection slower too: the
+// router publishes token w + 4 after token w).
 template <int NK, bool TAGGED>
 __device__ void topk_block_rows(const DecodeArgs& a, int* s_ids, float* s_w) {
   for (int t = threadIdx.x >> 6; t < a.T; t += kThreads / kWave) {
@@ -482,6 +485,7 @@ __device__ void routing(const DecodeArgs& a, char* lds) {
     const int row = less + before;
     a.row_token[row] = p / a.k;
     a.inv_row[p] = row;
+    a.row_pair[row] = p;
     a.route_w[p] = s_w[p];
     if (a.ids_out) a.ids_out[p] = e;
     if (a.w_out) a.w_out[p] = s_w[p];
@@ -1915,6 +1919,9 @@ __device__ void router_rows_blk(const DecodeArgs& a, int b, uint4* s_x) {
     if ((int)threadIdx.x + i * kThreads < total) s_x[threadIdx.x + i * kThreads] = v[i];
   __syncthreads();
   const float bb = a.bias ? a.bias[e] : 0.0f;
+  // token by token, each logit published as soon as it is summed (all the
+  // block's dot products first, then every logit, measured slower: the
+  // routing waves start on the early tokens while the later ones are summed)
   for (int t = 0; t < a.T; ++t) {
     float acc = 0.0f;
 #pragma unroll
@@ -2288,7 +2295,8 @@ constexpr int kMfSup = 18;    // super-steps of 128 K (I <= 2304)
 // bytes per staged row of bf16 h parts, padded so that the 16 rows a
 // fragment read touches fall in distinct LDS banks
 constexpr int kMfRowBytes = kMfSup * 256 + 16;
-constexpr int kMfLds = 16 * kMfRowBytes + 4 * 256 * 4;  // rows + a 16 x 16 tile per wave
+// rows, a 16 x 16 tile per wave, the choice of each bucket row (R <= 256)
+constexpr int kMfLds = 16 * kMfRowBytes + 4 * 256 * 4 + 256 * 4;
 
 // One item's weights for a lane: 23 vector loads (NVFP4: 27), so that two
 // buffers stay under the 63 loads a wave can have in flight.
@@ -2405,10 +2413,12 @@ __device__ __forceinline__ void mf_stage_h(const DecodeArgs& a, int row0, int m,
 
 // One item: 16 weight rows per wave against the staged (token, part) rows,
 // then y[row0 + t] for the item's rows, t < m.
+// y rows go out in choice order (row t k + j: token t's j-th expert), so
+// the combine reads them without the row map.
 template <bool NV>
 __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
                                            const MfW<NV>& r, const char* s_a, int rs,
-                                           float* s_c) {
+                                           float* s_c, const int* s_rp) {
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, ar = lane & 15;
   const int nsup = a.I >> 7;
   const int P = mf_parts(d.m);
@@ -2480,7 +2490,8 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
     float v = cw[(P * t) * 16 + ar] + cw[(P * t + 1) * 16 + ar];
     if (P == 3) v += cw[(P * t + 2) * 16 + ar];
     if (NV) v *= md;
-    if (n < a.H) a.y[(size_t)(d.row0 + t) * a.H + n] = v;
+    const int yr = min(max(s_rp[min(d.row0 + t, a.R - 1)], 0), a.R - 1);
+    if (n < a.H) a.y[(size_t)yr * a.H + n] = v;
   }
 }
 
@@ -2494,6 +2505,8 @@ __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs
   constexpr int rs = kMfRowBytes;
   char* s_a = lds;
   float* s_c = reinterpret_cast<float*>(lds + 16 * rs);
+  int* s_rp = reinterpret_cast<int*>(lds + 16 * rs + 4 * 256 * 4);
+  for (int i = threadIdx.x; i < a.R; i += kThreads) s_rp[i] = a.row_pair[i];  // seen after restage
   LaneTable tab;
   tab.load(a.tab, 1 + 3 * a.max_slots);
   const int ns = min(max(tab[0], 0), a.max_slots);
@@ -2517,11 +2530,11 @@ __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs
   for (int i0 = lo; i0 < hi; i0 += 2) {
     const int i1 = i0 + 1, i2 = i0 + 2;
     mf_issue<NV>(a, item(i1 < hi ? i1 : i0), B, i1 < hi);
-    mf_compute<NV>(a, item(i0), A, s_a, rs, s_c);
+    mf_compute<NV>(a, item(i0), A, s_a, rs, s_c, s_rp);
     if (i1 < hi && i1 / per != staged) restage(i1);
     mf_issue<NV>(a, item(i2 < hi ? i2 : i0), A, i2 < hi);
     if (i1 < hi) {
-      mf_compute<NV>(a, item(i1), B, s_a, rs, s_c);
+      mf_compute<NV>(a, item(i1), B, s_a, rs, s_c, s_rp);
       if (i2 < hi && i2 / per != staged) restage(i2);
     }
   }
@@ -2577,12 +2590,33 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
 }
 
 // Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
-// token in fixed order (shared row, then j = 0..k-1).
+// token in fixed order (shared row, then j = 0..k-1). The routed y rows are
+// in choice order (the down launch wrote them so), so every load is
+// independent of the others: one memory round trip.
 __global__ __launch_bounds__(kThreads) void combine_block_kernel(DecodeArgs a) {
   // every wait of the call ran in the earlier launches; the status read is
   // in flight with the combine's loads, which do not wait on it
   const uint32_t code = call_wait_code(a);
-  combine_column(a, blockIdx.x, code != 0);
+  const int n = blockIdx.x * kDnRows + (threadIdx.x & 31);
+  if (n < a.H) {
+    for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
+      float v = a.y_shared_ext ? a.y_shared_ext[(size_t)t * a.H + n]
+                : a.has_shared ? a.y[(size_t)(a.R + t) * a.H + n] : 0.0f;
+      for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
+        float yv[8], wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = t * a.k + min(j0 + u, a.k - 1);
+          yv[u] = a.y[(size_t)p * a.H + n];
+          wv[u] = a.route_w[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < a.k) v = fmaf(wv[u], yv[u], v);
+      }
+      a.out[(size_t)t * a.H + n] = code != 0 ? __builtin_nanf("") : v;
+    }
+  }
   finish_call(a, code, blockIdx.x, gridDim.x);
 }
 
@@ -2671,8 +2705,8 @@ constexpr long kForcedSpinLimit = 256;
 
 struct DecodeLayout {
   int max_slots, rows, gu_items, dn_items, nb_router;
-  size_t off_wstat, off_flags, off_cnt, off_tab, off_rt, off_inv, off_logits, off_w, off_h, off_y,
-      off_tagged, off_hw, off_yw, bytes;
+  size_t off_wstat, off_flags, off_cnt, off_tab, off_rt, off_inv, off_rp, off_logits, off_w, off_h,
+      off_y, off_tagged, off_hw, off_yw, bytes;
 };
 
 size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -2696,6 +2730,8 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   L.off_rt = o;
   o += al(sizeof(int32_t) * (size_t)L.rows);
   L.off_inv = o;
+  o += al(sizeof(int32_t) * (size_t)R);
+  L.off_rp = o;
   o += al(sizeof(int32_t) * (size_t)R);
   L.off_tagged = o;
   // one token: [2][E] tagged logit halves, kReplicas routing copies, the
@@ -2866,6 +2902,7 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
   a.tab = reinterpret_cast<int32_t*>(w + L.off_tab);
   a.row_token = reinterpret_cast<int32_t*>(w + L.off_rt);
   a.inv_row = reinterpret_cast<int32_t*>(w + L.off_inv);
+  a.row_pair = reinterpret_cast<int32_t*>(w + L.off_rp);
   a.logits = reinterpret_cast<float*>(w + L.off_logits);
   a.route_w = reinterpret_cast<float*>(w + L.off_w);
   a.h = reinterpret_cast<float*>(w + L.off_h);
