@@ -611,11 +611,12 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
             b += H * I + (H // 32) * (I // 32) + T * I * 4 + T * H * 4
         return "hbm", b
     if name in ("down_block_kernel", "down_block_mfma_kernel"):
-        # down of the U routed experts, h rows read, y rows written
-        return "hbm", U * dn_expert + R * I * 4 + R * H * 4
-    if name == "combine_block_kernel":
-        rows = R + (T if shared or shared8 else 0)
-        return "hbm", rows * H * 4 + T * H * 4 + T * w.k * 8
+        # down of the U routed experts, h rows read, y rows written as value
+        # words and read back by the launch's combine workgroups, with the
+        # shared rows; the output rows and the k ids and weights
+        sh_rows = T if shared or shared8 else 0
+        return "hbm", U * dn_expert + R * I * 4 + R * H * 16 + sh_rows * H * 4 + T * H * 4 \
+            + T * w.k * 8
     if name in ("gateup_stream_kernel", "gateup_kernel"):
         # routed gate/up of the U experts (+ the shared expert's down rows)
         b = U * gu_expert + T * H * 2 + R * I * 4

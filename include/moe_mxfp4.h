@@ -170,8 +170,11 @@ int moe_set_kernel_events(hipEvent_t* events, int n);
  *     passed through that wait is NaN (all of `out` if the routing's wait
  *     gave up), and if the routing's wait gave up, `topk_ids_out` is -1 and
  *     `topk_w_out` NaN;
- *   - 2..16 tokens: the call's last launch writes NaN to every element of
- *     `out`, -1 to `topk_ids_out` and NaN to `topk_w_out`.
+ *   - 2..16 tokens: if a wait of an earlier launch gave up, the call's last
+ *     launch writes NaN to every element of `out`, -1 to `topk_ids_out` and
+ *     NaN to `topk_w_out`; a wait of the last launch itself (2..8 tokens:
+ *     its combine's wait for the routed rows) writes NaN to the outputs it
+ *     feeds.
  * This call reads the result recorded in the
  * first 16 bytes of `ws` with a blocking device-to-host copy: synchronise
  * the call's stream first, and pass the same workspace before reusing it.

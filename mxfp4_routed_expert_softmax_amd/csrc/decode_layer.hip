@@ -83,6 +83,7 @@ constexpr uint32_t kWaitLogits = 2;       // routing: tagged logits
 constexpr uint32_t kWaitTable = 3;        // one-token gate/up: routing table copy
 constexpr uint32_t kWaitShared = 4;       // one-token shared down: shared gate/up flags
 constexpr uint32_t kWaitGateup = 5;       // one-token routed down: the slot's gate/up items
+constexpr uint32_t kWaitDown = 6;         // block combine: the routed y words
 // Result word of a few-token call: this magic above the call's 48-bit tag.
 // The call's status is the code of the status word when that word carries
 // the same tag, else OK.
@@ -234,8 +235,8 @@ __device__ __forceinline__ void report_timeout(const DecodeArgs& a, uint32_t cod
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-// A value word of the one-token launch: the low 32 bits of the call's tag
-// above an fp32 value. Like a tagged word, it shows by itself whether it
+// A value word (the one-token launch's h and y, a block's routed y): the
+// low 32 bits of the call's tag above an fp32 value. Like a tagged word, it shows by itself whether it
 // holds this call's value (foreign bytes pass with a chance of 2^-32 per
 // word), so its reader needs no flag and its writer no wait.
 __device__ __forceinline__ uint64_t value_word(const DecodeArgs& a, float v) {
@@ -2413,8 +2414,9 @@ __device__ __forceinline__ void mf_stage_h(const DecodeArgs& a, int row0, int m,
 
 // One item: 16 weight rows per wave against the staged (token, part) rows,
 // then y[row0 + t] for the item's rows, t < m.
-// y rows go out in choice order (row t k + j: token t's j-th expert), so
-// the combine reads them without the row map.
+// y rows go out in choice order (row t k + j: token t's j-th expert), as
+// value words, so the combine workgroups of the launch read them without the
+// row map and without a count: a word carrying the call's tag has landed.
 template <bool NV>
 __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
                                            const MfW<NV>& r, const char* s_a, int rs,
@@ -2491,7 +2493,63 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
     if (P == 3) v += cw[(P * t + 2) * 16 + ar];
     if (NV) v *= md;
     const int yr = min(max(s_rp[min(d.row0 + t, a.R - 1)], 0), a.R - 1);
-    if (n < a.H) a.y[(size_t)yr * a.H + n] = v;
+    if (n < a.H) cst(a.yw + (size_t)yr * a.H + n, value_word(a, v));
+  }
+}
+
+// Block combine, in the down launch after its matrix-core workgroups:
+// workgroup c sums output columns [32 c, 32 c + 32) of every token in fixed
+// order (shared row, then j = 0..k-1). Each wave polls its tokens' k routed
+// y words (choice order, so every load is independent) until all carry the
+// call's tag; dispatched after every down workgroup, it waits only for
+// their last stores to land. On a wait that gave up in an earlier launch
+// (or this one) its columns are NaN; workgroup 0 also writes -1 ids and NaN
+// weights then, and the call's result word.
+__device__ void combine_block_words(const DecodeArgs& a, int c) {
+  const uint32_t code = call_wait_code(a);
+  bool failed = code != 0;
+  const int n = min(c * kDnRows + (int)(threadIdx.x & 31), a.H - 1);
+  const bool col = c * kDnRows + (int)(threadIdx.x & 31) < a.H;
+  for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {  // wave-uniform trip
+    const float base = a.y_shared_ext ? a.y_shared_ext[(size_t)t * a.H + n]
+                       : a.has_shared ? a.y[(size_t)(a.R + t) * a.H + n] : 0.0f;
+    float v = base;
+    for (long it = 0; !failed; ++it) {
+      bool ok = true;
+      v = base;
+      for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
+        uint64_t yv[8];
+        float wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = t * a.k + min(j0 + u, a.k - 1);
+          yv[u] = cld(a.yw + (size_t)p * a.H + n);
+          wv[u] = a.route_w[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < a.k) {
+            ok &= is_mine(a, yv[u]);
+            v = fmaf(wv[u], __uint_as_float((uint32_t)yv[u]), v);
+          }
+      }
+      if (__all(ok)) break;
+      if (it >= kSpinLimit) {
+        if ((threadIdx.x & (kWave - 1)) == 0) report_timeout(a, kWaitDown);
+        failed = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (col) a.out[(size_t)t * a.H + n] = failed ? __builtin_nanf("") : v;
+  }
+  if (c == 0) {
+    if (code)
+      for (int i = threadIdx.x; i < a.R; i += kThreads) {
+        if (a.ids_out) a.ids_out[i] = -1;
+        if (a.w_out) a.w_out[i] = __builtin_nanf("");
+      }
+    if (threadIdx.x == 0) a.wstat[1] = result_word(a);
   }
 }
 
@@ -2502,6 +2560,10 @@ __device__ __forceinline__ void mf_compute(const DecodeArgs& a, const MfItem& d,
 template <bool NV>
 __global__ __launch_bounds__(kThreads, 2) void down_block_mfma_kernel(DecodeArgs a, int G) {
   __shared__ __align__(16) char lds[kMfLds];
+  if ((int)blockIdx.x >= G) {  // the combine workgroups, last in the grid
+    combine_block_words(a, (int)blockIdx.x - G);
+    return;
+  }
   constexpr int rs = kMfRowBytes;
   char* s_a = lds;
   float* s_c = reinterpret_cast<float*>(lds + 16 * rs);
@@ -2589,36 +2651,6 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_block_kernel(DecodeArgs a,
   }
 }
 
-// Block combine: workgroup c sums output columns [32 c, 32 c + 32) of every
-// token in fixed order (shared row, then j = 0..k-1). The routed y rows are
-// in choice order (the down launch wrote them so), so every load is
-// independent of the others: one memory round trip.
-__global__ __launch_bounds__(kThreads) void combine_block_kernel(DecodeArgs a) {
-  // every wait of the call ran in the earlier launches; the status read is
-  // in flight with the combine's loads, which do not wait on it
-  const uint32_t code = call_wait_code(a);
-  const int n = blockIdx.x * kDnRows + (threadIdx.x & 31);
-  if (n < a.H) {
-    for (int t = threadIdx.x >> 5; t < a.T; t += kThreads / 32) {
-      float v = a.y_shared_ext ? a.y_shared_ext[(size_t)t * a.H + n]
-                : a.has_shared ? a.y[(size_t)(a.R + t) * a.H + n] : 0.0f;
-      for (int j0 = 0; j0 < a.k; j0 += 8) {  // 8 rows' loads in flight at a time
-        float yv[8], wv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int p = t * a.k + min(j0 + u, a.k - 1);
-          yv[u] = a.y[(size_t)p * a.H + n];
-          wv[u] = a.route_w[p];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (j0 + u < a.k) v = fmaf(wv[u], yv[u], v);
-      }
-      a.out[(size_t)t * a.H + n] = code != 0 ? __builtin_nanf("") : v;
-    }
-  }
-  finish_call(a, code, blockIdx.x, gridDim.x);
-}
 
 // ---------------------------------------------------------------------------
 // Kernels
@@ -2747,12 +2779,13 @@ DecodeLayout layout(int T, int H, int I, int E, int k, int R, bool ffn, bool sha
   o += al(sizeof(float) * (size_t)L.rows * I);
   L.off_y = o;
   o += al(ffn ? 0 : sizeof(float) * (size_t)L.rows * H);
-  // one token: h and y as value words
+  // one token: h and y as value words; a block: y as value words
   const bool one = T == 1 && !ffn;
+  const bool blk = T >= 2 && T <= kBlockT && !ffn;
   L.off_hw = o;
   o += al(one ? sizeof(uint64_t) * (size_t)L.rows * I : 0);
   L.off_yw = o;
-  o += al(one ? sizeof(uint64_t) * (size_t)L.rows * H : 0);
+  o += al(one || blk ? sizeof(uint64_t) * (size_t)L.rows * H : 0);
   L.bytes = o;
   return L;
 }
@@ -2826,10 +2859,9 @@ void launch_block(const DecodeArgs& a, const DecodeLayout& L, const DecodeLaunch
     // fp32 tile per wave (76 KB of LDS); two workgroups a CU
     const int nd = L.max_slots * ((d.H + kMfRows - 1) / kMfRows), rd = 2 * cu_count();
     const int gd = nd < rd ? nd : rd;
-    launch("down_block_mfma_kernel", down_block_mfma_kernel<NV>, dim3(gd), dim3(kThreads), 0, s, a,
-           gd);
+    launch("down_block_mfma_kernel", down_block_mfma_kernel<NV>, dim3(gd + L.dn_items),
+           dim3(kThreads), 0, s, a, gd);
   }
-  launch("combine_block_kernel", combine_block_kernel, dim3(L.dn_items), dim3(kThreads), 0, s, a);
 }
 
 // The one-token fused launches take this call.

@@ -146,8 +146,7 @@ def _selected_bank(w, x, wr, bias):
     return S.gen_bank(w, 0, experts=sorted(sel))
 
 
-BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
-              "combine_block_kernel"]
+BLOCK_PATH = ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel"]
 
 
 @pytest.mark.parametrize("name,T,path", [

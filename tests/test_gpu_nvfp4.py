@@ -134,8 +134,7 @@ def _selected(w, x, wr):
 
 
 FUSED = ["gateup_fused_kernel"]
-BLOCK = ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
-         "combine_block_kernel"]
+BLOCK = ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel"]
 
 
 @pytest.mark.parametrize("name,T", [("decode", 1), ("spec5", 2), ("spec5", 5), ("spec5", 8),

@@ -376,8 +376,7 @@ BLOCKS = [
 
 # kernels of the block path (2..8 tokens)
 def block_path(T):
-    return ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
-            "combine_block_kernel"]
+    return ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel"]
 
 
 @pytest.mark.parametrize("variant", ["shared", "no_shared_with_bias"])

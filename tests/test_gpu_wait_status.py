@@ -45,8 +45,7 @@ PATHS = [
     ("one_token", S.Workload("one_mid", 91, T=1, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
      ["gateup_fused_kernel"]),
     ("block", S.Workload("blk_mid", 96, T=3, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
-     ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel",
-      "combine_block_kernel"]),
+     ["route_block_kernel", "gateup_block_kernel", "down_block_mfma_kernel"]),
     ("chain", S.Workload("chain9", 105, T=9, H=1024, E=64, k=4, I=512, exp_lo=-6, exp_hi=-3),
      ["route_kernel", "gateup_kernel", "down_kernel"]),
 ]
