@@ -4,28 +4,29 @@
 //
 // A prefill chunk of a few hundred tokens or more touches nearly every
 // expert (FreeToken issue #444, janit's comment, section 3), so the bank is
-// read once per 128 bucket rows and the arithmetic sits on the matrix cores:
+// read once per 64 bucket rows and the arithmetic sits on the matrix cores:
 //
 //   gate/up:  h = silu(X_e W_gate[e]^T) * (X_e W_up[e]^T)   bf16 MFMA, h -> fp16
 //   down:     y = h_e W_down[e]^T                            fp16 MFMA, y -> fp32
 //
 // X_e are the token rows of expert e's bucket, gathered through row_token;
 // the shared expert is one more bucket over all T tokens. Every bucket is
-// cut into 128-row blocks; a one-workgroup plan kernel lists the (row
-// block, column block) tiles of both GEMMs in an L2-friendly order, and
-// each XCD takes a consecutive stretch of the list.
+// cut into row blocks (64 rows; 128 for NVFP4 banks); a plan kernel lists
+// the (row block, column block) tiles of both GEMMs in an L2-friendly
+// order, and each XCD takes a consecutive stretch of the list.
 //
-// Per workgroup (512 threads, one per CU): 128 rows x 256 weight rows (for
-// gate/up: 128 gate + the 128 up rows of the same output columns), 8 waves
+// Per workgroup (256 threads, two a CU): 64 rows x 256 weight rows (for
+// gate/up: 128 gate + the 128 up rows of the same output columns), 4 waves
 // of 64 x 64 built from v_mfma_f32_16x16x32_bf16 / _f16. K advances 128 per
 // step through a 2-stage LDS pipeline filled by direct global -> LDS loads:
-//  * A: 128 rows x 128 K (bf16 x or fp16 h), each row's 16-byte pieces
+//  * A: 64 rows x 128 K (bf16 x or fp16 h), each row's 16-byte pieces
 //    permuted (piece p at slot p ^ (row & 15));
 //  * B: 256 weight rows x 64 bytes of packed E2M1 codes (piece p of row r
-//    at slot p ^ ((r / 4) & 3)).
-// The E8M0 scales of the tile's weight rows over all of K (40 KB for
-// gate/up at K = 5120) are loaded once per tile: per step they would be 4
-// bytes per row, one cache line each.
+//    at slot p ^ ((r / 4) & 3));
+//  * the step's E8M0 scales, 4 bytes per weight row.
+// A stage is 33 KB, so two workgroups share a CU and one's copies overlap
+// the other's matrix-core work. (NVFP4 banks keep one 512-thread workgroup
+// a CU: 128 rows, 8 waves, 8 scale bytes per weight row and step.)
 // Lane (column c, lane group g) of a wave takes the 32 codes of K range
 // [32 g, 32 g + 32) of its weight row, one E8M0 block, and converts them
 // with the gfx950 scaled FP4 conversion (exact: an E2M1 value times a power
@@ -45,7 +46,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 128;        // bucket rows per tile
+constexpr int kBM = 128;        // bucket rows per tile (the MXFP4 kernel: 64)
 constexpr int kBK = 128;        // K per pipeline step
 constexpr int kWRows = 256;     // weight rows per tile
 constexpr int kThreads = 512;   // 8 waves: 2 (rows) x 4 (weight rows)
@@ -54,7 +55,6 @@ constexpr int kAPieces = kBM * kBK / 8;       // 16-byte pieces of A per stage (
 constexpr int kBPieces = kWRows * kBK / 32;   // 16-byte pieces of codes per stage (1024)
 constexpr int kABytes = kAPieces * 16;        // 32 KB
 constexpr int kBBytes = kBPieces * 16;        // 16 KB
-constexpr int kStageBytes = kABytes + kBBytes;  // 48 KB
 // E8M0 bytes of the tile's 256 weight rows over all of K (K <= 8192: 64 KB),
 // loaded once per tile
 constexpr int kScaleBytes = kWRows * (8192 / 32);
@@ -72,7 +72,8 @@ struct GemmArgs {
   int32_t* tile_b[2];    // per GEMM (0 gate/up, 1 down): bucket of tile t
   int32_t* tile_mn[2];   // (row block << 8) | column block of tile t
   int32_t* tile_count;   // [2] tiles of each GEMM
-  int max_rb;            // capacity in 128-row blocks
+  int max_rb;            // capacity in row blocks
+  int bm;                // rows per tile (row block): 64, or 128
   _Float16* h;    // [R + T][I]: routed rows, then the shared expert's T rows
   float* y;       // [R][H]
   float* y_sh;    // [T][H]
@@ -111,9 +112,9 @@ constexpr int kPlanBlocks = 64;
 // blocks go by, and the row blocks sharing a weight tile (B) run together.
 // The GEMMs hand consecutive stretches of this list to each XCD.
 // Workgroups of 1024 threads (at most 1025 buckets).
-__device__ __forceinline__ int plan_chunk(int K) {
+__device__ __forceinline__ int plan_chunk(int K, int bm) {
   // row blocks whose activations take about 2.5 MB (L2 is 4 MB per XCD)
-  return min(max((5 << 19) / (kBM * K * 2), 1), 8);
+  return min(max((5 << 19) / (bm * K * 2), 1), 16);
 }
 
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int b = threadIdx.x + q * 1024;
-    cnt[q] = b < nb ? (bucket_of(g, b).count + kBM - 1) / kBM : 0;
+    cnt[q] = b < nb ? (bucket_of(g, b).count + g.bm - 1) / g.bm : 0;
   }
   int total0 = 0, total1 = 0;
   const int base0 = block_exclusive_scan(cnt[0], s_tmp, &total0);
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(GemmArgs g) {
 #pragma unroll
   for (int kind = 0; kind < 2; ++kind) {
     const int ncol = kind == 0 ? g.I / (kWRows / 2) : g.H / kWRows;
-    const int chunk = plan_chunk(kind == 0 ? g.H : g.I);
+    const int chunk = plan_chunk(kind == 0 ? g.H : g.I, g.bm);
     const int total = total_rb * ncol;
     for (int q = blockIdx.x * 1024 + threadIdx.x; q < total; q += gridDim.x * 1024) {
       // bucket: the last b with s_rb[b] * ncol <= q (buckets without rows
@@ -297,10 +298,20 @@ __device__ __forceinline__ void load_scale_rows(const void* src, F src_row, int 
 // span two scales, one for MFMA sub-steps 0-1 and one for 2-3. The
 // products E2M1 x E4M3 are exact in bf16 and fp16; the matrix scale
 // multiplies the fp32 sums in the epilogue.
-template <bool GU, bool NV>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
-  constexpr int kSt = NV ? kStageBytes + kNvSBytes : kStageBytes;   // bytes per stage
-  __shared__ __align__(16) char lds[NV ? kStages * kSt : kStages * kSt + kScaleBytes];
+// BM: bucket rows per tile, 64 (4 waves, two workgroups a CU) or 128 (8
+// waves, one a CU); the waves are 1 or 2 (rows) x 4 (weight rows). The
+// step's scales travel with each stage (PSC) except for MXFP4 at 128 rows,
+// whose tile scales over all of K are loaded once.
+template <bool GU, bool NV, int BM>
+__global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm_kernel(GemmArgs g) {
+  constexpr int NT = BM == 128 ? 512 : 256;
+  constexpr bool PSC = NV || BM == 64;
+  constexpr int kABy = BM * kBK * 2;           // A bytes per stage
+  constexpr int kSBy = NV ? kNvSBytes : (BM == 64 ? kWRows * 4 : 0);
+  constexpr int kSt = kABy + kBBytes + kSBy;   // bytes per stage
+  constexpr int kAL = BM * 16 / NT, kBL = kBPieces / NT;  // copies per thread and stage
+  static_assert(!NV || BM == 128, "NVFP4 scale copies cover 256 rows with 512 threads");
+  __shared__ __align__(16) char lds[PSC ? kStages * kSt : kStages * kSt + kScaleBytes];
   constexpr int kBN = GU ? kWRows / 2 : kWRows;  // output columns per tile
   const int N = GU ? g.I : g.H;
   const int K = GU ? g.H : g.I;
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   const int nb = g.E + (g.has_shared ? 1 : 0);
   const Bucket bk = bucket_of(g, min(max(g.tile_b[GU ? 0 : 1][t], 0), nb - 1));
   const int mn = g.tile_mn[GU ? 0 : 1][t];
-  const int m0 = (mn >> 8) * kBM;
+  const int m0 = (mn >> 8) * BM;
   const int n0 = min(mn & 255, ncol - 1) * kBN;
   if (m0 < 0 || m0 >= bk.count) return;
 
@@ -328,12 +339,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // A: thread tid fills slot (row 32 u + tid / 16, piece tid % 16), which
   // holds K piece (tid % 16) ^ (row % 16) of that row.
   const void* a_src = GU ? static_cast<const void*>(g.x) : static_cast<const void*>(g.h);
-  uint32_t a_off[kALoads];
+  uint32_t a_off[kAL];
   {
     const int piece = (tid & 15) ^ ((tid >> 4) & 15);
 #pragma unroll
-    for (int u = 0; u < kALoads; ++u) {
-      const int m = min(m0 + 32 * u + (tid >> 4), bk.count - 1);
+    for (int u = 0; u < kAL; ++u) {
+      const int m = min(m0 + (NT / 16) * u + (tid >> 4), bk.count - 1);
       int row;
       if (GU) {
         row = bk.shared ? m : (g.row_token ? g.row_token[bk.begin + m] : bk.begin + m);
@@ -355,30 +366,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   auto wrow = [&](int r) -> uint32_t {  // tile weight row -> row of the expert's matrix
     return GU ? (uint32_t)(r < 128 ? n0 + r : g.I + n0 + r - 128) : (uint32_t)(n0 + r);
   };
-  uint32_t b_off[kBLoads];
+  uint32_t b_off[kBL];
 #pragma unroll
-  for (int u = 0; u < kBLoads; ++u) {
-    const int r = 128 * u + (tid >> 2);
+  for (int u = 0; u < kBL; ++u) {
+    const int r = (NT / 4) * u + (tid >> 2);
     b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
   }
   const uint32_t s_lds = lds_base + kStages * kSt;
   // NV: thread tid copies dword tid % 2 of weight row tid / 2's 8 scale
-  // bytes of each K step into the stage
-  const uint32_t nv_off = NV ? wrow(tid >> 1) * srow + 4u * (uint32_t)(tid & 1) : 0u;
+  // bytes of each K step into the stage; MXFP4 at 64 rows: thread tid the 4
+  // scale bytes of weight row tid
+  const uint32_t nv_off = NV ? wrow(tid >> 1) * srow + 4u * (uint32_t)(tid & 1)
+                              : PSC ? wrow(tid) * srow : 0u;
 
   // Stage `st` <- K step `ks`.
   auto issue = [&](int st, int ks) {
     const uint32_t base = lds_base + (uint32_t)(st * kSt);
     const uint32_t k0 = (uint32_t)(ks * kBK);
 #pragma unroll
-    for (int u = 0; u < kALoads; ++u)
-      lds_load16(a_src, a_off[u] + 2u * k0, base + (uint32_t)((u * kThreads + 64 * wave) * 16));
+    for (int u = 0; u < kAL; ++u)
+      lds_load16(a_src, a_off[u] + 2u * k0, base + (uint32_t)((u * NT + 64 * wave) * 16));
 #pragma unroll
-    for (int u = 0; u < kBLoads; ++u)
-      lds_load16(cbase, b_off[u] + k0 / 2,
-                 base + kABytes + (uint32_t)((u * kThreads + 64 * wave) * 16));
+    for (int u = 0; u < kBL; ++u)
+      lds_load16(cbase, b_off[u] + k0 / 2, base + kABy + (uint32_t)((u * NT + 64 * wave) * 16));
     if constexpr (NV)
-      lds_load4(sbase, nv_off + k0 / 16, base + kABytes + kBBytes + (uint32_t)(64 * wave * 4));
+      lds_load4(sbase, nv_off + k0 / 16, base + kABy + kBBytes + (uint32_t)(64 * wave * 4));
+    else if constexpr (PSC)
+      lds_load4(sbase, nv_off + k0 / 32, base + kABy + kBBytes + (uint32_t)(64 * wave * 4));
   };
   // The tile's scales: rows r of the tile (gate/up: two runs of 128 rows,
   // down: one run of 256), srow bytes each, contiguous in the bank and in
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // 2 % slower here.)
   auto load_scales = [&]() {
     const int pieces = kWRows * (int)srow / 4;
-    for (int p0 = 64 * wave; p0 < pieces; p0 += kThreads) {
+    for (int p0 = 64 * wave; p0 < pieces; p0 += NT) {
       const int p = min(p0 + lane, pieces - 1);
       const uint32_t b = 4u * (uint32_t)p;
       const uint32_t r = b / srow;
@@ -410,10 +424,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   auto compute = [&](int st, int st_k) {
     const char* sb = lds + st * kSt;
     const uint4* sa = reinterpret_cast<const uint4*>(sb);
-    const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABytes);
+    const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABy);
     const uint8_t* ss = reinterpret_cast<const uint8_t*>(lds + kStages * kSt) +
                         (size_t)st_k * 4;  // this K step's 4 scale bytes of each row
-    const uint16_t* ssn = reinterpret_cast<const uint16_t*>(sb + kABytes + kBBytes);
+    const uint16_t* ssn = reinterpret_cast<const uint16_t*>(sb + kABy + kBBytes);
+    const uint8_t* ssp = reinterpret_cast<const uint8_t*>(sb + kABy + kBBytes);
     uint4 bc[4];
     float sc[4], sc2[4];
 #pragma unroll
@@ -424,6 +439,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ssn[r * 4 + grp], 1.0f, false);
         sc[j] = f.x;
         sc2[j] = f.y;
+      } else if constexpr (PSC) {
+        sc[j] = sc2[j] = e8m0_to_f32(ssp[r * 4 + grp]);
       } else {
         sc[j] = sc2[j] = e8m0_to_f32(ss[r * srow + grp]);
       }
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
   // stage ks visible to every wave and frees the other buffer (read at
   // step ks - 1) for ks + 1.
   const int steps = K / kBK;
-  if constexpr (!NV) load_scales();
+  if constexpr (!PSC) load_scales();
   issue(0, 0);
   for (int ks = 0; ks < steps; ++ks) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1050,7 +1067,7 @@ struct GemmLayout {
 GemmLayout gemm_layout(void* ws, int T, int H, int I, int E, int R, bool shared) {
   GemmLayout L;
   const size_t rows = (size_t)R + (shared ? T : 0);
-  L.max_rb = (R + kBM - 1) / kBM + E + (shared ? (T + kBM - 1) / kBM + 1 : 0);
+  L.max_rb = (R + 63) / 64 + E + (shared ? (T + 63) / 64 + 1 : 0);  // blocks of >= 64 rows
   L.ncol_gu = I / (kWRows / 2);
   L.ncol_dn = H / kWRows;
   const size_t hb = (rows * I * sizeof(_Float16) + 255) & ~(size_t)255;
@@ -1073,7 +1090,7 @@ MxLayout mx_layout(void* ws, int T, int H, int I, int E, int R, bool shared) {
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   MxLayout L;
   const size_t rows = (size_t)R + (shared ? T : 0);
-  L.max_rb = (R + kBM - 1) / kBM + E + (shared ? (T + kBM - 1) / kBM + 1 : 0);
+  L.max_rb = (R + 63) / 64 + E + (shared ? (T + 63) / 64 + 1 : 0);  // blocks of >= 64 rows
   L.ncol_gu = I / (kWRows / 2);
   L.ncol_dn = H / kWRows;
   const size_t nt = 2 * (size_t)L.max_rb * (L.ncol_gu + L.ncol_dn) + 2;
@@ -1142,6 +1159,7 @@ void launch_expert_gemm_mx(const FfnProblem& p, void* ws, hipStream_t s) {
   g.xs = L.xs;
   g.hq = L.hq;
   g.hs = L.hs;
+  g.bm = kBM;  // these kernels tile 128 rows
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   launch_quant_mxfp8(p.x, (long)p.T * p.H / 32, L.xq, L.xs, s);
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
@@ -1184,6 +1202,7 @@ void launch_fp8_gemm(const Fp8Ffn& p, void* ws, hipStream_t s) {
   g.max_rb = L.max_rb;
   g.h = L.h;
   g.y_sh = p.y;
+  g.bm = kBM;  // these kernels tile 128 rows
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
   launch("gemm_fp8w_gateup_kernel", gemm_fp8w_kernel<true>, dim3(grid_gu), dim3(kThreads), 0, s, g);
@@ -1226,14 +1245,18 @@ void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   g.h = L.h;
   g.y = p.y;
   g.y_sh = p.y_sh;
+  g.bm = p.routed.codec == kCodecNvfp4 ? 128 : 64;
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   // grids: every tile the lists can hold, rounded up to the 8 XCDs
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
   const bool nv = p.routed.codec == kCodecNvfp4;
-  launch("gemm_gateup_kernel", nv ? gemm_kernel<true, true> : gemm_kernel<true, false>,
-         dim3(grid_gu), dim3(kThreads), 0, s, g);
-  launch("gemm_down_kernel", nv ? gemm_kernel<false, true> : gemm_kernel<false, false>,
-         dim3(grid_dn), dim3(kThreads), 0, s, g);
+  if (nv) {
+    launch("gemm_gateup_kernel", gemm_kernel<true, true, 128>, dim3(grid_gu), dim3(512), 0, s, g);
+    launch("gemm_down_kernel", gemm_kernel<false, true, 128>, dim3(grid_dn), dim3(512), 0, s, g);
+  } else {
+    launch("gemm_gateup_kernel", gemm_kernel<true, false, 64>, dim3(grid_gu), dim3(256), 0, s, g);
+    launch("gemm_down_kernel", gemm_kernel<false, false, 64>, dim3(grid_dn), dim3(256), 0, s, g);
+  }
 }
 
 }  // namespace moe

@@ -545,6 +545,31 @@ def test_layer_token_counts_share_one_workspace():
         assert err < (HP.FP32_TOL if T <= 16 else HP.GEMM_TOL), (T, err)
 
 
+@pytest.mark.parametrize("T", [1, 5, 8])
+def test_layer_back_to_back_calls_with_new_tokens_share_a_workspace(T):
+    # the few-token paths hand values between workgroups as words tagged with
+    # the call: a second call on the same workspace, with other tokens, must
+    # not take the first call's words (its results would then be the first
+    # call's, or a mix)
+    w = S.get("tiny")
+    d = S.gen_inputs(w, 0)
+    rd, sd = HP.bank_to_dev(d["routed"]), HP.bank_to_dev(d["shared"])
+    wr = HP.to_dev(d["w_router"])
+    ws = M.workspace(T, w.H, w.I, w.E, w.k, HP.dev())
+    for call in (1, 2, 3):
+        x_bits = S.gen_tokens(w, 11, call=call, T=T)
+        out = torch.empty((T, w.H), dtype=torch.float32, device=HP.dev())
+        ids = torch.empty((T, w.k), dtype=torch.int32, device=HP.dev())
+        wt = torch.empty((T, w.k), dtype=torch.float32, device=HP.dev())
+        M.moe_layer_forward(HP.to_dev(x_bits), wr, None, rd, sd, w.k, out, ids, wt, ws)
+        HP.assert_waits_ok(ws)
+        ref = O.layer(x_bits, d["w_router"], None, d["routed"], d["shared"], w.k)
+        alt = HP.check_routing(ref, _np(ids), _np(wt), w.k)
+        err = HP.rel_l2(_np(out), HP.reference_rows(ref, d["routed"], d["shared"],
+                                                      ref["tokens"], alt))
+        assert err < HP.FP32_TOL, (T, call, err)
+
+
 def test_layer_with_garbage_workspace():
     w = S.get("spec5")
     x, wr = S.gen_tokens(w, 0), S.gen_router(w, 0)
