@@ -11,7 +11,7 @@
 //
 // X_e are the token rows of expert e's bucket, gathered through row_token;
 // the shared expert is one more bucket over all T tokens. Every bucket is
-// cut into row blocks (64 rows; 128 for NVFP4 banks); a plan kernel lists
+// cut into 64-row blocks; a plan kernel lists
 // the (row block, column block) tiles of both GEMMs in an L2-friendly
 // order, and each XCD takes a consecutive stretch of the list.
 //
@@ -24,9 +24,9 @@
 //  * B: 256 weight rows x 64 bytes of packed E2M1 codes (piece p of row r
 //    at slot p ^ ((r / 4) & 3));
 //  * the step's E8M0 scales, 4 bytes per weight row.
-// A stage is 33 KB, so two workgroups share a CU and one's copies overlap
-// the other's matrix-core work. (NVFP4 banks keep one 512-thread workgroup
-// a CU: 128 rows, 8 waves, 8 scale bytes per weight row and step.)
+// A stage is 33 KB (34 KB with an NVFP4 bank's 8 scale bytes per weight
+// row), so two workgroups share a CU and one's copies overlap the other's
+// matrix-core work.
 // Lane (column c, lane group g) of a wave takes the 32 codes of K range
 // [32 g, 32 g + 32) of its weight row, one E8M0 block, and converts them
 // with the gfx950 scaled FP4 conversion (exact: an E2M1 value times a power
@@ -46,7 +46,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 128;        // bucket rows per tile (the MXFP4 kernel: 64)
+constexpr int kBM = 128;        // bucket rows per tile (gemm_kernel: 64)
 constexpr int kBK = 128;        // K per pipeline step
 constexpr int kWRows = 256;     // weight rows per tile
 constexpr int kThreads = 512;   // 8 waves: 2 (rows) x 4 (weight rows)
@@ -73,7 +73,7 @@ struct GemmArgs {
   int32_t* tile_mn[2];   // (row block << 8) | column block of tile t
   int32_t* tile_count;   // [2] tiles of each GEMM
   int max_rb;            // capacity in row blocks
-  int bm;                // rows per tile (row block): 64, or 128
+  int bm;                // rows per tile (row block): 64, or 128 (FP8, MX)
   _Float16* h;    // [R + T][I]: routed rows, then the shared expert's T rows
   float* y;       // [R][H]
   float* y_sh;    // [T][H]
@@ -298,10 +298,11 @@ __device__ __forceinline__ void load_scale_rows(const void* src, F src_row, int 
 // span two scales, one for MFMA sub-steps 0-1 and one for 2-3. The
 // products E2M1 x E4M3 are exact in bf16 and fp16; the matrix scale
 // multiplies the fp32 sums in the epilogue.
-// BM: bucket rows per tile, 64 (4 waves, two workgroups a CU) or 128 (8
-// waves, one a CU); the waves are 1 or 2 (rows) x 4 (weight rows). The
-// step's scales travel with each stage (PSC) except for MXFP4 at 128 rows,
-// whose tile scales over all of K are loaded once.
+// BM: bucket rows per tile, 64 (4 waves, two workgroups a CU; the one
+// instantiated) or 128 (8 waves, one a CU, measured slower); the waves are
+// 1 or 2 (rows) x 4 (weight rows). The step's scales travel with each stage
+// (PSC) except for MXFP4 at 128 rows, whose tile scales over all of K are
+// loaded once.
 template <bool GU, bool NV, int BM>
 __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm_kernel(GemmArgs g) {
   constexpr int NT = BM == 128 ? 512 : 256;
@@ -310,7 +311,6 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
   constexpr int kSBy = NV ? kNvSBytes : (BM == 64 ? kWRows * 4 : 0);
   constexpr int kSt = kABy + kBBytes + kSBy;   // bytes per stage
   constexpr int kAL = BM * 16 / NT, kBL = kBPieces / NT;  // copies per thread and stage
-  static_assert(!NV || BM == 128, "NVFP4 scale copies cover 256 rows with 512 threads");
   __shared__ __align__(16) char lds[PSC ? kStages * kSt : kStages * kSt + kScaleBytes];
   constexpr int kBN = GU ? kWRows / 2 : kWRows;  // output columns per tile
   const int N = GU ? g.I : g.H;
@@ -373,11 +373,14 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
     b_off[u] = wrow(r) * crow + 16u * (uint32_t)((tid & 3) ^ ((r >> 2) & 3));
   }
   const uint32_t s_lds = lds_base + kStages * kSt;
-  // NV: thread tid copies dword tid % 2 of weight row tid / 2's 8 scale
-  // bytes of each K step into the stage; MXFP4 at 64 rows: thread tid the 4
+  // NV: dword d of the stage's scales is dword d % 2 of weight row d / 2's
+  // 8 scale bytes of the K step (thread tid copies d = tid, and with 256
+  // threads also d = tid + 256); MXFP4 at 64 rows: thread tid copies the 4
   // scale bytes of weight row tid
   const uint32_t nv_off = NV ? wrow(tid >> 1) * srow + 4u * (uint32_t)(tid & 1)
                               : PSC ? wrow(tid) * srow : 0u;
+  const uint32_t nv_off2 = NV && NT == 256 ? wrow((tid + 256) >> 1) * srow + 4u * (uint32_t)(tid & 1)
+                                           : 0u;
 
   // Stage `st` <- K step `ks`.
   auto issue = [&](int st, int ks) {
@@ -389,9 +392,12 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
 #pragma unroll
     for (int u = 0; u < kBL; ++u)
       lds_load16(cbase, b_off[u] + k0 / 2, base + kABy + (uint32_t)((u * NT + 64 * wave) * 16));
-    if constexpr (NV)
+    if constexpr (NV) {
       lds_load4(sbase, nv_off + k0 / 16, base + kABy + kBBytes + (uint32_t)(64 * wave * 4));
-    else if constexpr (PSC)
+      if constexpr (NT == 256)
+        lds_load4(sbase, nv_off2 + k0 / 16,
+                  base + kABy + kBBytes + (uint32_t)((256 + 64 * wave) * 4));
+    } else if constexpr (PSC)
       lds_load4(sbase, nv_off + k0 / 32, base + kABy + kBBytes + (uint32_t)(64 * wave * 4));
   };
   // The tile's scales: rows r of the tile (gate/up: two runs of 128 rows,
@@ -1245,14 +1251,14 @@ void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s) {
   g.h = L.h;
   g.y = p.y;
   g.y_sh = p.y_sh;
-  g.bm = p.routed.codec == kCodecNvfp4 ? 128 : 64;
+  g.bm = 64;
   launch("gemm_plan_kernel", gemm_plan_kernel, dim3(kPlanBlocks), dim3(1024), 0, s, g);
   // grids: every tile the lists can hold, rounded up to the 8 XCDs
   const int grid_gu = (int)((n_gu + 7) / 8 * 8), grid_dn = (int)((n_dn + 7) / 8 * 8);
   const bool nv = p.routed.codec == kCodecNvfp4;
   if (nv) {
-    launch("gemm_gateup_kernel", gemm_kernel<true, true, 128>, dim3(grid_gu), dim3(512), 0, s, g);
-    launch("gemm_down_kernel", gemm_kernel<false, true, 128>, dim3(grid_dn), dim3(512), 0, s, g);
+    launch("gemm_gateup_kernel", gemm_kernel<true, true, 64>, dim3(grid_gu), dim3(256), 0, s, g);
+    launch("gemm_down_kernel", gemm_kernel<false, true, 64>, dim3(grid_dn), dim3(256), 0, s, g);
   } else {
     launch("gemm_gateup_kernel", gemm_kernel<true, false, 64>, dim3(grid_gu), dim3(256), 0, s, g);
     launch("gemm_down_kernel", gemm_kernel<false, false, 64>, dim3(grid_dn), dim3(256), 0, s, g);
