@@ -776,6 +776,12 @@ __device__ void combine_column(const DecodeArgs& a, int c, bool failed) {
 constexpr int kGuStreamMax = 896;
 // Down items (32-row groups) per workgroup of the one-token launch (1 or 2).
 constexpr int kDnPerWg = 2;
+// The last slots' down work goes one item per workgroup instead: their h
+// flags come last (their gate/up workgroups are dispatched last), so halving
+// the work behind each of those flags shortens the launch's tail. Measured
+// at 6 slots: the last two slots single is 0.6-1 us faster than all pairs;
+// the last three, four or six are slower (more workgroups behind the flags).
+constexpr int kDnSingleSlots = 2;
 
 // sg / su: the words holding the lane's scale bytes (byte lane % 4 of each).
 struct GuRegs {
@@ -1615,7 +1621,7 @@ __device__ void finish_parts(const DecodeArgs& a, int c0, bool live1, const Down
 template <bool NV>
 __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a, int n_shared,
                                                                 int n_sd, int G, int per,
-                                                                int dpw) {
+                                                                int dpw, int ns_pair) {
   extern __shared__ __align__(16) char lds[];
   const int b0 = blockIdx.x;
   if (b0 < a.nb_router) {
@@ -1647,7 +1653,8 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
   }
   if (b0 >= a.nb_router + 1 + n_shared + G) {
     // down workgroups: dpw (1 or 2) column groups each (one for the FP8
-    // shared expert), the shared expert's first, then slot by slot
+    // shared expert), the shared expert's first, then slot by slot; slots
+    // from ns_pair on take one column group per workgroup
     const int d = b0 - (a.nb_router + 1 + n_shared + G);
     const DownLds L(a, lds);
     const int per_slot = (a.dn_items + dpw - 1) / dpw;
@@ -1656,9 +1663,18 @@ __global__ __launch_bounds__(kThreads, 3) void gateup_fused_kernel(DecodeArgs a,
       finish_parts(a, d, false, L);
       return;
     }
-    const int slot = d < n_sd ? -1 : (d - n_sd) / per_slot;
-    const int c0 = dpw * (d < n_sd ? d : (d - n_sd) - slot * per_slot);
-    const bool live1 = dpw == 2 && c0 + 1 < a.dn_items;
+    const int dr = d - n_sd, n_pair = ns_pair * per_slot;
+    int slot = -1, c0 = dpw * d;
+    bool live1 = dpw == 2 && c0 + 1 < a.dn_items;
+    if (d >= n_sd && dr < n_pair) {
+      slot = dr / per_slot;
+      c0 = dpw * (dr - slot * per_slot);
+      live1 = dpw == 2 && c0 + 1 < a.dn_items;
+    } else if (d >= n_sd) {
+      slot = ns_pair + (dr - n_pair) / a.dn_items;
+      c0 = (dr - n_pair) % a.dn_items;
+      live1 = false;
+    }
     down_pair<NV>(a, slot, c0, live1, n_shared, L);
     finish_parts(a, c0, live1, L);
     return;
@@ -2963,13 +2979,15 @@ void launch_decode(const DecodeLaunch& d, void* ws, hipStream_t s) {
     const int per = max(2, (routed_gu + kGuStreamMax - 1) / kGuStreamMax);
     const int gg = (routed_gu + per - 1) / per;
     const bool nv = d.routed.codec == kCodecNvfp4;
-    // down workgroups: kDnPerWg 32-row groups each (FP8 shared expert: one)
+    // down workgroups: kDnPerWg 32-row groups each (FP8 shared expert: one),
+    // one each for the last kDnSingleSlots slots
     const int per_slot = (L.dn_items + kDnPerWg - 1) / kDnPerWg;
-    const int nd = L.max_slots * per_slot;
+    const int ns_pair = max(L.max_slots - kDnSingleSlots, 0);
+    const int nd = ns_pair * per_slot + (L.max_slots - ns_pair) * L.dn_items;
     if (shared && !d.shared_fp8) n_sd = per_slot;
     launch("gateup_fused_kernel", nv ? gateup_fused_kernel<true> : gateup_fused_kernel<false>,
            dim3(L.nb_router + 1 + n_sh + gg + n_sd + nd), dim3(kThreads), kLdsBytes, s, a, n_sh,
-           n_sd, gg, per, kDnPerWg);
+           n_sd, gg, per, kDnPerWg, ns_pair);
     return;
   }
   // A block of 2..8 tokens: router + routing, then the streaming gate/up

@@ -19,11 +19,13 @@ def test_committed_traffic_record_matches_the_committed_kernel():
     # record left behind by a later change would report no traffic at all
     t = bench.recorded_traffic("gateup_fused_kernel", "decode")
     assert isinstance(t, int)
-    # within 2 % of the launch's algorithmic bytes (the whole one-token
-    # layer with 6 routed experts, 135.98 MB): no re-reads of weights
+    # within 3 % of the launch's algorithmic bytes (the whole one-token
+    # layer with 6 routed experts, 135.98 MB). The excess allowed covers the
+    # down workgroups' reads of the h rows as 8-byte words; one expert's
+    # down matrix (6.2 MB, 4.6 %) read twice would exceed it.
     _, algo = bench.kernel_work("gateup_fused_kernel", S.get("decode"), 6)
     assert abs(algo / 135.98e6 - 1.0) < 1e-4
-    assert abs(t / algo - 1.0) < 0.02
+    assert abs(t / algo - 1.0) < 0.03
 
 
 def _fake_tree(tmp_path, src_text, recorded_sha):
