@@ -311,7 +311,13 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
   constexpr int kSBy = NV ? kNvSBytes : (BM == 64 ? kWRows * 4 : 0);
   constexpr int kSt = kABy + kBBytes + kSBy;   // bytes per stage
   constexpr int kAL = BM * 16 / NT, kBL = kBPieces / NT;  // copies per thread and stage
-  __shared__ __align__(16) char lds[PSC ? kStages * kSt : kStages * kSt + kScaleBytes];
+  // gate/up at 64 rows: two 16-byte scale chunks per weight row (4 K steps
+  // of MXFP4 scales, 2 of NVFP4) after the stages (down, K = I, has 72-byte
+  // MXFP4 scale rows at the layer's shape and keeps the per-step loads)
+  constexpr int kChunkBy = BM != 64 || !GU ? 0 : kWRows * 16;
+  constexpr int kCkSteps = NV ? 2 : 4;  // K steps per chunk
+  __shared__ __align__(16) char lds[PSC ? kStages * kSt + 2 * kChunkBy
+                                        : kStages * kSt + kScaleBytes];
   constexpr int kBN = GU ? kWRows / 2 : kWRows;  // output columns per tile
   const int N = GU ? g.I : g.H;
   const int K = GU ? g.H : g.I;
@@ -381,6 +387,14 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
                               : PSC ? wrow(tid) * srow : 0u;
   const uint32_t nv_off2 = NV && NT == 256 ? wrow((tid + 256) >> 1) * srow + 4u * (uint32_t)(tid & 1)
                                            : 0u;
+  // Scale rows a multiple of 16 bytes: thread tid copies row tid's scale
+  // bytes of kCkSteps K steps at a time, one 16-byte load in place of a
+  // 4-byte load (two for NVFP4) every step, each of which touches the cache
+  // lines of 256 scale rows for 1 KB (2 KB)
+  bool chunked = false;
+  if constexpr (kChunkBy > 0) chunked = (srow & 15u) == 0 && ((uintptr_t)sbase & 15u) == 0;
+  const uint32_t c_lds = lds_base + kStages * kSt;
+  const uint32_t ck_off = kChunkBy > 0 ? wrow(tid) * srow : 0u;
 
   // Stage `st` <- K step `ks`.
   auto issue = [&](int st, int ks) {
@@ -392,13 +406,22 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
 #pragma unroll
     for (int u = 0; u < kBL; ++u)
       lds_load16(cbase, b_off[u] + k0 / 2, base + kABy + (uint32_t)((u * NT + 64 * wave) * 16));
+    if constexpr (kChunkBy > 0) {
+      if (chunked) {
+        if (ks % kCkSteps == 0)
+          lds_load16(sbase, ck_off + k0 / (NV ? 16 : 32),
+                     c_lds + (uint32_t)(((ks / kCkSteps) & 1) * kChunkBy + 64 * wave * 16));
+        return;
+      }
+    }
     if constexpr (NV) {
       lds_load4(sbase, nv_off + k0 / 16, base + kABy + kBBytes + (uint32_t)(64 * wave * 4));
       if constexpr (NT == 256)
         lds_load4(sbase, nv_off2 + k0 / 16,
                   base + kABy + kBBytes + (uint32_t)((256 + 64 * wave) * 4));
-    } else if constexpr (PSC)
+    } else if constexpr (PSC) {
       lds_load4(sbase, nv_off + k0 / 32, base + kABy + kBBytes + (uint32_t)(64 * wave * 4));
+    }
   };
   // The tile's scales: rows r of the tile (gate/up: two runs of 128 rows,
   // down: one run of 256), srow bytes each, contiguous in the bank and in
@@ -433,8 +456,20 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
     const uint4* sbk = reinterpret_cast<const uint4*>(sb + kABy);
     const uint8_t* ss = reinterpret_cast<const uint8_t*>(lds + kStages * kSt) +
                         (size_t)st_k * 4;  // this K step's 4 scale bytes of each row
+    // this step's scale pair grp of row r (NVFP4): ssn[r * nst + grp]; its
+    // scale byte grp of row r (MXFP4): ssp[r * sst + grp]
     const uint16_t* ssn = reinterpret_cast<const uint16_t*>(sb + kABy + kBBytes);
     const uint8_t* ssp = reinterpret_cast<const uint8_t*>(sb + kABy + kBBytes);
+    int nst = 4, sst = 4;
+    if constexpr (kChunkBy > 0) {
+      if (chunked) {
+        const char* ck = lds + kStages * kSt + ((st_k / kCkSteps) & 1) * kChunkBy;
+        ssn = reinterpret_cast<const uint16_t*>(ck + (st_k & 1) * 8);
+        ssp = reinterpret_cast<const uint8_t*>(ck + (st_k & 3) * 4);
+        nst = 8;
+        sst = 16;
+      }
+    }
     uint4 bc[4];
     float sc[4], sc2[4];
 #pragma unroll
@@ -442,11 +477,11 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
       const int r = frag_row<GU>(wn, j, c);
       bc[j] = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
       if constexpr (NV) {
-        const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ssn[r * 4 + grp], 1.0f, false);
+        const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ssn[r * nst + grp], 1.0f, false);
         sc[j] = f.x;
         sc2[j] = f.y;
       } else if constexpr (PSC) {
-        sc[j] = sc2[j] = e8m0_to_f32(ssp[r * 4 + grp]);
+        sc[j] = sc2[j] = e8m0_to_f32(ssp[r * sst + grp]);
       } else {
         sc[j] = sc2[j] = e8m0_to_f32(ss[r * srow + grp]);
       }
