@@ -438,6 +438,160 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
     }
   };
 
+  // A bucket of at most 16 rows: one row group, so the tile holds 16 x
+  // rows (4 KB a step) and three stages of it fit in the same LDS, letting
+  // the weight copies run two steps ahead of the MFMAs (such tiles are bound
+  // by their copies, not by matrix work). Each wave converts its 64 weight
+  // rows as in the 64-row tile and runs 4 MFMAs per sub-step.
+  if constexpr (BM == 64) {
+    if (bk.count <= 16) {
+      constexpr int kSA = 16 * kBK * 2;          // A bytes per stage
+      constexpr int kSS = kSA + kBBytes + kSBy;  // bytes per stage
+      constexpr int kS3 = 3;                     // stages
+      static_assert(kS3 * kSS + 2 * kChunkBy <= (int)sizeof(lds), "skinny stages exceed the LDS");
+      const uint32_t ck3 = lds_base + kS3 * kSS;  // the two scale chunks
+      auto issue_s = [&](int st, int ks) {
+        const uint32_t base = lds_base + (uint32_t)(st * kSS);
+        const uint32_t k0 = (uint32_t)(ks * kBK);
+        lds_load16(a_src, a_off[0] + 2u * k0, base + (uint32_t)(64 * wave * 16));
+#pragma unroll
+        for (int u = 0; u < kBL; ++u)
+          lds_load16(cbase, b_off[u] + k0 / 2, base + kSA + (uint32_t)((u * NT + 64 * wave) * 16));
+        if (chunked) {
+          if (ks % kCkSteps == 0)
+            lds_load16(sbase, ck_off + k0 / (NV ? 16 : 32),
+                       ck3 + (uint32_t)(((ks / kCkSteps) & 1) * kChunkBy + 64 * wave * 16));
+        } else if constexpr (NV) {
+          lds_load4(sbase, nv_off + k0 / 16, base + kSA + kBBytes + (uint32_t)(64 * wave * 4));
+          lds_load4(sbase, nv_off2 + k0 / 16, base + kSA + kBBytes + (uint32_t)((256 + 64 * wave) * 4));
+        } else {
+          lds_load4(sbase, nv_off + k0 / 32, base + kSA + kBBytes + (uint32_t)(64 * wave * 4));
+        }
+      };
+      // copies per thread of step ks's stage
+      auto n_loads = [&](int ks) {
+        return 1 + kBL + (chunked ? (ks % kCkSteps == 0 ? 1 : 0) : (NV ? 2 : 1));
+      };
+      f32x4_t as[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) as[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      auto compute_s = [&](int st, int st_k) {
+        const char* sb = lds + st * kSS;
+        const uint4* sa = reinterpret_cast<const uint4*>(sb);
+        const uint4* sbk = reinterpret_cast<const uint4*>(sb + kSA);
+        const uint16_t* ssn = reinterpret_cast<const uint16_t*>(sb + kSA + kBBytes);
+        const uint8_t* ssp = reinterpret_cast<const uint8_t*>(sb + kSA + kBBytes);
+        int nst = 4, sst = 4;
+        if (chunked) {
+          const char* ck = lds + kS3 * kSS + ((st_k / kCkSteps) & 1) * kChunkBy;
+          ssn = reinterpret_cast<const uint16_t*>(ck + (st_k & 1) * 8);
+          ssp = reinterpret_cast<const uint8_t*>(ck + (st_k & 3) * 4);
+          nst = 8;
+          sst = 16;
+        }
+        uint4 bc[4];
+        float sc[4], sc2[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = frag_row<GU>(wn, j, c);
+          bc[j] = sbk[r * 4 + (grp ^ ((r >> 2) & 3))];
+          if constexpr (NV) {
+            const f32x2_t f =
+                __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ssn[r * nst + grp], 1.0f, false);
+            sc[j] = f.x;
+            sc2[j] = f.y;
+          } else {
+            sc[j] = sc2[j] = e8m0_to_f32(ssp[r * sst + grp]);
+          }
+        }
+        // A row c, K values 32 grp + 8 s: piece 4 grp + s
+        Op<GU> bcur[4], bnext[4];
+        uint4 acur = sa[c * 16 + ((4 * grp) ^ c)], anext = acur;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (NV)
+            bcur[j] = cvt8_nv<GU>(word_of(bc[j], 0), sc[j]);
+          else
+            bcur[j] = cvt8<GU>(word_of(bc[j], 0), sc[j]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < 3) {
+            anext = sa[c * 16 + ((4 * grp + s + 1) ^ c)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if constexpr (NV)
+                bnext[j] = cvt8_nv<GU>(word_of(bc[j], s + 1), s + 1 < 2 ? sc[j] : sc2[j]);
+              else
+                bnext[j] = cvt8<GU>(word_of(bc[j], s + 1), sc[j]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) as[j] = mma<GU>(acur, bcur[j], as[j]);
+          if (s < 3) {
+            acur = anext;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bcur[q] = bnext[q];
+          }
+        }
+      };
+      // Stage ks lands while ks - 1 computes; at the top of step ks only
+      // stage ks + 1's copies may still be in flight (loads complete in
+      // order), then one barrier makes stage ks visible and frees the
+      // buffer of step ks - 1 for ks + 2.
+      const int steps_s = K / kBK;
+      issue_s(0, 0);
+      if (steps_s > 1) issue_s(1, 1);
+      for (int ks = 0; ks < steps_s; ++ks) {
+        const int n1 = ks + 1 < steps_s ? n_loads(ks + 1) : 0;
+        if (n1 == 0)
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (n1 == 5)
+          asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else if (n1 == 6)
+          asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+        __syncthreads();
+        if (ks + 2 < steps_s) issue_s((ks + 2) % kS3, ks + 2);
+        compute_s(ks % kS3, ks);
+      }
+      float mg = 1.0f, mu = 1.0f;
+      if constexpr (NV) {
+        if (bv.gscale) {
+          mg = bv.gscale[bk.e * 3 + (GU ? 0 : 2)];
+          mu = bv.gscale[bk.e * 3 + 1];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * grp + v;
+        if (m >= bk.count) continue;
+        if constexpr (GU) {
+          _Float16* hr = g.h + (size_t)(bk.begin + m) * g.I + n0 + 32 * wn + c;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if constexpr (NV)
+              hr[16 * j] = (_Float16)silu_mul(as[j][v] * mg, as[j + 2][v] * mu);
+            else
+              hr[16 * j] = (_Float16)silu_mul(as[j][v], as[j + 2][v]);
+          }
+        } else {
+          float* yr = (bk.shared ? g.y_sh + (size_t)m * g.H : g.y + (size_t)(bk.begin + m) * g.H) +
+                      n0 + 64 * wn + c;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (NV)
+              yr[16 * j] = as[j][v] * mg;
+            else
+              yr[16 * j] = as[j][v];
+          }
+        }
+      }
+      return;
+    }
+  }
+
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)

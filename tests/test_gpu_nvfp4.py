@@ -69,6 +69,26 @@ def test_ffn_bucketed_rows(w, tol, kernel):
     assert err < tol
 
 
+def test_ffn_gemm_buckets_around_sixteen_rows():
+    # buckets of at most 16 rows take 16-row tiles with three stages (8 K
+    # steps of gate/up: four 2-step scale chunks); 17 rows and more take the
+    # 64-row tiles
+    w = S.Workload("nv_k8", 98, T=200, H=1024, E=6, k=2, I=512, exp_lo=-6, exp_hi=-3)
+    counts = np.array([16, 17, 15, 1, 0, 100])  # 149 rows: above the GEMV path
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    rng = np.random.default_rng([w.cfg_id, 12])
+    row_token = rng.integers(0, w.T, R).astype(np.int32)
+    x = S.gen_tokens(w, 1)
+    bank = S.gen_nvfp4_bank(w, 1)
+    y, names = run_ffn(x, bank, offsets, row_token, R)
+    assert "gemm_gateup_kernel" in names
+    ref = N.expert_rows_nvfp4(O.bf16_to_f64(x), bank, offsets, row_token)
+    err = HP.rel_l2(y, ref)
+    print(counts.tolist(), err)
+    assert err < HP.GEMM_TOL
+
+
 @pytest.mark.parametrize("T", [4, 300])
 def test_ffn_identity_probe(T):
     n = 256

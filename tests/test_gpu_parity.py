@@ -648,6 +648,32 @@ def test_gemm_ffn_hand_made_buckets():
     assert _row_errors(y, ref).max() < 4 * HP.GEMM_TOL
 
 
+# hidden 1024 / intermediate 512: 8 K steps of gate/up (two 4-step scale
+# chunks), 4 of down
+GEMM_K8 = S.Workload("gemm_k8", 91, T=200, H=1024, E=6, k=2, I=512, exp_lo=-6, exp_hi=-3,
+                     desc="grouped-GEMM parity shape, 8 K steps")
+
+
+def test_gemm_ffn_buckets_around_sixteen_rows():
+    # buckets of at most 16 rows take 16-row tiles with three stages; 17 rows
+    # and more take the 64-row tiles
+    w = GEMM_K8
+    counts = np.array([16, 17, 15, 1, 0, 100])  # 149 rows: above the GEMV path
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    rng = np.random.default_rng([w.cfg_id, 12])
+    row_token = rng.integers(0, w.T, R).astype(np.int32)
+    x = S.gen_tokens(w, 1)
+    bank = S.gen_bank(w, 1)
+    y = run_ffn(x, bank, offsets, row_token, R)
+    assert "gemm_gateup_kernel" in [M.moe_launch_name(i) for i in range(M.moe_last_call_launches())]
+    ref = O.expert_rows(O.bf16_to_f64(x), bank, offsets, row_token)
+    err = _row_errors(y, ref)
+    print(f"buckets {counts.tolist()}: max row rel-L2 {err.max():.3e}")
+    assert HP.rel_l2(y, ref) < HP.GEMM_TOL
+    assert err.max() < 4 * HP.GEMM_TOL
+
+
 def test_gemm_ffn_single_expert_identity_rows():
     # the shared-expert form: one-expert bank, no offsets, row r = token r
     w = GEMM_MID
