@@ -110,22 +110,34 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 // direct global -> LDS loads in which 8 lanes cover a row's 128 contiguous
 // bytes (whole cache lines), double buffered, so the fragment reads hit LDS
 // instead of scattering 64-byte pieces of 16 rows over the cache. Piece p of
-// row r sits at slot p ^ (r % 8).
+// row r sits at slot p ^ (r % 8). ST stages: with 2, two workgroups share a
+// CU; with 4 (one a CU), the copies run three steps ahead, for grids of at
+// most one tile per CU (a 2k-token call has 48 tiles), whose workgroups
+// cannot hide a step's load latency behind each other. Measured: 2k tokens
+// 66 against 85 us; at 16k tokens (384 tiles) four stages took 142 against
+// 103 us.
 // ---------------------------------------------------------------------------
 constexpr int kRtBK = 64;
 constexpr int kRtStage = 2 * 128 * kRtBK * 2;  // A and B tiles, bf16: 32 KB
 
+// m0 is named as clobbered: each copy rewrites it, so the compiler must keep
+// no value of its own there (clang warns that m0 is a reserved register; the
+// warning is silenced for this function only).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void rt_lds_load16(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
                :
                : "v"(voff), "s"(lds), "s"(base)
-               : "memory");
+               : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
+template <int ST>
 __global__ __launch_bounds__(256) void router_mfma_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
-  __shared__ __align__(16) char lds[2 * kRtStage];
+  __shared__ __align__(16) char lds[ST * kRtStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, c = lane & 15, g = lane >> 4;
@@ -153,13 +165,24 @@ __global__ __launch_bounds__(256) void router_mfma_lds_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Stage ks lands while earlier steps compute: at the top of step ks the
+  // copies of up to ST - 2 later stages (8 per thread each) may still be in
+  // flight (loads complete in order), then one barrier makes stage ks
+  // visible and frees the buffer of step ks - 1 for ks + ST - 1.
+  static_assert(ST >= 2 && ST <= 4, "2..4 stages");
   const int steps = H / kRtBK;
-  issue(0, 0);
+  for (int p = 0; p < ST - 1 && p < steps; ++p) issue(p, p * kRtBK);
   for (int ks = 0; ks < steps; ++ks) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int ahead = min(steps - 1 - ks, ST - 2);
+    if (ahead >= 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (ahead == 1)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (ks + 1 < steps) issue((ks + 1) & 1, (ks + 1) * kRtBK);
-    const uint4* sa = reinterpret_cast<const uint4*>(lds + (ks & 1) * kRtStage);
+    if (ks + ST - 1 < steps) issue((ks + ST - 1) % ST, (ks + ST - 1) * kRtBK);
+    const uint4* sa = reinterpret_cast<const uint4*>(lds + (ks % ST) * kRtStage);
     const uint4* sb = sa + 1024;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -196,7 +219,9 @@ void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bi
                           int T, int H, int E, float* logits, hipStream_t s) {
   if (T > kRouterGemvMaxT && H % kRtBK == 0 && (size_t)T * H * 2 < (1ull << 32) &&
       (size_t)E * H * 2 < (1ull << 32)) {
-    launch("router_mfma_lds_kernel", router_mfma_lds_kernel, dim3((T + 127) / 128, (E + 127) / 128),
+    const dim3 grid((T + 127) / 128, (E + 127) / 128);
+    launch("router_mfma_lds_kernel",
+           grid.x * grid.y <= 256 ? router_mfma_lds_kernel<4> : router_mfma_lds_kernel<2>, grid,
            dim3(256), 0, s, x, wr, bias, T, H, E, logits);
     return;
   }
