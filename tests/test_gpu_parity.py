@@ -652,12 +652,16 @@ def test_gemm_ffn_hand_made_buckets():
 # chunks), 4 of down
 GEMM_K8 = S.Workload("gemm_k8", 91, T=200, H=1024, E=6, k=2, I=512, exp_lo=-6, exp_hi=-3,
                      desc="grouped-GEMM parity shape, 8 K steps")
+# hidden 768: 24-byte gate/up scale rows, so gate/up copies its scales with
+# a 4-byte load per row and step instead of 16-byte chunks
+GEMM_K6 = S.Workload("gemm_k6", 92, T=200, H=768, E=6, k=2, I=256, exp_lo=-6, exp_hi=-3,
+                     desc="grouped-GEMM parity shape, per-step scale loads")
 
 
-def test_gemm_ffn_buckets_around_sixteen_rows():
+@pytest.mark.parametrize("w", [GEMM_K8, GEMM_K6], ids=["chunked_scales", "per_step_scales"])
+def test_gemm_ffn_buckets_around_sixteen_rows(w):
     # buckets of at most 16 rows take 16-row tiles with three stages; 17 rows
     # and more take the 64-row tiles
-    w = GEMM_K8
     counts = np.array([16, 17, 15, 1, 0, 100])  # 149 rows: above the GEMV path
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(offsets[-1])
