@@ -26,7 +26,12 @@
 //  * the step's E8M0 scales, 4 bytes per weight row.
 // A stage is 33 KB (34 KB with an NVFP4 bank's 8 scale bytes per weight
 // row), so two workgroups share a CU and one's copies overlap the other's
-// matrix-core work.
+// matrix-core work. Gate/up, whose scale rows are a multiple of 16 bytes at
+// the layer's shape, instead copies each weight row's scales 16 bytes at a
+// time (4 K steps; 2 for NVFP4) into two chunk buffers after the stages.
+// A bucket of at most 16 rows takes a 16-row tile: 4 KB of A a step, so
+// three stages fit in the same LDS and its weight copies run two steps
+// ahead (such tiles are bound by their copies).
 // Lane (column c, lane group g) of a wave takes the 32 codes of K range
 // [32 g, 32 g + 32) of its weight row, one E8M0 block, and converts them
 // with the gfx950 scaled FP4 conversion (exact: an E2M1 value times a power
