@@ -652,13 +652,17 @@ def test_gemm_ffn_hand_made_buckets():
 # chunks), 4 of down
 GEMM_K8 = S.Workload("gemm_k8", 91, T=200, H=1024, E=6, k=2, I=512, exp_lo=-6, exp_hi=-3,
                      desc="grouped-GEMM parity shape, 8 K steps")
-# hidden 768: 24-byte gate/up scale rows, so gate/up copies its scales with
-# a 4-byte load per row and step instead of 16-byte chunks
+# hidden 768: 24-byte gate/up scale rows, not a multiple of 16 bytes, so
+# gate/up loads its scales per step
 GEMM_K6 = S.Workload("gemm_k6", 92, T=200, H=768, E=6, k=2, I=256, exp_lo=-6, exp_hi=-3,
                      desc="grouped-GEMM parity shape, per-step scale loads")
+# intermediate 768: down's 24-byte scale rows, 6 K steps
+GEMM_I768 = S.Workload("gemm_i768", 93, T=200, H=512, E=6, k=2, I=768, exp_lo=-6, exp_hi=-3,
+                       desc="grouped-GEMM parity shape, 6 down K steps")
 
 
-@pytest.mark.parametrize("w", [GEMM_K8, GEMM_K6], ids=["chunked_scales", "per_step_scales"])
+@pytest.mark.parametrize("w", [GEMM_K8, GEMM_K6, GEMM_I768],
+                         ids=["chunked_scales", "per_step_scales", "down_k768"])
 def test_gemm_ffn_buckets_around_sixteen_rows(w):
     # buckets of at most 16 rows take 16-row tiles with three stages; 17 rows
     # and more take the 64-row tiles
