@@ -235,19 +235,19 @@ void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bi
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token. Lane l holds logits l, l+64, ... (E <= 1024, so
-// at most 16 per lane). Each of the k rounds takes the lane-local best
+// Top-k: one wave per token. Lane l holds logits l, l+64, ... (NK per lane:
+// 6 where E <= 384, else 16 for E <= 1024). Each of the k rounds takes the lane-local best
 // untaken entry, then a butterfly argmax across the wave under the order
 // (larger value, then lower id); the winner's owner marks it taken. Weights
 // are exp(l_j - l_1) normalised over the chosen k (the full-softmax
 // normaliser cancels). NaN logits rank as -inf.
 // ---------------------------------------------------------------------------
-constexpr int kTopkMaxPerLane = 16;
 
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+template <int NK>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T,
                                                    int E, int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
@@ -255,10 +255,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* L = logits + (size_t)t * E;
-  float v[kTopkMaxPerLane];
+  float v[NK];
   uint32_t taken = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkMaxPerLane; ++i) {
+  for (int i = 0; i < NK; ++i) {
     const int e = lane + kWave * i;
     float val = -INFINITY;
     if (e < E) {
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < kTopkMaxPerLane; ++i) {
+    for (int i = 0; i < NK; ++i) {
       const int e = lane + kWave * i;
       if (!((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
         bv = v[i];
@@ -308,7 +308,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                  hipStream_t s) {
-  launch("topk_kernel", topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+  launch("topk_kernel", E <= 6 * kWave ? topk_kernel<6> : topk_kernel<16>, dim3((T + 3) / 4),
+         dim3(256), 0, s, logits, T, E, k, ids, w);
 }
 
 }  // namespace moe

@@ -65,6 +65,20 @@ def test_router_topk_matches_oracle(name):
     HP.check_routing(ref, ids, wt, w.k)
 
 
+@pytest.mark.parametrize("T", [3, 300])
+def test_router_topk_many_experts(T):
+    # E = 1000: 16 logits per lane in the top-k wave (up to 384: 6); T = 3
+    # takes the router GEMV, T = 300 the MFMA router
+    w = S.Workload("router_e1000", 94, T=T, H=256, E=1000, k=8, I=128, exp_lo=-6, exp_hi=-3)
+    x = S.gen_tokens(w, 0)
+    wr = S.gen_router(w, 0)
+    ref = O.route(x, wr, None, w.k)
+    lg, ids, wt = run_router(w, x, wr, None)
+    L = ref["logits"]
+    assert np.abs(lg - L).max() / np.abs(L).max() < 1e-5
+    HP.check_routing(ref, ids, wt, w.k)
+
+
 def test_router_zero_weights_tie_to_lowest_ids():
     w = S.get("tiny")
     x = S.gen_tokens(w, 0)
