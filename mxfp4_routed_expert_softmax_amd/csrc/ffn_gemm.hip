@@ -454,6 +454,8 @@ __global__ __launch_bounds__(BM == 128 ? 512 : 256, BM == 128 ? 1 : 2) void gemm
       constexpr int kSS = kSA + kBBytes + kSBy;  // bytes per stage
       constexpr int kS3 = 3;                     // stages
       static_assert(kS3 * kSS + 2 * kChunkBy <= (int)sizeof(lds), "skinny stages exceed the LDS");
+      // the waits below count 1 A copy and 4 B copies per stage, plus its scales
+      static_assert(kBL == 4 && 16 * 16 == NT, "skinny stage copies per thread");
       const uint32_t ck3 = lds_base + kS3 * kSS;  // the two scale chunks
       auto issue_s = [&](int st, int ks) {
         const uint32_t base = lds_base + (uint32_t)(st * kSS);
