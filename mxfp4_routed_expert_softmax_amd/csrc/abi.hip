@@ -161,7 +161,7 @@ LayerWs layer_ws(void* ws, int T, int H, int I, int E, int k) {
   const size_t R = (size_t)T * k;
   Carve c(ws);
   LayerWs L;
-  L.logits = c.take<float>((size_t)T * E);
+  L.logits = c.take<float>((size_t)T * E * router_split(T, H, E));  // the router's partials
   L.ids = c.take<int32_t>(R);
   L.w = c.take<float>(R);
   L.offsets = c.take<int32_t>((size_t)E + 1);
@@ -501,10 +501,11 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
   float* w = topk_w_out ? topk_w_out : L.w;
   const int R = T * k;
 
+  const int rsplit = router_split(T, H, E);
   launch_router_logits(static_cast<const uint16_t*>(x_bf16),
                        static_cast<const uint16_t*>(w_router_bf16), logit_bias, T, H, E, L.logits,
-                       stream);
-  launch_topk(L.logits, T, E, k, ids, w, stream);
+                       stream, rsplit);
+  launch_topk(L.logits, T, E, k, ids, w, stream, rsplit);
   launch_permute(ids, T, k, E, L.offsets, L.row_token, L.inv_row, L.active, L.perm, stream);
 
   FfnProblem p{};
@@ -669,10 +670,11 @@ int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
   int32_t* ids = topk_ids_out ? topk_ids_out : L.ids;
   float* w = topk_w_out ? topk_w_out : L.w;
   const int R = T * k;
+  const int rsplit = router_split(T, H, E);
   launch_router_logits(static_cast<const uint16_t*>(x_bf16),
                        static_cast<const uint16_t*>(w_router_bf16), logit_bias, T, H, E, L.logits,
-                       stream);
-  launch_topk(L.logits, T, E, k, ids, w, stream);
+                       stream, rsplit);
+  launch_topk(L.logits, T, E, k, ids, w, stream, rsplit);
   launch_permute(ids, T, k, E, L.offsets, L.row_token, L.inv_row, L.active, L.perm, stream);
   FfnProblem p{};
   p.x = static_cast<const uint16_t*>(x_bf16);

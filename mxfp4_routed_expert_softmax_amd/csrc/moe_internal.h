@@ -31,10 +31,14 @@ constexpr int kRouterGemvMaxT = 16;
 // Pair counts up to this are bucketed by one workgroup.
 constexpr int kPermuteChunk = 2048;
 
+// split > 1 (router_split): the router writes `split` partial logit arrays
+// of [T][E] over consecutive ranges of H (the bias in the first), and the
+// top-k sums them in order.
+int router_split(int T, int H, int E);
 void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
-                          int T, int H, int E, float* logits, hipStream_t s);
+                          int T, int H, int E, float* logits, hipStream_t s, int split = 1);
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                 hipStream_t s);
+                 hipStream_t s, int split = 1);
 
 size_t permute_ws_bytes(int T, int k, int E);
 // `active` [E] receives the ids of experts with rows, ascending, then -1s.

@@ -133,10 +133,13 @@ __device__ __forceinline__ void rt_lds_load16(const void* base, uint32_t voff, u
 }
 #pragma clang diagnostic pop
 
+// blockIdx.z: the range of H (steps K steps of 64 from z * steps) whose
+// partial sums go to logits + z T E; the bias goes into the first.
 template <int ST>
 __global__ __launch_bounds__(256) void router_mfma_lds_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits) {
+    const float* __restrict__ bias, int T, int H, int E, float* __restrict__ logits,
+    int steps) {
   __shared__ __align__(16) char lds[ST * kRtStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -149,8 +152,9 @@ __global__ __launch_bounds__(256) void router_mfma_lds_kernel(
   for (int u = 0; u < 4; ++u) {
     const int r = 32 * u + (tid >> 3);
     const int piece = (tid & 7) ^ (r & 7);
-    a_off[u] = ((uint32_t)min(mt + r, T - 1) * (uint32_t)H + (uint32_t)(piece * 8)) * 2u;
-    b_off[u] = ((uint32_t)min(nt + r, E - 1) * (uint32_t)H + (uint32_t)(piece * 8)) * 2u;
+    const uint32_t kz = (uint32_t)(blockIdx.z * steps * kRtBK);
+    a_off[u] = ((uint32_t)min(mt + r, T - 1) * (uint32_t)H + kz + (uint32_t)(piece * 8)) * 2u;
+    b_off[u] = ((uint32_t)min(nt + r, E - 1) * (uint32_t)H + kz + (uint32_t)(piece * 8)) * 2u;
   }
   auto issue = [&](int st, int k0) {
     const uint32_t base = lds_base + (uint32_t)(st * kRtStage);
@@ -170,7 +174,6 @@ __global__ __launch_bounds__(256) void router_mfma_lds_kernel(
   // flight (loads complete in order), then one barrier makes stage ks
   // visible and frees the buffer of step ks - 1 for ks + ST - 1.
   static_assert(ST >= 2 && ST <= 4, "2..4 stages");
-  const int steps = H / kRtBK;
   for (int p = 0; p < ST - 1 && p < steps; ++p) issue(p, p * kRtBK);
   for (int ks = 0; ks < steps; ++ks) {
     const int ahead = min(steps - 1 - ks, ST - 2);
@@ -204,25 +207,35 @@ __global__ __launch_bounds__(256) void router_mfma_lds_kernel(
   for (int j = 0; j < 4; ++j) {
     const int n = nt + 64 * wn + 16 * j + c;
     if (n >= E) continue;
-    const float bn = bias ? bias[n] : 0.0f;
+    const float bn = bias && blockIdx.z == 0 ? bias[n] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = mt + 64 * wm + 16 * i + 4 * g + v;
-        if (m < T) logits[(size_t)m * E + n] = acc[i][j][v] + bn;
+        if (m < T) logits[(size_t)blockIdx.z * T * E + (size_t)m * E + n] = acc[i][j][v] + bn;
       }
   }
 }
 
+// Grids of at most 64 tiles (2k tokens at E = 384: 48) split H in four, so
+// four times as many workgroups each take a quarter of the K steps.
+int router_split(int T, int H, int E) {
+  const long tiles = (long)((T + 127) / 128) * ((E + 127) / 128);
+  const bool lds_path = T > kRouterGemvMaxT && H % kRtBK == 0 &&
+                        (size_t)T * H * 2 < (1ull << 32) && (size_t)E * H * 2 < (1ull << 32);
+  return lds_path && (H / kRtBK) % 4 == 0 && tiles <= 64 ? 4 : 1;
+}
+
+// split: 1, or router_split(T, H, E) (which takes this LDS path)
 void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
-                          int T, int H, int E, float* logits, hipStream_t s) {
+                          int T, int H, int E, float* logits, hipStream_t s, int split) {
   if (T > kRouterGemvMaxT && H % kRtBK == 0 && (size_t)T * H * 2 < (1ull << 32) &&
       (size_t)E * H * 2 < (1ull << 32)) {
-    const dim3 grid((T + 127) / 128, (E + 127) / 128);
+    const dim3 grid((T + 127) / 128, (E + 127) / 128, split);
     launch("router_mfma_lds_kernel",
-           grid.x * grid.y <= 256 ? router_mfma_lds_kernel<4> : router_mfma_lds_kernel<2>, grid,
-           dim3(256), 0, s, x, wr, bias, T, H, E, logits);
+           grid.x * grid.y * grid.z <= 256 ? router_mfma_lds_kernel<4> : router_mfma_lds_kernel<2>,
+           grid, dim3(256), 0, s, x, wr, bias, T, H, E, logits, H / kRtBK / split);
     return;
   }
   if (T <= kRouterGemvMaxT) {
@@ -250,7 +263,7 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
 template <int NK>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T,
                                                    int E, int k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ w) {
+                                                   float* __restrict__ w, int split) {
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -263,6 +276,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     float val = -INFINITY;
     if (e < E) {
       val = L[e];
+      for (int z = 1; z < split; ++z) val += L[(size_t)z * T * E + e];  // partials in order
       val = (val != val) ? -INFINITY : val;
     } else {
       taken |= 1u << i;
@@ -307,9 +321,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                 hipStream_t s) {
+                 hipStream_t s, int split) {
   launch("topk_kernel", E <= 6 * kWave ? topk_kernel<6> : topk_kernel<16>, dim3((T + 3) / 4),
-         dim3(256), 0, s, logits, T, E, k, ids, w);
+         dim3(256), 0, s, logits, T, E, k, ids, w, split);
 }
 
 }  // namespace moe
