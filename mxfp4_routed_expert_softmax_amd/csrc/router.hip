@@ -7,6 +7,7 @@
 // logits with a fixed tie rule: larger logit first, equal logits -> lower id.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "topk_wave.h"
 
 namespace moe {
 
@@ -248,18 +249,14 @@ void launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bi
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token. Lane l holds logits l, l+64, ... (NK per lane:
-// 6 where E <= 384, else 16 for E <= 1024). Each of the k rounds takes the lane-local best
-// untaken entry, then a butterfly argmax across the wave under the order
-// (larger value, then lower id); the winner's owner marks it taken. Weights
-// are exp(l_j - l_1) normalised over the chosen k (the full-softmax
-// normaliser cancels). NaN logits rank as -inf.
+// Top-k: one wave per token, lane l holding the logits of experts l, l + 64,
+// ... (NK per lane: 6 where E <= 384, else 16 for E <= 1024), summed over
+// the router's partial arrays in order. The selection is the wave-wide one
+// of the few-token routing (topk_wave.h): k rounds of a lane-local maximum
+// and a wave maximum over keys ordered by (larger logit, then lower id);
+// NaN logits rank as -inf. Weights are exp(l_j - l_1) normalised over the
+// chosen k (the full-softmax normaliser cancels).
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
 template <int NK>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T,
                                                    int E, int k, int32_t* __restrict__ ids,
@@ -268,56 +265,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* L = logits + (size_t)t * E;
-  float v[NK];
-  uint32_t taken = 0;
+  float lv[NK];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     const int e = lane + kWave * i;
-    float val = -INFINITY;
+    float val = 0.0f;
     if (e < E) {
       val = L[e];
       for (int z = 1; z < split; ++z) val += L[(size_t)z * T * E + e];  // partials in order
-      val = (val != val) ? -INFINITY : val;
-    } else {
-      taken |= 1u << i;
     }
-    v[i] = val;
+    lv[i] = val;
   }
-  float my_val = 0.0f, top = 0.0f;
-  int my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = lane + kWave * i;
-      if (!((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    if (lane == j) {
-      my_val = bv;
-      my_id = bi;
-    }
-    if (j == 0) top = bv;
-  }
-  const float z = (lane < k) ? expf(my_val - top) : 0.0f;
-  const float sum = wave_sum(z);
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
-    w[(size_t)t * k + lane] = z / sum;
-  }
+  topk_row_f64<NK>(lv, E, k, ids + (size_t)t * k, w + (size_t)t * k);
 }
 
 void launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
