@@ -402,7 +402,7 @@ def prefill_record(args, M, S, np, torch, bank, routed_np, shared_np):
     U = int(torch.unique(ids).numel())
     kern = sweep_kernel_times(M, torch, np, call, Kp)
     gemms = {}
-    for name in ("gemm_gateup_kernel", "gemm_down_kernel"):
+    for name in ("gemm_gateup_kernel", "gemm_down_kernel", "gemm_down_combine_kernel"):
         if name in kern:
             fl = kernel_work(name, w, U)[1][0]
             tf = fl / (kern[name] * 1e-6) / 1e12
@@ -641,8 +641,13 @@ def kernel_work(name, w, U, shared=True, nvfp4=False, shared8=False):
         return "gemm", (rows * 2.0 * 2 * H * I,
                         (U + (1 if shared else 0)) * gu_expert + T * H * 2 + rows * I * 2)
     if name == "gemm_down_kernel":
-        return "gemm", (rows * 2.0 * H * I,
-                        (U + (1 if shared else 0)) * dn_expert + rows * I * 2 + rows * H * 4)
+        # with an MXFP4 or NVFP4 shared expert the layer runs its down tiles
+        # in gemm_down_combine_kernel: this launch takes the routed rows
+        return "gemm", (R * 2.0 * H * I, U * dn_expert + R * I * 2 + R * H * 4)
+    if name == "gemm_down_combine_kernel":
+        # the shared expert's down rows, each token combined in the epilogue:
+        # the k routed y rows read, the output written
+        return "gemm", (T * 2.0 * H * I, dn_expert + T * I * 2 + R * H * 4 + T * H * 4)
     if name == "gemm_mx_gateup_kernel":
         # activations and h at one byte plus one scale byte per 32
         return "gemm", (rows * 2.0 * 2 * H * I,

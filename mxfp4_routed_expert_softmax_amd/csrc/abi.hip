@@ -527,12 +527,23 @@ int layer_forward(const void* x_bf16, const void* w_router_bf16, const float* lo
     p.h_sh = L.h_sh;
     p.y_sh = L.y_sh;
   }
-  if (mx_act)
+  if (mx_act) {
     launch_expert_gemm_mx(p, L.ffn, stream);
-  else if (gemm_supported(T, H, I, R, shared != nullptr))
+  } else if (gemm_supported(T, H, I, R, shared != nullptr)) {
+    if (shared) {
+      // the shared expert's down tiles may combine each token
+      p.inv_row = L.inv_row;
+      p.topk_w = w;
+      p.k = k;
+      p.out = out;
+      if (launch_expert_gemm(p, L.ffn, stream)) return launch_status();
+      launch_combine(L.y, L.inv_row, w, L.y_sh, T, k, H, R, out, stream);
+      return launch_status();
+    }
     launch_expert_gemm(p, L.ffn, stream);
-  else
+  } else {
     launch_expert_ffn(p, stream);
+  }
   // an FP8 shared expert runs after the routed FFN, in the same scratch
   if (shared8)
     launch_fp8_ffn(static_cast<const uint16_t*>(x_bf16), shared8, T, L.y_sh, L.ffn, stream);
@@ -695,10 +706,21 @@ int moe_layer_forward_nvfp4(const void* x_bf16, const void* w_router_bf16,
     p.h_sh = L.h_sh;
     p.y_sh = L.y_sh;
   }
-  if (T > kDecodeMaxT && gemm_supported(T, H, I, R, shared != nullptr))
+  if (T > kDecodeMaxT && gemm_supported(T, H, I, R, shared != nullptr)) {
+    if (shared) {
+      // the shared expert's down tiles may combine each token
+      p.inv_row = L.inv_row;
+      p.topk_w = w;
+      p.k = k;
+      p.out = out;
+      if (launch_expert_gemm(p, L.ffn, stream)) return launch_status();
+      launch_combine(L.y, L.inv_row, w, L.y_sh, T, k, H, R, out, stream);
+      return launch_status();
+    }
     launch_expert_gemm(p, L.ffn, stream);
-  else
+  } else {
     launch_expert_ffn(p, stream);
+  }
   launch_combine(L.y, L.inv_row, w, shared ? L.y_sh : nullptr, T, k, H, R, out, stream);
   return launch_status();
 }

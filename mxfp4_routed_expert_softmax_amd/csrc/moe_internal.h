@@ -79,6 +79,15 @@ struct FfnProblem {
   BankView shared;
   float* h_sh;               // [T][I]
   float* y_sh;               // [T][H]
+  // Layer calls on the grouped GEMM with a shared expert: the combine's
+  // inputs and output. With out set and enough tokens, the shared expert's
+  // down tiles run in a launch of their own after the routed ones and
+  // combine each token in their epilogue (no y_sh round trip, no combine
+  // launch).
+  const int32_t* inv_row;    // [T][k]
+  const float* topk_w;       // [T][k]
+  int k;
+  float* out;                // [T][H] or null
 };
 
 size_t ffn_ws_bytes(int T, int H, int I, int R, bool shared);
@@ -88,7 +97,9 @@ void launch_expert_ffn(const FfnProblem& p, hipStream_t s);
 // FfnProblem's h / h_sh are unused). Call only where gemm_supported().
 bool gemm_supported(int T, int H, int I, int R, bool shared);
 size_t gemm_ws_bytes(int T, int H, int I, int E, int R, bool shared);
-void launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s);
+// Returns whether the launches also wrote p.out (the combine folded into
+// the shared expert's down tiles); otherwise the caller combines.
+bool launch_expert_gemm(const FfnProblem& p, void* ws, hipStream_t s);
 
 // MXFP8-activation mode of the grouped GEMM: x and h rounded to E4M3 with
 // one E8M0 scale per 32, the bank's E2M1 codes fed to the scaled MFMA as
